@@ -1,0 +1,250 @@
+"""KDA forward prefill benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg2] [--cp auto]
+
+One step = one kda_fwd call (index tables, chunk prep, recurrence and, when the
+plan splits sequences, pre-scan + merge + segment recurrence) over one batch
+of seeded synthetic inputs already resident in HBM.  W untimed steps, then
+exactly K steps timed with HIP events on the stream the library launches on,
+bracketed by device synchronisation.  Prints ONE JSON line.
+
+Per-stage kernel time comes from the library's own event hook
+(kda_profile_enable / kda_profile_collect) over the same timed region; the
+roofline object is computed for the stage that takes the most time.
+
+The CPU baseline times the fp64 oracle (unchanged) on a bounded sample of the
+same workload: the first sequence's first L tokens for every head, one head per
+worker process, before any GPU work starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s at H=16,D=128, T=4K–64K; % of MFMA/HBM roofline"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
+D = 128
+C = 16
+# algorithmic work per token-head (one token of one head)
+BYTES_IN = 4 * 2 * D + 2  # q, k, v, g bf16 + beta bf16
+BYTES_OUT = 2 * D  # out bf16
+FLOPS_PATH = 6 * D * D + 10 * C * D  # 3 chunk GEMMs of 2*16*128*128 per 16 tokens + five 16x16x128 products
+FLOPS_PREP = 4 * 2 * C * C * D // C  # A, Aqk, W, Ut (16x16x128 each) per 16 tokens
+FLOPS_RECUR = 6 * D * D + 2 * C * D  # W S, Qbar S, Khat^T U, Aqk U per token
+
+
+_CPU_X = None  # inputs shared with the forked baseline workers
+
+
+def _cpu_worker(args):
+    name, head, L = args
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kda_oracle as O
+
+    with threadpool_limits(1):
+        x = _CPU_X
+        cu = x["cu_seqlens"]
+        t0 = 0 if cu is None else int(cu[0])
+        sl = slice(t0, t0 + L)
+        s0 = None if x["initial_state"] is None else x["initial_state"][:1]
+        t = time.perf_counter()
+        O.kda_forward(x["q"][:1, sl], x["k"][:1, sl], x["v"][:1, sl], x["g"][:1, sl], x["beta"][:1, sl], x["A_log"],
+                      x["dt_bias"], x["scale"], x["lower_bound"], s0, None, heads=[head])
+        return time.perf_counter() - t
+
+
+def cpu_baseline(name: str, target_s: float) -> dict:
+    import multiprocessing as mp
+
+    import kda_inputs
+
+    global _CPU_X
+    w = kda_inputs.WORKLOADS[name]
+    _CPU_X = kda_inputs.make_inputs(w)
+    first_len = w.T if w.seqlens is None else int(w.seqlens[0])
+    # calibrate on one head, 64 tokens, in this process
+    L0 = min(64, first_len)
+    per_tok = _cpu_worker((name, 0, L0)) / L0
+    workers = max(1, min(16, os.cpu_count() or 1, w.H))
+    rounds = math.ceil(w.H / workers)
+    L = int(max(16, min(first_len, target_s / (per_tok * rounds))))
+    ctx = mp.get_context("fork")
+    t = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        pool.map(_cpu_worker, [(name, h, L) for h in range(w.H)])
+    wall = time.perf_counter() - t
+    return {
+        "value": L / wall,
+        "unit": "tokens/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{w.name}: first {L} tokens of sequence 0, all {w.H} heads, fp64 token recurrence, "
+                  f"one head per process ({workers} processes), {wall:.1f} s wall",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="cfg2", help="cfg1..cfg5 (cfg4a/cfg4b)")
+    ap.add_argument("--cp", default="auto", help="auto | off | force")
+    ap.add_argument("--seg", type=int, default=0, help="segment length in chunks (0 = library choice)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (scale reference for HBM counters)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); multi-GPU runs are not part of this build",
+              file=sys.stderr)
+        return 2
+
+    import kda_inputs
+
+    w = kda_inputs.WORKLOADS[a.config]
+    cpu = None if a.no_cpu_baseline else cpu_baseline(a.config, a.cpu_seconds)
+
+    import numpy as np
+    import torch
+
+    import kimi_delta_attention_02_amd as kda
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        return 1
+    kda.load_library()
+    dev = torch.device("cuda:0")
+    x = kda_inputs.make_inputs(w)
+
+    def bf(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr)).view(torch.bfloat16).to(dev)
+
+    q, k, v, g, beta = (bf(x[n]) for n in ("q", "k", "v", "g", "beta"))
+    A_log = torch.from_numpy(x["A_log"]).to(dev)
+    dt_bias = torch.from_numpy(x["dt_bias"]).to(dev)
+    sdt = torch.float32 if w.state_dtype == "fp32" else torch.bfloat16
+    init = None
+    if x["initial_state"] is not None:
+        init = bf(x["initial_state"]) if w.state_dtype == "bf16" else torch.from_numpy(x["initial_state"]).to(dev)
+    final = torch.empty(w.N, w.H, D, D, dtype=sdt, device=dev) if w.want_final else None
+    cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).to(dev)
+    out = torch.empty_like(q)
+    total = w.B * w.T
+    seg = kda.plan_seg_chunks(total, w.H, w.N, a.cp, a.seg)
+    ws = torch.empty(kda.get_workspace_size(total, w.H, w.N, a.cp, a.seg), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.fwd(q, k, v, g, beta, x["scale"], out, A_log=A_log, dt_bias=dt_bias, lower_bound=x["lower_bound"],
+                workspace=ws, initial_state=init, final_state=final, cu_seqlens=cu, cp_mode=a.cp, seg_chunks=a.seg)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    kda.profile_enable(True)
+    evs[0].record(stream)
+    for i in range(a.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    kda.profile_enable(False)
+    stages = kda.profile_collect()
+    total_ms = evs[0].elapsed_time(evs[-1])
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
+    q1, q3 = len(per) // 4, len(per) - len(per) // 4
+    iqr_mean = float(np.mean(per[q1:q3])) if q3 > q1 else float(np.mean(per))
+    ms = total_ms / a.steps
+    th = total * w.H  # token-heads per step
+    state_bytes = 0
+    if init is not None:
+        state_bytes += init.numel() * init.element_size()
+    if final is not None:
+        state_bytes += final.numel() * final.element_size()
+
+    # algorithmic work per stage launch
+    stage_work = {
+        "prep": (th * BYTES_IN, th * FLOPS_PREP),
+        "recur0": (th * BYTES_OUT + state_bytes, th * FLOPS_RECUR),
+        "recur1": (th * BYTES_OUT + state_bytes, th * FLOPS_RECUR),
+        "index": (0, 0),
+        "merge": (0, 0),
+    }
+    stage_avg = {n: (t / c if c else 0.0) for n, (t, c) in stages.items()}
+    dom = max(stage_avg, key=lambda n: stages[n][0])
+    bytes_d, flops_d = stage_work[dom]
+    if dom == "recur0" and seg > 0:  # with a split the recurrence work is shared by recur0 and recur1
+        bytes_d, flops_d = bytes_d, flops_d
+    t_s = stage_avg[dom] / 1e3
+    gbs = bytes_d / t_s / 1e9 if t_s > 0 else 0.0
+    tfl = flops_d / t_s / 1e12 if t_s > 0 else 0.0
+    if bytes_d / (PEAK_HBM_GBS * 1e9) >= flops_d / (PEAK_BF16_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfl / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = {"prep": "kda_prep_kernel", "recur0": "kda_recur_kernel", "recur1": "kda_recur_kernel",
+                      "index": "kda_index_scan", "merge": "kda_merge_kernel"}[dom]
+    roof["stage"] = dom
+    roof["avg_launch_ms"] = round(stage_avg[dom], 4)
+
+    path_bytes = th * (BYTES_IN + BYTES_OUT) + state_bytes
+    path_flops = th * FLOPS_PATH
+    res = {
+        "metric": METRIC,
+        "value": round(total / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs, see kda_inputs)",
+        "config": {
+            "workload": w.name, "B": w.B, "T": w.T, "H": w.H, "D": D, "num_seqs": w.N,
+            "global_batch": w.B, "seq_len": w.T, "lower_bound": w.lower_bound,
+            "state": w.state_dtype, "plan": "serial" if seg == 0 else f"segments of {seg} chunks",
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "path": {
+            "token_heads_per_s": round(th / (ms / 1e3), 1),
+            "achieved_GBs": round(path_bytes / (ms / 1e3) / 1e9, 1),
+            "achieved_TFLOPs": round(path_flops / (ms / 1e3) / 1e12, 2),
+            "hbm_frac": round(path_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_frac": round(path_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "iqr_mean_ms": round(iqr_mean, 4),
+        },
+        "stages_ms_per_step": {n: round(t / a.steps, 4) for n, (t, c) in stages.items() if c},
+    }
+    if a.copy_probe_mib > 0:
+        n = a.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = n
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) KDA forward prefill library (libkda.so).
+ *
+ * Kimi Delta Attention forward, one chain = one sequence x one head,
+ * K = V = 128, chunk C = 16 tokens:
+ *   q^ = q / sqrt(|q|^2 + 1e-6), k^ likewise; b = sigmoid(beta);
+ *   l  = lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h]))  (per key channel)
+ *   S_t = (I - b_t k^_t k^_t^T) Diag(exp(l_t)) S_{t-1} + b_t k^_t v_t^T;  o_t = scale * S_t^T q^_t
+ * The state tensors hold S^T: element [n][h][v][k] = S[k][v].
+ *
+ * Interface from the pages: "How to Use FlashKDA as a Backend for
+ * flash-linear-attention", sections "Kernel API and Tensor Requirements" (dtypes,
+ * shapes, lower_bound range) and "State Handling and Variable-Length Batches"
+ * (state [B,H,V,K] or [N,H,V,K], cu_seqlens with B = 1); "How FlashKDA
+ * Integrates with CUTLASS", sections "Workspace Allocation and Memory Alignment"
+ * (caller-allocated uint8 workspace sized by get_workspace_size(B*T, H)) and
+ * "State Management and Accumulator Types" (bf16 or fp32 states); cuLA PR #106,
+ * commit list (K1 chunk prep / K2 recurrence, CHUNK = 16; segment split
+ * K1 -> pre_scan -> merge -> segment K2, bit-identical to serial) and review
+ * thread (use_intracard_cp auto / True / False; no implicit conversions).
+ *
+ * Conventions for every call below:
+ *  - All tensor pointers are DEVICE pointers, contiguous, in the layouts stated.
+ *    The library never dereferences them on the host, never allocates, never
+ *    frees, never synchronises and never copies device -> host.
+ *  - kda_fwd is asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *  - Validation happens before any launch.  On error the status is negative,
+ *    nothing is launched, the outputs are untouched and kda_last_error() holds
+ *    a message.  There are no implicit dtype or layout conversions.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+#define KDA_CHUNK 16
+#define KDA_WORKSPACE_ALIGN 256
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = -1,          /* bad pointer, size, range or combination */
+  KDA_ERR_UNSUPPORTED = -2,          /* valid request this library does not implement (D != 128) */
+  KDA_ERR_WORKSPACE_TOO_SMALL = -3,  /* workspace_bytes < kda_get_workspace_size(...) */
+  KDA_ERR_HIP = -4                   /* a HIP launch failed */
+} kda_status;
+
+typedef enum { KDA_STATE_BF16 = 0, KDA_STATE_FP32 = 1 } kda_state_dtype;
+
+/* Segment split of long sequences ("intracard context parallel" on the cuLA
+ * PR #106 page: use_intracard_cp = "auto" | False | True). */
+typedef enum { KDA_CP_AUTO = 0, KDA_CP_OFF = 1, KDA_CP_FORCE = 2 } kda_cp_mode;
+
+/* Segment length, in chunks of 16 tokens, that kda_fwd will use for these
+ * sizes: 0 means serial (one segment per sequence).  Pure host arithmetic.
+ *   total_tokens : B*T (all batch rows, or the packed varlen length)
+ *   num_heads    : H >= 1;  num_seqs: N >= 1 (B for fixed length)
+ *   cp_mode      : kda_cp_mode;  seg_chunks: > 0 forces that segment length in
+ *                  AUTO and FORCE modes, 0 lets the library choose.
+ * Returns a negative kda_status on invalid arguments. */
+int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num_seqs,
+                            int32_t cp_mode, int32_t seg_chunks);
+
+/* Workspace bytes kda_fwd needs for these sizes and this plan (the pages'
+ * get_workspace_size(B*T, H), plus the sequence count and segment plan, since
+ * per-chunk and per-segment buffers scale with them).  Pure host arithmetic,
+ * no device calls.  Returns 0 on invalid arguments (see kda_last_error). */
+size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t num_seqs,
+                              int32_t cp_mode, int32_t seg_chunks);
+
+/* KDA forward.
+ *   q, k, v, g   : bf16 [B, T, H, 128], contiguous
+ *   beta         : bf16 [B, T, H] (logits; the sigmoid is applied inside)
+ *   scale        : output scale (finite)
+ *   out          : bf16 [B, T, H, 128], written (RNE)
+ *   A_log        : fp32 [H];  dt_bias: fp32 [H, 128]
+ *   lower_bound  : in [-5, 0]
+ *   initial_state: NULL or [N, H, 128(V), 128(K)] in state_dtype (read)
+ *   final_state  : NULL or [N, H, 128(V), 128(K)] in state_dtype (written);
+ *                  may alias initial_state.  Any of the four presence
+ *                  combinations is valid.
+ *   state_dtype  : kda_state_dtype, applies to whichever state is present
+ *   cu_seqlens   : NULL (fixed length, N = B) or int32 [num_seqs + 1] device
+ *                  offsets into the packed token axis (then B must be 1).
+ *                  Offsets are clamped into a non-decreasing sequence within
+ *                  [0, B*T] on the device, so malformed offsets cannot cause
+ *                  out-of-bounds access; they are not otherwise diagnosed.
+ *   num_seqs     : N; with cu_seqlens == NULL it must equal B (or be 0)
+ *   B, T, H, D   : D must be 128
+ *   workspace    : device buffer, KDA_WORKSPACE_ALIGN-aligned, of at least
+ *                  kda_get_workspace_size(B*T, H, N, cp_mode, seg_chunks) bytes;
+ *                  owned by the caller, clobbered by the call, and must not be
+ *                  shared by calls that may overlap.
+ *   cp_mode, seg_chunks : segment plan, as for kda_plan_seg_chunks
+ *   stream       : hipStream_t to launch on (NULL = default stream)
+ * B*T == 0 with no final_state returns KDA_OK without a launch. */
+int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                const void* initial_state, void* final_state, int32_t state_dtype,
+                const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t D,
+                void* workspace, size_t workspace_bytes, int32_t cp_mode, int32_t seg_chunks,
+                void* stream);
+
+/* Byte offsets of the workspace regions for these sizes and plan, so a caller
+ * can inspect the chunk-prep records and index tables a kda_fwd call left in
+ * its workspace.  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
+ * order of kda_ws_offset.  Returns KDA_OK or a negative kda_status. */
+typedef enum {
+  KDA_WS_COUNTERS = 0,      /* int32[4]: n_chunks, n_segs, sanitize flags, reserved */
+  KDA_WS_SEQ_START,         /* int32[N+1]   clamped sequence boundaries (last = end of the last sequence) */
+  KDA_WS_SEQ_LEN,           /* int32[N]     clamped length */
+  KDA_WS_SEQ_CHUNK_OFF,     /* int32[N+1]   prefix sums of ceil(len/16) */
+  KDA_WS_SEQ_SEG_OFF,       /* int32[N+1]   prefix sums of max(1, ceil(chunks/seg)) */
+  KDA_WS_CHUNK_TAB,         /* int32[max_chunks][2] (sequence, chunk in sequence) */
+  KDA_WS_SEG_TAB,           /* int32[max_segs][4] (sequence, chunk begin, chunk end, segment in sequence) */
+  KDA_WS_CHUNK_REC,         /* per (chunk, head) chunk-prep records, KDA_CHUNK_REC_BYTES each */
+  KDA_WS_SEG_M,             /* fp32 [max_segs][H][128][128] segment transitions M^T (CP only) */
+  KDA_WS_SEG_R,             /* fp32 [max_segs][H][128][128] zero-start segment states R^T (CP only) */
+  KDA_WS_SEG_S,             /* fp32 [max_segs][H][128][128] state entering each segment, [v][k] (CP only) */
+  KDA_WS_MAX_CHUNKS,        /* (count, not an offset) chunk-table capacity */
+  KDA_WS_MAX_SEGS,          /* (count, not an offset) segment-table capacity */
+  KDA_WS_TOTAL,             /* total bytes (= kda_get_workspace_size) */
+  KDA_WS_NUM_OFFSETS
+} kda_ws_offset;
+
+#define KDA_CHUNK_REC_BYTES 21504
+
+int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
+                              int32_t seg_chunks, int64_t* offs);
+
+/* Per-stage kernel timing for benchmarks.  While enabled on a host thread,
+ * every kda_fwd on that thread records a pair of HIP events around each stage
+ * on its stream (the events are created by the library on first use and kept
+ * for reuse).  kda_profile_collect waits for the recorded events, adds the
+ * elapsed milliseconds of each stage into stage_ms[0..n_stages-1] and the
+ * number of timed launches of the stage into stage_calls, and forgets them.
+ * Stages: KDA_STAGE_INDEX (index scan + table fill), KDA_STAGE_PREP (chunk
+ * prep), KDA_STAGE_RECUR0 (recurrence / pre-scan), KDA_STAGE_MERGE,
+ * KDA_STAGE_RECUR1 (segment recurrence).  Returns KDA_OK or KDA_ERR_HIP. */
+typedef enum {
+  KDA_STAGE_INDEX = 0,
+  KDA_STAGE_PREP,
+  KDA_STAGE_RECUR0,
+  KDA_STAGE_MERGE,
+  KDA_STAGE_RECUR1,
+  KDA_NUM_STAGES
+} kda_stage;
+
+int32_t kda_profile_enable(int32_t enable);
+int32_t kda_profile_collect(double* stage_ms, int64_t* stage_calls, int32_t n_stages);
+
+/* Static description of a status code. */
+const char* kda_strerror(int32_t status);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version string. */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,320 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// segment planning, workspace carving and the launch sequence.
+//
+// Launch sequence of one kda_fwd call, all on the caller's stream, with no
+// host synchronisation, allocation or device-to-host copy:
+//   index scan + table fill  ->  chunk prep (every chunk x head)
+//   -> recurrence phase 0 (serial sequences / segment 0, and the pre-scan of
+//      middle segments)  [-> merge -> recurrence phase 1 (segments >= 1)]
+// The bracketed part runs only when the plan splits sequences into segments
+// (cuLA PR #106 commit list: "K1 once -> pre_scan -> merge -> segment-K2").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+constexpr int64_t kMaxTokens = (int64_t)INT32_MAX - 16;  // tables are int32
+constexpr int kTargetUnits = 512;   // (segment, head) units the automatic plan aims for
+constexpr int kMinSegChunks = 32;   // shortest automatic segment (512 tokens)
+constexpr int kSerialChains = 256;  // chains that already fill the chip without splitting
+
+// ---- optional per-stage event timing (benchmarks) ----
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local Profiler g_prof;
+
+struct StageTimer {
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  StageTimer(int st, hipStream_t stream) : stage(st), s(stream) {
+    if (!g_prof.on) return;
+    a = g_prof.get();
+    if (a) hipEventRecord(a, s);
+  }
+  ~StageTimer() {
+    if (!a) return;
+    hipEvent_t b = g_prof.get();
+    if (!b) {
+      g_prof.pool.push_back(a);
+      return;
+    }
+    hipEventRecord(b, s);
+    g_prof.recs.push_back({stage, a, b});
+  }
+};
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int64_t max_chunks_for(int64_t total, int32_t N) {
+  // sum_i ceil(len_i / 16) <= (sum_i len_i + 15 N) / 16 for lengths summing to total
+  return (total + 15 * (int64_t)N) / kda::C;
+}
+
+// segment length in chunks (0 = serial); negative status on bad arguments
+int32_t plan(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg_chunks) {
+  if (total < 0 || total > kMaxTokens) return fail(KDA_ERR_INVALID_ARG, "total_tokens %lld out of range", (long long)total);
+  if (H < 1 || H > 65535) return fail(KDA_ERR_INVALID_ARG, "num_heads %d out of range [1, 65535]", H);
+  if (N < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must be >= 1", N);
+  if (cp_mode < KDA_CP_AUTO || cp_mode > KDA_CP_FORCE) return fail(KDA_ERR_INVALID_ARG, "cp_mode %d invalid", cp_mode);
+  if (seg_chunks < 0) return fail(KDA_ERR_INVALID_ARG, "seg_chunks %d must be >= 0", seg_chunks);
+  if (cp_mode == KDA_CP_OFF) return 0;
+  if (seg_chunks > 0) return seg_chunks;
+  const int64_t mc = max_chunks_for(total, N);
+  int64_t seg = (mc * H + kTargetUnits - 1) / kTargetUnits;
+  if (seg < kMinSegChunks) seg = kMinSegChunks;
+  if (cp_mode == KDA_CP_FORCE) return (int32_t)seg;
+  // automatic: keep serial when the chains already fill the chip or the
+  // sequences are too short for the pre-scan and merge to pay off
+  if ((int64_t)N * H >= kSerialChains) return 0;
+  if (mc < 4 * seg) return 0;
+  return (int32_t)seg;
+}
+
+struct Layout {
+  int64_t off[KDA_WS_NUM_OFFSETS];
+  int32_t seg;
+};
+
+int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg_chunks, Layout* out) {
+  const int32_t seg = plan(total, H, N, cp_mode, seg_chunks);
+  if (seg < 0) return seg;
+  const int64_t mc = max_chunks_for(total, N);
+  const int64_t ms = seg > 0 ? mc / seg + N : N;
+  if (mc > INT32_MAX / 2 || ms > INT32_MAX / 2)
+    return fail(KDA_ERR_INVALID_ARG, "problem too large for the index tables");
+  const int64_t A = KDA_WORKSPACE_ALIGN;
+  int64_t o = 0;
+  auto take = [&](int idx, int64_t bytes) {
+    out->off[idx] = o;
+    o = align_up(o + bytes, A);
+  };
+  take(KDA_WS_COUNTERS, 16);
+  take(KDA_WS_SEQ_START, 4 * ((int64_t)N + 1));
+  take(KDA_WS_SEQ_LEN, 4 * (int64_t)N);
+  take(KDA_WS_SEQ_CHUNK_OFF, 4 * ((int64_t)N + 1));
+  take(KDA_WS_SEQ_SEG_OFF, 4 * ((int64_t)N + 1));
+  take(KDA_WS_CHUNK_TAB, 8 * mc);
+  take(KDA_WS_SEG_TAB, 16 * ms);
+  take(KDA_WS_CHUNK_REC, mc * H * (int64_t)kda::REC_BYTES);
+  const int64_t seg_bytes = seg > 0 ? ms * H * (int64_t)kda::D * kda::D * 4 : 0;
+  take(KDA_WS_SEG_M, seg_bytes);
+  take(KDA_WS_SEG_R, seg_bytes);
+  take(KDA_WS_SEG_S, seg_bytes);
+  out->off[KDA_WS_MAX_CHUNKS] = mc;
+  out->off[KDA_WS_MAX_SEGS] = ms;
+  out->off[KDA_WS_TOTAL] = o;
+  out->seg = seg;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
+                            int32_t seg_chunks) {
+  return plan(total_tokens, num_heads, num_seqs, cp_mode, seg_chunks);
+}
+
+size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
+                              int32_t seg_chunks) {
+  Layout lay;
+  if (layout(total_tokens, num_heads, num_seqs, cp_mode, seg_chunks, &lay) != KDA_OK) return 0;
+  return (size_t)lay.off[KDA_WS_TOTAL];
+}
+
+int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
+                              int32_t seg_chunks, int64_t* offs) {
+  if (!offs) return fail(KDA_ERR_INVALID_ARG, "offs is NULL");
+  Layout lay;
+  const int32_t st = layout(total_tokens, num_heads, num_seqs, cp_mode, seg_chunks, &lay);
+  if (st != KDA_OK) return st;
+  std::memcpy(offs, lay.off, sizeof(lay.off));
+  return KDA_OK;
+}
+
+int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale, void* out,
+                const float* A_log, const float* dt_bias, float lower_bound, const void* initial_state,
+                void* final_state, int32_t state_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                int64_t T, int32_t H, int32_t D, void* workspace, size_t workspace_bytes, int32_t cp_mode,
+                int32_t seg_chunks, void* stream) {
+  g_last_error.clear();
+  // ---- pure argument checks (no HIP calls before these pass) ----
+  if (D != kda::D) return fail(KDA_ERR_UNSUPPORTED, "head dimension %d unsupported (only 128)", D);
+  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARG, "B=%d and T=%lld must be >= 0", B, (long long)T);
+  if (H < 1) return fail(KDA_ERR_INVALID_ARG, "H=%d must be >= 1", H);
+  if (T > 0 && B > kMaxTokens / T) return fail(KDA_ERR_INVALID_ARG, "B*T too large");
+  const int64_t total = (int64_t)B * T;
+  if (!(lower_bound >= -5.0f && lower_bound <= 0.0f))
+    return fail(KDA_ERR_INVALID_ARG, "lower_bound %g outside [-5, 0]", (double)lower_bound);
+  if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite");
+  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32)
+    return fail(KDA_ERR_INVALID_ARG, "state_dtype %d invalid", state_dtype);
+  int32_t N;
+  if (cu_seqlens) {
+    if (B != 1) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens requires B == 1 (got B=%d)", B);
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must be >= 1 with cu_seqlens", num_seqs);
+    N = num_seqs;
+  } else {
+    if (num_seqs != 0 && num_seqs != B)
+      return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must equal B=%d without cu_seqlens", num_seqs, B);
+    N = B;
+  }
+  if (N < 1) {
+    // B == 0 without cu_seqlens: nothing to compute and no state to write
+    return KDA_OK;
+  }
+  if (total > 0 && (!q || !k || !v || !g || !beta || !out))
+    return fail(KDA_ERR_INVALID_ARG, "q, k, v, g, beta and out must be non-NULL");
+  if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARG, "A_log and dt_bias must be non-NULL");
+  Layout lay;
+  const int32_t st = layout(total, H, N, cp_mode, seg_chunks, &lay);
+  if (st != KDA_OK) return st;
+  if (total == 0 && !final_state) return KDA_OK;
+  if (!workspace) return fail(KDA_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % KDA_WORKSPACE_ALIGN != 0)
+    return fail(KDA_ERR_INVALID_ARG, "workspace must be %d-byte aligned", KDA_WORKSPACE_ALIGN);
+  if ((int64_t)workspace_bytes < lay.off[KDA_WS_TOTAL])
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %lld", workspace_bytes,
+                (long long)lay.off[KDA_WS_TOTAL]);
+
+  // ---- carve ----
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kda::Tables t;
+  t.counters = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_COUNTERS]);
+  t.seq_start = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_START]);
+  t.seq_len = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_LEN]);
+  t.seq_chunk_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_CHUNK_OFF]);
+  t.seq_seg_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_SEG_OFF]);
+  t.chunk_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_CHUNK_TAB]);
+  t.seg_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_TAB]);
+  uint8_t* rec = ws + lay.off[KDA_WS_CHUNK_REC];
+  const bool cp = lay.seg > 0;
+  float* segM = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;
+  float* segR = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
+  float* segS = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_S]) : nullptr;
+  const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
+  const int64_t ms = lay.off[KDA_WS_MAX_SEGS];
+
+  kda::Problem p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g);
+  p.beta = static_cast<const uint16_t*>(beta);
+  p.out = static_cast<uint16_t*>(out);
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.init_state = initial_state;
+  p.final_state = final_state;
+  p.state_fp32 = state_dtype == KDA_STATE_FP32;
+  p.scale = scale;
+  p.lower_bound = lower_bound;
+  p.H = H;
+  p.N = N;
+  p.total_tokens = total;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    StageTimer tm(KDA_STAGE_INDEX, s);
+    e = kda::launch_index(cu_seqlens, N, T, total, lay.seg, mc, ms, t, s);
+  }
+  if (e == hipSuccess) {
+    StageTimer tm(KDA_STAGE_PREP, s);
+    e = kda::launch_prep(p, t, rec, mc, s);
+  }
+  if (e == hipSuccess) {
+    StageTimer tm(KDA_STAGE_RECUR0, s);
+    e = kda::launch_recur(p, t, rec, segM, segR, segS, ms, 0, s);
+  }
+  if (cp) {
+    if (e == hipSuccess) {
+      StageTimer tm(KDA_STAGE_MERGE, s);
+      e = kda::launch_merge(p, t, segM, segR, segS, s);
+    }
+    if (e == hipSuccess) {
+      StageTimer tm(KDA_STAGE_RECUR1, s);
+      e = kda::launch_recur(p, t, rec, segM, segR, segS, ms, 1, s);
+    }
+  }
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+int32_t kda_profile_enable(int32_t enable) {
+  g_prof.on = enable != 0;
+  return KDA_OK;
+}
+
+int32_t kda_profile_collect(double* stage_ms, int64_t* stage_calls, int32_t n_stages) {
+  int32_t status = KDA_OK;
+  for (auto& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      status = fail(KDA_ERR_HIP, "event timing failed");
+    } else if (r.stage < n_stages) {
+      if (stage_ms) stage_ms[r.stage] += ms;
+      if (stage_calls) stage_calls[r.stage] += 1;
+    }
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  return status;
+}
+
+const char* kda_strerror(int32_t status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KDA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+const char* kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

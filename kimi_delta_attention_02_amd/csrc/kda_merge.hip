@@ -1,0 +1,87 @@
+// Segment merge ("merge" on the cuLA PR #106 page: K1 once -> pre_scan ->
+// merge -> segment K2).
+//
+// For every sequence with n >= 3 segments, the state entering segment i+1 is
+// S_{i+1} = M_i S_i + R_i for i = 1 .. n-2, in fp32, where (M_i, R_i) is the
+// exact affine map of middle segment i produced by the pre-scan and S_1 was
+// written by the recurrence over segment 0.  Value columns are independent, so
+// each workgroup owns 16 of them and walks the segments of its sequence in
+// order; the products use v_mfma_f32_16x16x4_f32.  When M_i has underflowed to
+// zero the result is R_i exactly, which is what makes the segmented path
+// reproduce the serial bits once the zero-start chain has converged.
+//
+// All matrices are stored transposed ([v][k], like the state tensors).
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+constexpr int SP = 17;  // LDS pitch of the 128 x 16 column block
+}
+
+__global__ __launch_bounds__(256) void kda_merge_kernel(Problem p, Tables t, const float* __restrict__ segM,
+                                                        const float* __restrict__ segR, float* __restrict__ segS) {
+  __shared__ float Sl[D * SP];
+  const int seq = blockIdx.x;
+  const int h = blockIdx.y;
+  const int vb = blockIdx.z;  // 16-column block
+  const int s0 = t.seq_seg_off[seq];
+  const int ns = t.seq_seg_off[seq + 1] - s0;
+  if (ns < 3) return;
+  const int H = p.H;
+  const int w = threadIdx.x >> 6;
+  const int L = threadIdx.x & 63;
+  const int g = L >> 4;
+  const int c = L & 15;
+  const int v = 16 * vb + c;
+  const long long mat = (long long)D * D;
+
+  {  // S_1 -> LDS
+    const float* src = segS + ((long long)(s0 + 1) * H + h) * mat;
+    for (int e = threadIdx.x; e < D * 16; e += 256) {
+      const int k = e & (D - 1);
+      const int vv = e >> 7;
+      Sl[k * SP + vv] = src[(long long)(16 * vb + vv) * D + k];
+    }
+  }
+  __syncthreads();
+
+  for (int i = 1; i <= ns - 2; ++i) {
+    const long long base = ((long long)(s0 + i) * H + h) * mat;
+    const float* Mt = segM + base;  // Mt[p][k] = M[k][p]
+    const float* Rt = segR + base;
+    f32x4 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int to = 2 * w + u;  // output row tile
+      acc[u] = *reinterpret_cast<const f32x4*>(Rt + (long long)v * D + 16 * to + 4 * g);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int pr = 16 * tt + 4 * g + ii;  // reduction index supplied by lane group g
+          acc[u] = mfma_f32_k4(Mt[(long long)pr * D + 16 * to + c], Sl[pr * SP + c], acc[u]);
+        }
+    }
+    __syncthreads();
+    float* dst = segS + ((long long)(s0 + i + 1) * H + h) * mat;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int to = 2 * w + u;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) Sl[(16 * to + 4 * g + ii) * SP + c] = acc[u][ii];
+      *reinterpret_cast<f32x4*>(dst + (long long)v * D + 16 * to + 4 * g) = acc[u];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_merge(const Problem& p, Tables t, const float* segM, const float* segR, float* segS,
+                        hipStream_t st) {
+  if (p.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_merge_kernel, dim3((unsigned)p.N, (unsigned)p.H, D / 16), dim3(256), 0, st, p, t, segM, segR,
+                     segS);
+  return hipGetLastError();
+}
+
+}  // namespace kda

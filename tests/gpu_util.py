@@ -1,0 +1,158 @@
+"""Helpers for the GPU tests: move seeded inputs to the device, call the
+library through its binding, decode workspace records, compare to the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import kda_inputs
+from oracle import kda_oracle as O
+
+# acceptance: relative L2 <= 1e-2 and max-abs <= 3e-2 x RMS of the reference
+REL_L2 = 1e-2
+MAX_ABS_RMS = 3e-2
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_inputs(x: dict, device="cuda"):
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
+
+    d = {n: bf(x[n]) for n in ("q", "k", "v", "g", "beta")}
+    d["A_log"] = torch.from_numpy(x["A_log"]).to(device)
+    d["dt_bias"] = torch.from_numpy(x["dt_bias"]).to(device)
+    s = x["initial_state"]
+    if s is None:
+        d["initial_state"] = None
+    elif s.dtype == np.uint16:
+        d["initial_state"] = bf(s)
+    else:
+        d["initial_state"] = torch.from_numpy(s).to(device)
+    d["cu_seqlens"] = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).to(device)
+    return d
+
+
+def run_gpu(w, x, d, cp_mode="auto", seg_chunks=0, want_final=True, init=True, workspace=None, alias=False):
+    """One library call; returns (out tensor, final tensor or None, workspace)."""
+    import torch
+    import kimi_delta_attention_02_amd as kda
+
+    N = w.N
+    sdt = torch.float32 if w.state_dtype == "fp32" else torch.bfloat16
+    init_t = d["initial_state"] if init else None
+    final = None
+    if want_final:
+        if alias and init_t is not None:
+            init_t = init_t.clone()
+            final = init_t
+        else:
+            final = torch.full((N, w.H, 128, 128), float("nan"), dtype=sdt, device=d["q"].device)
+    out = torch.full_like(d["q"], float("nan"))
+    if workspace is None:
+        need = kda.get_workspace_size(w.B * w.T, w.H, N, cp_mode, seg_chunks)
+        workspace = torch.empty(need, dtype=torch.uint8, device=d["q"].device)
+    kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], out, A_log=d["A_log"], dt_bias=d["dt_bias"],
+            lower_bound=x["lower_bound"], workspace=workspace, initial_state=init_t, final_state=final,
+            cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode, seg_chunks=seg_chunks)
+    torch.cuda.synchronize()
+    return out, final, workspace
+
+
+def to_f64(t) -> np.ndarray:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return O.widen(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.double().cpu().numpy()
+
+
+def spans(w, x):
+    return O.sequence_spans(w.B, w.T, x["cu_seqlens"])
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    diff = got - ref
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.max(np.abs(diff))) if diff.size else 0.0
+    return rel, mx, rms
+
+
+def assert_close(got, ref, what):
+    rel, mx, rms = errors(got, ref)
+    say(f"{what}: rel_l2={rel:.3e} max_abs={mx:.3e} rms={rms:.3e}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert rel <= REL_L2, f"{what}: relative L2 {rel:.3e} > {REL_L2}"
+    assert mx <= MAX_ABS_RMS * rms, f"{what}: max-abs {mx:.3e} > {MAX_ABS_RMS} x rms {rms:.3e}"
+
+
+def check_against_oracle(w, x, out, final, seqs=None, heads=None, init=True, final_dtype=None):
+    """Compare the selected chains with the fp64 oracle (token recurrence)."""
+    outs, finals = O.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["A_log"], x["dt_bias"], x["scale"],
+                                 x["lower_bound"], x["initial_state"] if init else None, x["cu_seqlens"],
+                                 seqs=seqs, heads=heads)
+    sp = spans(w, x)
+    seqs = list(range(len(sp))) if seqs is None else list(seqs)
+    heads = list(range(w.H)) if heads is None else list(heads)
+    got_o = []
+    ref_o = []
+    for si, i in enumerate(seqs):
+        b, t0, L = sp[i]
+        if L == 0:
+            continue
+        got_o.append(to_f64(out[b, t0:t0 + L][:, heads]).reshape(-1))
+        ref_o.append(outs[si].reshape(-1))
+    if got_o:
+        assert_close(np.concatenate(got_o), np.concatenate(ref_o), f"{w.name} out")
+    if final is not None:
+        g = to_f64(final[seqs][:, heads])
+        ref = finals
+        if final_dtype == "bf16":
+            ref = O.round_to_bf16(ref)
+        assert_close(g.reshape(-1), ref.reshape(-1), f"{w.name} final_state")
+    return outs, finals
+
+
+def read_ws(ws, offs, name, count, dtype):
+    import torch
+
+    nbytes = count * np.dtype(dtype).itemsize
+    a = ws[offs[name]:offs[name] + nbytes].cpu().numpy()
+    return a.view(dtype)
+
+
+def decode_record(buf: np.ndarray) -> dict:
+    """Decode one chunk record (bytes) into plain [token][channel] arrays."""
+    W = np.zeros((16, 128))
+    Q = np.zeros((16, 128))
+    Kh = np.zeros((16, 128))
+    Ut = np.zeros((16, 128))
+    Aqk = np.zeros((16, 16))
+    w16 = O.widen(buf[0:4096].view(np.uint16).reshape(4, 64, 8))
+    q16 = O.widen(buf[4096:8192].view(np.uint16).reshape(4, 64, 8))
+    kh16 = O.widen(buf[8192:12288].view(np.uint16).reshape(8, 64, 4))
+    ut = buf[12288:20480].view(np.float32).reshape(8, 64, 4).astype(np.float64)
+    aq = O.widen(buf[20480:20992].view(np.uint16).reshape(64, 4))
+    gc = buf[20992:21504].view(np.float32).astype(np.float64)
+    for L in range(64):
+        g, c = L // 16, L % 16
+        for s in range(4):
+            for e in range(4):
+                W[c, 32 * s + 4 * g + e] = w16[s, L, e]
+                W[c, 32 * s + 16 + 4 * g + e] = w16[s, L, 4 + e]
+                Q[c, 32 * s + 4 * g + e] = q16[s, L, e]
+                Q[c, 32 * s + 16 + 4 * g + e] = q16[s, L, 4 + e]
+        for t in range(8):
+            for e in range(4):
+                Kh[4 * g + e, 16 * t + c] = kh16[t, L, e]
+                Ut[4 * g + e, 16 * t + c] = ut[t, L, e]
+        for e in range(4):
+            Aqk[c, 4 * g + e] = aq[L, e]
+    return dict(W=W, Qbar=Q, Khat=Kh, Ut=Ut, Aqk=Aqk, gamma_C=gc)

@@ -1,0 +1,121 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, plans and sizes workspaces consistently, and rejects
+invalid calls before any HIP call is made (so these run on a CPU host)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import kimi_delta_attention_02_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path()):
+        pytest.fail("libkda.so is not built (python -m kimi_delta_attention_02_amd.build)")
+    return kda.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "kda_fwd" in names and "kda_get_workspace_size" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in names:
+        getattr(lib, n)  # resolvable through ctypes
+
+
+def test_version_and_strerror(lib):
+    assert b"gfx950" in lib.kda_version()
+    assert lib.kda_strerror(0) == b"ok"
+    assert lib.kda_strerror(-3) == b"workspace too small"
+
+
+def test_plan_modes():
+    # OFF is always serial; FORCE always splits; AUTO splits only few, long chains
+    assert kda.plan_seg_chunks(65536, 16, 1, "off") == 0
+    assert kda.plan_seg_chunks(1024, 16, 1, "force") > 0
+    assert kda.plan_seg_chunks(65536, 16, 1, "auto") > 0
+    assert kda.plan_seg_chunks(8 * 8192, 32, 8, "auto") == 0  # 256 chains fill the chip
+    assert kda.plan_seg_chunks(1023, 16, 1, "auto") == 0  # too short to split
+    assert kda.plan_seg_chunks(65536, 16, 1, "auto", 64) == 64
+    assert kda.plan_seg_chunks(65536, 16, 1, "off", 64) == 0
+    with pytest.raises(kda.KdaError):
+        kda.plan_seg_chunks(100, 0, 1)
+
+
+def test_workspace_layout_consistent():
+    for args in [(256, 2, 1, "off", 0), (8192, 16, 2, "auto", 0), (79890, 16, 7, "force", 64), (0, 4, 3, "auto", 0)]:
+        size = kda.get_workspace_size(*args)
+        off = kda.workspace_offsets(*args)
+        assert off["total"] == size
+        prev = -1
+        for name in kda.WS_FIELDS[:11]:
+            assert off[name] % kda.WS_ALIGN == 0
+            assert off[name] >= prev
+            prev = off[name]
+        total, H, N = args[0], args[1], args[2]
+        assert off["max_chunks"] == (total + 15 * N) // 16
+        seg = kda.plan_seg_chunks(*args)
+        assert off["max_segs"] == (off["max_chunks"] // seg + N if seg else N)
+        assert off["seg_m"] - off["chunk_rec"] >= off["max_chunks"] * H * kda.CHUNK_REC_BYTES
+        if seg == 0:
+            assert off["seg_s"] == off["seg_r"] == off["seg_m"]
+
+
+def _call(lib, **kw):
+    """kda_fwd with fake, never-dereferenced pointers (every case here fails
+    validation before any device access or HIP call)."""
+    P = ctypes.c_void_p(0x10000)
+    a = dict(q=P, k=P, v=P, g=P, beta=P, scale=0.1, out=P, A_log=P, dt_bias=P, lower_bound=-1.0,
+             initial_state=None, final_state=None, state_dtype=1, cu_seqlens=None, num_seqs=0, B=1, T=64, H=2,
+             D=128, workspace=ctypes.c_void_p(0x100000), workspace_bytes=1 << 40, cp_mode=0, seg_chunks=0,
+             stream=None)
+    a.update(kw)
+    return lib.kda_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(D=64), -2, "head dimension"),
+    (dict(lower_bound=0.5), -1, "lower_bound"),
+    (dict(lower_bound=-5.5), -1, "lower_bound"),
+    (dict(lower_bound=float("nan")), -1, "lower_bound"),
+    (dict(scale=float("inf")), -1, "scale"),
+    (dict(state_dtype=7), -1, "state_dtype"),
+    (dict(B=2, cu_seqlens=ctypes.c_void_p(0x2000), num_seqs=2), -1, "B == 1"),
+    (dict(cu_seqlens=ctypes.c_void_p(0x2000), num_seqs=0), -1, "num_seqs"),
+    (dict(B=2, num_seqs=3), -1, "num_seqs"),
+    (dict(q=None), -1, "non-NULL"),
+    (dict(out=None), -1, "non-NULL"),
+    (dict(A_log=None), -1, "A_log"),
+    (dict(H=0), -1, "H="),
+    (dict(T=-1), -1, ">= 0"),
+    (dict(workspace=None), -1, "workspace"),
+    (dict(workspace=ctypes.c_void_p(0x100010)), -1, "aligned"),
+    (dict(workspace_bytes=1024), -3, "need"),
+    (dict(cp_mode=5), -1, "cp_mode"),
+    (dict(seg_chunks=-2), -1, "seg_chunks"),
+])
+def test_fwd_rejects_before_launch(lib, kw, status, msg):
+    st = _call(lib, **kw)
+    assert st == status
+    assert msg in lib.kda_last_error().decode()
+
+
+def test_empty_call_is_a_no_op(lib):
+    # B*T == 0 without a final state returns OK with no launch (and no HIP call)
+    assert _call(lib, T=0) == 0
+    assert _call(lib, B=0, T=10) == 0

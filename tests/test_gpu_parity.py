@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs,
+plus the bitwise invariants of the GPU path itself.  All calls go through the
+C ABI (via the ctypes binding)."""
+import numpy as np
+import pytest
+
+import kda_inputs
+from oracle import kda_oracle as O
+from tests.gpu_util import (assert_close, check_against_oracle, decode_record, dev_inputs, read_ws, run_gpu, say,
+                            to_f64)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kimi_delta_attention_02_amd as kda
+
+    kda.load_library()
+
+
+def _case(w, cp_mode="auto", seg_chunks=0, seqs=None, heads=None, init=True, want_final=True, alias=False):
+    say(f"case {w.name} seed={w.seed} cp={cp_mode} seg={seg_chunks} init={init} final={want_final} alias={alias}")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out, final, ws = run_gpu(w, x, d, cp_mode, seg_chunks, want_final=want_final, init=init, alias=alias)
+    check_against_oracle(w, x, out, final, seqs=seqs, heads=heads, init=init and x["initial_state"] is not None,
+                         final_dtype=w.state_dtype)
+    return x, d, out, final, ws
+
+
+# ------------------------------------------------------------------- small shapes, every chain checked
+def test_config1_full():
+    _case(kda_inputs.WORKLOADS["cfg1"])
+
+
+@pytest.mark.parametrize("lens", [[1], [15], [16], [17], [33, 1, 16, 70], [0, 5, 0, 40]])
+def test_ragged_varlen(lens):
+    _case(kda_inputs.custom(seqlens=lens, H=3, lower_bound=-5.0, seed=sum(lens) + len(lens), name=f"varlen{lens}"))
+
+
+@pytest.mark.parametrize("lb", [0.0, -1.0, -5.0])
+def test_lower_bound_range(lb):
+    _case(kda_inputs.custom(B=2, T=100, H=2, lower_bound=lb, seed=21, name=f"lb{lb}"))
+
+
+@pytest.mark.parametrize("init,final", [(False, False), (False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("sdt", ["fp32", "bf16"])
+def test_state_presence_combinations(init, final, sdt):
+    w = kda_inputs.custom(B=2, T=50, H=2, state_dtype=sdt, seed=22, name=f"state_{sdt}_{init}_{final}")
+    _case(w, init=init, want_final=final)
+
+
+@pytest.mark.parametrize("sdt", ["fp32", "bf16"])
+def test_final_state_may_alias_initial(sdt):
+    _case(kda_inputs.custom(B=1, T=90, H=2, state_dtype=sdt, seed=23, name=f"alias_{sdt}"), alias=True)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3])
+def test_segment_path_small(seg):
+    w = kda_inputs.custom(seqlens=[200, 16, 48, 1, 130], H=2, lower_bound=-1.0, seed=24, name=f"segsmall{seg}")
+    _case(w, cp_mode="force", seg_chunks=seg)
+
+
+def test_segment_path_slow_decay():
+    # lb = 0: no decay at all, the merge must carry the full transition M
+    w = kda_inputs.custom(B=1, T=400, H=2, lower_bound=0.0, seed=25, name="segnodecay")
+    _case(w, cp_mode="force", seg_chunks=4)
+
+
+def test_zero_tokens_with_final_state():
+    w = kda_inputs.custom(seqlens=[0, 0], H=2, seed=26, name="empty")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out, final, _ = run_gpu(w, x, d)
+    np.testing.assert_array_equal(to_f64(final), O.widen(x["initial_state"]))
+
+
+# ------------------------------------------------------------------- K1 records against the oracle's chunk quantities
+def test_chunk_records_match_oracle():
+    w = kda_inputs.custom(seqlens=[40, 16, 7], H=2, lower_bound=-5.0, seed=27, name="records")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    _, _, ws = run_gpu(w, x, d, cp_mode="off")
+    import kimi_delta_attention_02_amd as kda
+
+    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, "off", 0)
+    rec = ws[offs["chunk_rec"]:].cpu().numpy()
+    sp = O.sequence_spans(w.B, w.T, x["cu_seqlens"])
+    gchunk = 0
+    for i, (b, t0, L) in enumerate(sp):
+        for c0 in range(0, L, 16):
+            m = min(16, L - c0)
+            for h in range(w.H):
+                sl = (b, slice(t0 + c0, t0 + c0 + m), h)
+                qh = O.l2_normalize(O.widen(x["q"][sl]))
+                kh = O.l2_normalize(O.widen(x["k"][sl]))
+                lam = O.log_decay(O.widen(x["g"][sl])[:, None, :], x["A_log"][h:h + 1], x["dt_bias"][h:h + 1],
+                                  x["lower_bound"])[:, 0]
+                bt = O.sigmoid(O.widen(x["beta"][sl]))
+                ref = O.chunk_quantities(qh, kh, O.widen(x["v"][sl]), lam, bt, x["scale"])
+                base = (gchunk * w.H + h) * kda.CHUNK_REC_BYTES
+                got = decode_record(rec[base:base + kda.CHUNK_REC_BYTES])
+                for name in ("W", "Qbar", "Khat", "Ut", "Aqk"):
+                    assert_close(got[name][:m].reshape(-1), ref[name].reshape(-1), f"chunk {gchunk} h{h} {name}")
+                    assert np.all(got[name][m:] == 0), f"{name} rows past the chunk end must be zero"
+                np.testing.assert_allclose(got["gamma_C"], ref["gamma_C"], rtol=2e-5, atol=0)
+            gchunk += 1
+
+
+# ------------------------------------------------------------------- index tables, bit-exact
+@pytest.mark.parametrize("lens,seg", [([1023, 1025, 1, 16, 4097, 8191, 65537], 64), ([0, 1, 15, 16, 17, 0], 1),
+                                      ([65536] + [1024] * 5, 0), ([65537], 37)])
+def test_index_tables_bit_exact(lens, seg):
+    w = kda_inputs.custom(seqlens=lens, H=1, seed=28, name="tables")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    mode = "force" if seg else "off"
+    _, _, ws = run_gpu(w, x, d, cp_mode=mode, seg_chunks=seg, want_final=False)
+    import kimi_delta_attention_02_amd as kda
+
+    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, mode, seg)
+    ref = O.index_tables(lens, 16, seg if seg else None)
+    N = len(lens)
+    cnt = read_ws(ws, offs, "counters", 4, np.int32)
+    assert cnt[0] == ref["seq_chunk_off"][-1] and cnt[1] == ref["seq_seg_off"][-1] and cnt[2] == 0
+    np.testing.assert_array_equal(read_ws(ws, offs, "seq_chunk_off", N + 1, np.int32), ref["seq_chunk_off"])
+    np.testing.assert_array_equal(read_ws(ws, offs, "seq_seg_off", N + 1, np.int32), ref["seq_seg_off"])
+    nch, nsg = int(cnt[0]), int(cnt[1])
+    np.testing.assert_array_equal(read_ws(ws, offs, "chunk_tab", 2 * nch, np.int32).reshape(-1, 2), ref["chunk_tab"])
+    np.testing.assert_array_equal(read_ws(ws, offs, "seg_tab", 4 * nsg, np.int32).reshape(-1, 4), ref["seg_tab"])
+    np.testing.assert_array_equal(read_ws(ws, offs, "seq_len", N, np.int32), lens)
+
+
+def test_malformed_offsets_are_clamped():
+    """Decreasing or out-of-range offsets are clamped into a non-decreasing
+    sequence inside [0, total] (memory-safe), and flagged in the counters."""
+    w = kda_inputs.custom(seqlens=[10, 30, 20], H=1, seed=29, name="badcu")
+    x = kda_inputs.make_inputs(w)
+    x["cu_seqlens"] = np.array([0, 40, 25, 90], dtype=np.int32)  # 25 < 40; 90 > total 60
+    d = dev_inputs(x)
+    _, _, ws = run_gpu(w, x, d, cp_mode="off", want_final=False)
+    import kimi_delta_attention_02_amd as kda
+
+    offs = kda.workspace_offsets(60, 1, 3, "off", 0)
+    np.testing.assert_array_equal(read_ws(ws, offs, "seq_start", 4, np.int32), [0, 40, 40, 60])
+    np.testing.assert_array_equal(read_ws(ws, offs, "seq_len", 3, np.int32), [40, 0, 20])
+    assert read_ws(ws, offs, "counters", 4, np.int32)[2] != 0
+
+
+# ------------------------------------------------------------------- bitwise invariants of the GPU path
+def test_deterministic_and_varlen_equals_separate_calls():
+    lens = [37, 16, 80, 5]
+    w = kda_inputs.custom(seqlens=lens, H=2, seed=30, name="bitwise")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out1, fin1, _ = run_gpu(w, x, d, cp_mode="off")
+    out2, fin2, _ = run_gpu(w, x, d, cp_mode="off")
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)) and torch.equal(fin1, fin2)
+    cu = x["cu_seqlens"]
+    for i, L in enumerate(lens):
+        wi = kda_inputs.custom(B=1, T=L, H=2, seed=30, name="part")
+        xi = dict(x)
+        for n in ("q", "k", "v", "g", "beta"):
+            xi[n] = np.ascontiguousarray(x[n][:, cu[i]:cu[i + 1]])
+        xi["initial_state"] = x["initial_state"][i:i + 1]
+        xi["cu_seqlens"] = None
+        di = dev_inputs(xi)
+        oi, fi, _ = run_gpu(wi, xi, di, cp_mode="off")
+        assert torch.equal(oi.view(torch.int16), out1[:, cu[i]:cu[i + 1]].view(torch.int16))
+        assert torch.equal(fi, fin1[i:i + 1])
+
+
+def test_state_chaining_bitwise():
+    """fwd(x1 || x2) == fwd(x2; S0 = final(x1)) bit for bit when len(x1) % 16 == 0 (fp32 state)."""
+    w = kda_inputs.custom(B=1, T=160, H=2, seed=31, name="chain")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out, fin, _ = run_gpu(w, x, d, cp_mode="off")
+    parts = []
+    state = d["initial_state"]
+    for a, b in ((0, 64), (64, 160)):
+        wi = kda_inputs.custom(B=1, T=b - a, H=2, seed=31, name="chainpart")
+        xi = dict(x)
+        for n in ("q", "k", "v", "g", "beta"):
+            xi[n] = np.ascontiguousarray(x[n][:, a:b])
+        di = dev_inputs(xi)
+        di["initial_state"] = state
+        oi, fi, _ = run_gpu(wi, xi, di, cp_mode="off")
+        parts.append(oi)
+        state = fi
+    assert torch.equal(torch.cat(parts, 1).view(torch.int16), out.view(torch.int16))
+    assert torch.equal(state, fin)
+
+
+# ------------------------------------------------------------------- the five workloads at full size
+def _full(name, seqs, heads, cp_mode="auto"):
+    w = kda_inputs.WORKLOADS[name]
+    return _case(w, cp_mode=cp_mode, seqs=seqs, heads=heads)
+
+
+def test_config2_full_size():
+    _full("cfg2", seqs=[0, 1], heads=[0, 7, 15])
+
+
+def test_config3_full_size():
+    _full("cfg3", seqs=[0, 1, 2, 3, 4, 5, 6], heads=[3])
+
+
+def test_config5_full_size():
+    _full("cfg5", seqs=[0, 7], heads=[0, 31])
+
+
+@pytest.mark.parametrize("name", ["cfg4a", "cfg4b"])
+def test_config4_segmented_bit_identical_to_serial(name):
+    w = kda_inputs.WORKLOADS[name]
+    say(f"case {name} serial vs segmented")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
+    check_against_oracle(w, x, out_s, fin_s, seqs=[0] if name == "cfg4a" else [0, 5], heads=[5],
+                         final_dtype=w.state_dtype)
+    for seg in (0, 64):
+        out_c, fin_c, _ = run_gpu(w, x, d, cp_mode="force", seg_chunks=seg)
+        same_o = torch.equal(out_c.view(torch.int16), out_s.view(torch.int16))
+        same_f = torch.equal(fin_c, fin_s)
+        say(f"{name} seg={seg}: out identical={same_o} final identical={same_f}")
+        assert same_o and same_f
