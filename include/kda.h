@@ -128,7 +128,7 @@ typedef enum {
   KDA_WS_NUM_OFFSETS
 } kda_ws_offset;
 
-#define KDA_CHUNK_REC_BYTES 21504
+#define KDA_CHUNK_REC_BYTES 26112
 
 int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
                               int32_t seg_chunks, int64_t* offs);

@@ -45,7 +45,7 @@ _lib = None
 
 HEAD_DIM = 128
 CHUNK = 16
-CHUNK_REC_BYTES = 21504
+CHUNK_REC_BYTES = 26112
 WS_ALIGN = 256
 WS_FIELDS = [
     "counters", "seq_start", "seq_len", "seq_chunk_off", "seq_seg_off", "chunk_tab", "seg_tab",
@@ -102,6 +102,10 @@ def load_library():
 
 
 def _cp(cp_mode) -> int:
+    if isinstance(cp_mode, int) and not isinstance(cp_mode, bool):
+        if cp_mode not in (0, 1, 2):
+            raise ValueError(f"cp_mode must be 0 (auto), 1 (off) or 2 (force), got {cp_mode}")
+        return cp_mode
     if isinstance(cp_mode, str):
         cp_mode = cp_mode.lower()
     if cp_mode not in _CP:

@@ -26,19 +26,24 @@ constexpr int D = KDA_HEAD_DIM;  // K = V = 128
 constexpr int C = KDA_CHUNK;     // 16 tokens per chunk
 
 // ---- chunk record layout (bytes) ----
-// W   : 4 k-steps x 64 lanes x 16 B  (bf16x8: W[c][32s+4g+0..3], W[c][32s+16+4g+0..3])
-// Q   : 4 k-steps x 64 lanes x 16 B  (same arrangement for Qbar)
-// KH  : 8 row tiles x 64 lanes x 8 B (bf16x4: Khat[4g+0..3][16t+c])
-// UT  : 8 col tiles x 64 lanes x 16 B (fp32x4: Ut[4g+0..3][16j+c])
-// AQK : 64 lanes x 8 B              (bf16x4: Aqk[c][4g+0..3], lower-inclusive)
-// GC  : 128 x fp32                  (gamma_C per key channel)
+// W    : 4 k-steps x 64 lanes x 16 B (bf16x8: W[c][32s+4g+0..3], W[c][32s+16+4g+0..3])
+// Q    : 4 k-steps x 64 lanes x 16 B (same arrangement for Qbar)
+// KH_HI: 8 row tiles x 64 lanes x 8 B (bf16x4: Khat[4g+0..3][16t+c], high part)
+// KH_LO: same, low part (Khat - bf16(Khat), rounded to bf16)
+// UT   : 8 col tiles x 64 lanes x 16 B (fp32x4: Ut[4g+0..3][16j+c])
+// AQK_HI / AQK_LO : 64 lanes x 8 B (bf16x4: Aqk[c][4g+0..3], lower-inclusive, high / low part)
+// GC   : 128 x fp32 (gamma_C per key channel)
+// A value x stored as a high/low pair is x_hi = bf16(x), x_lo = bf16(x - x_hi);
+// products with such an operand carry ~16 mantissa bits instead of 8.
 constexpr int REC_W = 0;
 constexpr int REC_Q = 4096;
-constexpr int REC_KH = 8192;
-constexpr int REC_UT = 12288;
-constexpr int REC_AQK = 20480;
-constexpr int REC_GC = 20992;
-constexpr int REC_BYTES = 21504;
+constexpr int REC_KH_HI = 8192;
+constexpr int REC_KH_LO = 12288;
+constexpr int REC_UT = 16384;
+constexpr int REC_AQK_HI = 24576;
+constexpr int REC_AQK_LO = 25088;
+constexpr int REC_GC = 25600;
+constexpr int REC_BYTES = 26112;
 static_assert(REC_BYTES == KDA_CHUNK_REC_BYTES, "record size");
 
 // ---- counters block ----
@@ -118,6 +123,20 @@ __device__ __forceinline__ u32x2 pack4(f32x4 x) {
   r.x = pack2(x[0], x[1]);
   r.y = pack2(x[2], x[3]);
   return r;
+}
+
+// x = hi + lo + O(2^-16 |x|): hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ float hi_part(float x) { return __uint_as_float((uint32_t)f32_to_bf16(x) << 16); }
+
+__device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo) {
+  f32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = hi_part(x[i]);
+    l[i] = x[i] - h[i];
+  }
+  hi = pack4(h);
+  lo = pack4(l);
 }
 
 __device__ __forceinline__ i16x4 as_i16x4(u32x2 x) { return __builtin_bit_cast(i16x4, x); }

@@ -4,8 +4,8 @@
 // One wavefront per (chunk, head).  For the chunk's m <= 16 tokens (rows past
 // m are zero keys/values with zero log decay and zero beta, so they change
 // nothing) it computes, in fp32:
-//   q^ = q / sqrt(|q|^2 + 1e-6), k^ likewise         (use_qk_l2norm_in_kernel)
-//   b  = sigmoid(beta)                                 (use_beta_sigmoid_in_kernel)
+//   q^ = q / sqrt(|q|^2 + 1e-6), k^ likewise           (use_qk_l2norm_in_kernel)
+//   b  = sigmoid(beta)                                   (use_beta_sigmoid_in_kernel)
 //   l  = lower_bound * sigmoid(exp(A_log) (g + dt_bias)) (gate in kernel, safe gate;
 //        lower_bound in [-5, 0] keeps |cumulative l| <= 80 over 16 tokens, so
 //        exp(+-G) below stays finite in fp32 and bf16)
@@ -13,14 +13,20 @@
 //   Qbar = scale q^ gamma, Kbar = k^ gamma, Ktil = k^ / gamma, Khat = Ktil gamma_C
 //   A  = StrictLower(Diag(b) Kbar Ktil^T), T = (I + A)^{-1} by forward substitution
 //   W  = T Diag(b) Kbar,  Ut = T Diag(b) V,  Aqk = LowerInclusive(Qbar Ktil^T)
-// and writes W, Qbar, Khat (bf16), Ut (fp32), Aqk (bf16) and gamma_C (fp32)
-// into the chunk record in the recurrence kernel's operand order.
+// and writes W, Qbar (bf16), Khat and Aqk (bf16 high/low pairs), Ut and
+// gamma_C (fp32) into the chunk record in the recurrence kernel's operand order.
+//
+// Precision: the small products A, Aqk, W and Ut take their operands as bf16
+// high/low pairs, each packed into one 16x16x32 MFMA (the K dimension carries
+// both halves), so they are accurate to ~2^-16 instead of bf16's 2^-8; the
+// largest outputs are ~10x the output RMS, where plain bf16 operands alone
+// would exceed a 3% of RMS error.
 //
 // Lane L owns key channels 2L and 2L+1 for all 16 tokens while loading (each
 // load instruction reads one 256-byte token row) and while forming the decays
-// (the cumulative sum runs in registers).  The bf16 tiles go to LDS twice:
-// token-major rows for the 16x16x32 products over channels, channel-major rows
-// for the 16x16x16 products over tokens.
+// (the cumulative sum runs in registers).  The bf16 tiles go through LDS:
+// token-major rows for the products over channels, then (same storage)
+// channel-major rows for the products over tokens.
 #include "kda_internal.h"
 
 namespace kda {
@@ -30,14 +36,13 @@ namespace {
 constexpr int ROWP = 136;  // token-major bf16 row pitch (272 B: 16-B aligned, conflict-free b128 reads)
 constexpr int COLP = 20;   // channel-major bf16 row pitch (40 B: conflict-free b64 reads)
 constexpr int MP = 20;     // fp32 16x16 matrix pitch (80 B: 16-B aligned rows)
+constexpr int ROWT = C * ROWP;  // one token-major tile
+constexpr int COLT = D * COLP;  // one channel-major tile
 
 struct PrepSmem {
-  uint16_t qrow[C * ROWP];
-  uint16_t kbrow[C * ROWP];
-  uint16_t ktrow[C * ROWP];
-  uint16_t kbcol[D * COLP];
-  uint16_t khcol[D * COLP];
-  uint16_t vcol[D * COLP];
+  // phase 1: Kbar hi/lo, Ktil hi/lo, Qbar hi/lo as token-major rows (6 tiles);
+  // phase 2: Kbar hi/lo, Khat hi/lo, V as channel-major rows (5 tiles)
+  uint16_t buf[6 * ROWT > 5 * COLT ? 6 * ROWT : 5 * COLT];
   float A[C * MP];
   float Tp[C * MP];
   float beta[C];
@@ -57,6 +62,43 @@ __device__ __forceinline__ void store_col16(uint16_t* row, const float* x) {
     w.y = pack2(x[4 * i + 2], x[4 * i + 3]);
     p[i] = w;
   }
+}
+
+// writes hi = bf16(x) and lo = bf16(x - hi) for 16 tokens of one channel
+__device__ __forceinline__ void store_col16_split(uint16_t* row_hi, uint16_t* row_lo, const float* x) {
+  float h[C], l[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    h[i] = hi_part(x[i]);
+    l[i] = x[i] - h[i];
+  }
+  store_col16(row_hi, h);
+  store_col16(row_lo, l);
+}
+
+__device__ __forceinline__ void store_row2_split(uint16_t* hi, uint16_t* lo, int off, float a, float b) {
+  const float ha = hi_part(a), hb = hi_part(b);
+  *reinterpret_cast<uint32_t*>(hi + off) = pack2(ha, hb);
+  *reinterpret_cast<uint32_t*>(lo + off) = pack2(a - ha, b - hb);
+}
+
+// sum_k X[m][k] Y[n][k] over the 128 channels of two token-major tiles given as
+// high/low pairs: X_hi Y_hi + X_hi Y_lo + X_lo Y_hi (4 k-steps of 32 channels)
+__device__ __forceinline__ f32x4 rows_dot_split(const uint16_t* xh, const uint16_t* xl, const uint16_t* yh,
+                                                const uint16_t* yl, int c, int g) {
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int o = c * ROWP + 32 * s + 8 * g;
+    const u32x4 a_h = *reinterpret_cast<const u32x4*>(xh + o);
+    const u32x4 a_l = *reinterpret_cast<const u32x4*>(xl + o);
+    const u32x4 b_h = *reinterpret_cast<const u32x4*>(yh + o);
+    const u32x4 b_l = *reinterpret_cast<const u32x4*>(yl + o);
+    acc = mfma_k32(a_h, b_h, acc);
+    acc = mfma_k32(a_h, b_l, acc);
+    acc = mfma_k32(a_l, b_h, acc);
+  }
+  return acc;
 }
 
 }  // namespace
@@ -152,51 +194,34 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(Problem p, Tables t, uint8
   const float gC1 = __expf(G1);
   reinterpret_cast<f32x2*>(r + REC_GC)[L] = f32x2{gC0, gC1};
 
-  float qb0[C], qb1[C], kb0[C], kb1[C], kt0[C], kt1[C];
+  uint16_t* const kbh = sm.buf;
+  uint16_t* const kbl = sm.buf + ROWT;
+  uint16_t* const kth = sm.buf + 2 * ROWT;
+  uint16_t* const ktl = sm.buf + 3 * ROWT;
+  uint16_t* const qbh = sm.buf + 4 * ROWT;
+  uint16_t* const qbl = sm.buf + 5 * ROWT;
+  float kb0[C], kb1[C], kt0[C], kt1[C];
 #pragma unroll
   for (int i = 0; i < C; ++i) {
-    const float sq = p.scale * lane_read(rn, 2 * i);     // scale / |q_i|
-    const float rk = lane_read(rn, 2 * (C + i));         // 1 / |k_i|
-    const float e0 = __expf(l0[i]), e1 = __expf(l1[i]);  // gamma
+    const float sq = p.scale * lane_read(rn, 2 * i);       // scale / |q_i|
+    const float rk = lane_read(rn, 2 * (C + i));           // 1 / |k_i|
+    const float e0 = __expf(l0[i]), e1 = __expf(l1[i]);    // gamma
     const float i0 = __expf(-l0[i]), i1 = __expf(-l1[i]);  // 1 / gamma
     const float kh0 = k0[i] * rk, kh1 = k1[i] * rk;
-    qb0[i] = q0[i] * sq * e0;
-    qb1[i] = q1[i] * sq * e1;
     kb0[i] = kh0 * e0;
     kb1[i] = kh1 * e1;
     kt0[i] = kh0 * i0;
     kt1[i] = kh1 * i1;
-    *reinterpret_cast<uint32_t*>(&sm.qrow[i * ROWP + c0]) = pack2(qb0[i], qb1[i]);
-    *reinterpret_cast<uint32_t*>(&sm.kbrow[i * ROWP + c0]) = pack2(kb0[i], kb1[i]);
-    *reinterpret_cast<uint32_t*>(&sm.ktrow[i * ROWP + c0]) = pack2(kt0[i], kt1[i]);
-  }
-  {
-    float kh0c[C], kh1c[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      kh0c[i] = kt0[i] * gC0;
-      kh1c[i] = kt1[i] * gC1;
-    }
-    store_col16(&sm.kbcol[c0 * COLP], kb0);
-    store_col16(&sm.kbcol[(c0 + 1) * COLP], kb1);
-    store_col16(&sm.khcol[c0 * COLP], kh0c);
-    store_col16(&sm.khcol[(c0 + 1) * COLP], kh1c);
-    store_col16(&sm.vcol[c0 * COLP], v0);
-    store_col16(&sm.vcol[(c0 + 1) * COLP], v1);
+    const int o = i * ROWP + c0;
+    store_row2_split(kbh, kbl, o, kb0[i], kb1[i]);
+    store_row2_split(kth, ktl, o, kt0[i], kt1[i]);
+    store_row2_split(qbh, qbl, o, q0[i] * sq * e0, q1[i] * sq * e1);
   }
   __syncthreads();
 
   // ---- A_raw = Kbar Ktil^T and Aqk^T = Ktil Qbar^T over the 128 channels ----
-  f32x4 Araw = zero4(), AqkT = zero4();
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int o = c * ROWP + 32 * s + 8 * g;
-    const u32x4 kb = *reinterpret_cast<const u32x4*>(&sm.kbrow[o]);
-    const u32x4 kt = *reinterpret_cast<const u32x4*>(&sm.ktrow[o]);
-    const u32x4 qb = *reinterpret_cast<const u32x4*>(&sm.qrow[o]);
-    Araw = mfma_k32(kb, kt, Araw);  // D[4g+i][c] = Kbar_{4g+i} . Ktil_c
-    AqkT = mfma_k32(kt, qb, AqkT);  // D[4g+i][c] = Ktil_{4g+i} . Qbar_c = Aqk[c][4g+i]
-  }
+  const f32x4 Araw = rows_dot_split(kbh, kbl, kth, ktl, c, g);  // D[4g+i][c] = Kbar_{4g+i} . Ktil_c
+  const f32x4 AqkT = rows_dot_split(kth, ktl, qbh, qbl, c, g);  // D[4g+i][c] = Aqk[c][4g+i]
   {
     f32x4 aq;
 #pragma unroll
@@ -205,9 +230,39 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(Problem p, Tables t, uint8
       sm.A[row * MP + c] = (c < row) ? sm.beta[row] * Araw[i] : 0.f;
       aq[i] = (row <= c) ? AqkT[i] : 0.f;
     }
-    reinterpret_cast<u32x2*>(r + REC_AQK)[L] = pack4(aq);
+    u32x2 ah, al;
+    split4(aq, ah, al);
+    reinterpret_cast<u32x2*>(r + REC_AQK_HI)[L] = ah;
+    reinterpret_cast<u32x2*>(r + REC_AQK_LO)[L] = al;
+  }
+  // Qbar (high part) in the recurrence's operand order, before the rows are reused
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(&qbh[c * ROWP + 32 * s + 4 * g]);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(&qbh[c * ROWP + 32 * s + 16 + 4 * g]);
+    reinterpret_cast<u32x4*>(r + REC_Q)[s * 64 + L] = cat(lo, hi);
   }
   __syncthreads();
+
+  // ---- phase 2: channel-major tiles (same storage) ----
+  uint16_t* const kbch = sm.buf;
+  uint16_t* const kbcl = sm.buf + COLT;
+  uint16_t* const khch = sm.buf + 2 * COLT;
+  uint16_t* const khcl = sm.buf + 3 * COLT;
+  uint16_t* const vc = sm.buf + 4 * COLT;
+  {
+    store_col16_split(&kbch[c0 * COLP], &kbcl[c0 * COLP], kb0);
+    store_col16_split(&kbch[(c0 + 1) * COLP], &kbcl[(c0 + 1) * COLP], kb1);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      kt0[i] *= gC0;  // Khat = Ktil gamma_C
+      kt1[i] *= gC1;
+    }
+    store_col16_split(&khch[c0 * COLP], &khcl[c0 * COLP], kt0);
+    store_col16_split(&khch[(c0 + 1) * COLP], &khcl[(c0 + 1) * COLP], kt1);
+    store_col16(&vc[c0 * COLP], v0);
+    store_col16(&vc[(c0 + 1) * COLP], v1);
+  }
 
   // ---- T = (I + A)^{-1} by forward substitution; lane c owns column c ----
   {
@@ -227,37 +282,39 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(Problem p, Tables t, uint8
   }
   __syncthreads();
 
-  const u32x2 tf = pack4(*reinterpret_cast<const f32x4*>(&sm.Tp[c * MP + 4 * g]));  // T'[c][4g..4g+3]
+  u32x2 tf_h, tf_l;  // T'[c][4g..4g+3] as a high/low pair
+  split4(*reinterpret_cast<const f32x4*>(&sm.Tp[c * MP + 4 * g]), tf_h, tf_l);
+  const u32x4 tf_hl = cat(tf_h, tf_l);
 
-  // ---- W^T = Kbar^T T'^T (row tiles over channels); stored as W rows ----
+  // ---- W^T = Kbar^T T'^T, one channel tile per MFMA pair:
+  // [Kbar^T_hi | Kbar^T_hi] [T'^T_hi ; T'^T_lo] + [Kbar^T_lo | Kbar^T_lo] [T'^T_hi ; T'^T_lo]
   f32x4 WT[8];
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    const u32x2 kbT = *reinterpret_cast<const u32x2*>(&sm.kbcol[(16 * tt + c) * COLP + 4 * g]);
-    WT[tt] = mfma_k16(kbT, tf, zero4());  // D[4g+i][c] = W[token c][16tt+4g+i]
+    const int o = (16 * tt + c) * COLP + 4 * g;
+    const u32x2 kh = *reinterpret_cast<const u32x2*>(&kbch[o]);
+    const u32x2 kl = *reinterpret_cast<const u32x2*>(&kbcl[o]);
+    f32x4 acc = mfma_k32(cat(kh, kh), tf_hl, zero4());
+    WT[tt] = mfma_k32(cat(kl, kl), tf_hl, acc);  // D[4g+i][c] = W[token c][16tt+4g+i]
   }
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     reinterpret_cast<u32x4*>(r + REC_W)[s * 64 + L] = cat(pack4(WT[2 * s]), pack4(WT[2 * s + 1]));
 
-  // ---- Ut = T' V (column tiles over value columns) ----
+  // ---- Ut = T' V = [T'_hi | T'_lo] [V ; V] (column tiles over value columns) ----
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const u32x2 vT = *reinterpret_cast<const u32x2*>(&sm.vcol[(16 * jj + c) * COLP + 4 * g]);
-    reinterpret_cast<f32x4*>(r + REC_UT)[jj * 64 + L] = mfma_k16(tf, vT, zero4());
+    const u32x2 vT = *reinterpret_cast<const u32x2*>(&vc[(16 * jj + c) * COLP + 4 * g]);
+    reinterpret_cast<f32x4*>(r + REC_UT)[jj * 64 + L] = mfma_k32(tf_hl, cat(vT, vT), zero4());
   }
 
-  // ---- Qbar and Khat in the recurrence's operand order ----
+  // ---- Khat high/low in the recurrence's operand order ----
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.qrow[c * ROWP + 32 * s + 4 * g]);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.qrow[c * ROWP + 32 * s + 16 + 4 * g]);
-    reinterpret_cast<u32x4*>(r + REC_Q)[s * 64 + L] = cat(lo, hi);
+  for (int tt = 0; tt < 8; ++tt) {
+    const int o = (16 * tt + c) * COLP + 4 * g;
+    reinterpret_cast<u32x2*>(r + REC_KH_HI)[tt * 64 + L] = *reinterpret_cast<const u32x2*>(&khch[o]);
+    reinterpret_cast<u32x2*>(r + REC_KH_LO)[tt * 64 + L] = *reinterpret_cast<const u32x2*>(&khcl[o]);
   }
-#pragma unroll
-  for (int tt = 0; tt < 8; ++tt)
-    reinterpret_cast<u32x2*>(r + REC_KH)[tt * 64 + L] =
-        *reinterpret_cast<const u32x2*>(&sm.khcol[(16 * tt + c) * COLP + 4 * g]);
 }
 
 hipError_t launch_prep(const Problem& p, Tables t, uint8_t* rec, int64_t max_chunks, hipStream_t st) {

@@ -31,7 +31,8 @@ struct ChunkOps {
   u32x4 W[4];
   u32x4 Q[4];
   u32x2 Kh[8];
-  u32x2 Aqk;
+  u32x2 Kl[8];
+  u32x2 Aqh, Aql;
   f32x4 Ut[NTW];
   f32x4 gC[8];
 };
@@ -43,16 +44,68 @@ __device__ __forceinline__ void load_ops(ChunkOps& o, const uint8_t* __restrict_
   if (want_out) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) o.Q[s] = reinterpret_cast<const u32x4*>(r + REC_Q)[s * 64 + L];
-    o.Aqk = reinterpret_cast<const u32x2*>(r + REC_AQK)[L];
+    o.Aqh = reinterpret_cast<const u32x2*>(r + REC_AQK_HI)[L];
+    o.Aql = reinterpret_cast<const u32x2*>(r + REC_AQK_LO)[L];
   }
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt) o.Kh[tt] = reinterpret_cast<const u32x2*>(r + REC_KH)[tt * 64 + L];
+  for (int tt = 0; tt < 8; ++tt) {
+    o.Kh[tt] = reinterpret_cast<const u32x2*>(r + REC_KH_HI)[tt * 64 + L];
+    o.Kl[tt] = reinterpret_cast<const u32x2*>(r + REC_KH_LO)[tt * 64 + L];
+  }
   if (want_ut) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) o.Ut[j] = reinterpret_cast<const f32x4*>(r + REC_UT)[(ct0 + j) * 64 + L];
   }
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) o.gC[tt] = reinterpret_cast<const f32x4*>(r + REC_GC)[4 * tt + g];
+}
+
+// One chunk of the recurrence for this wavefront's column tiles.
+//   U = Ut - W S (bf16 W and S); U kept as a high/low pair
+//   O^T = S^T Qbar^T + U^T Aqk^T     (Aqk and U as high/low pairs)
+//   S <- Diag(gamma_C) S + Khat^T U  (Khat and U as high/low pairs)
+// Every product is a 16x16x32 MFMA; the split products put both halves of a
+// 16-token reduction into the 32-long K dimension, e.g.
+//   [Khat_hi | Khat_hi] [U_hi ; U_lo] + [Khat_lo | Khat_lo] [U_hi ; U_lo].
+__device__ __forceinline__ void chunk_step(f32x4 (&S)[8][NTW], const ChunkOps& op, bool want_out, bool want_ut,
+                                           uint16_t* __restrict__ out_row, bool store) {
+  u32x2 Sb[8][NTW];
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < NTW; ++jj) Sb[tt][jj] = pack4(S[tt][jj]);
+
+  u32x4 Uhl[NTW];
+#pragma unroll
+  for (int jj = 0; jj < NTW; ++jj) {
+    f32x4 X = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) X = mfma_k32(op.W[s], cat(Sb[2 * s][jj], Sb[2 * s + 1][jj]), X);
+    const f32x4 U = want_ut ? op.Ut[jj] - X : -X;
+    u32x2 uh, ul;
+    split4(U, uh, ul);
+    Uhl[jj] = cat(uh, ul);
+  }
+
+  if (want_out) {
+#pragma unroll
+    for (int jj = 0; jj < NTW; ++jj) {
+      f32x4 Ot = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Ot = mfma_k32(cat(Sb[2 * s][jj], Sb[2 * s + 1][jj]), op.Q[s], Ot);
+      Ot = mfma_k32(Uhl[jj], cat(op.Aqh, op.Aqh), Ot);
+      Ot = mfma_k32(Uhl[jj], cat(op.Aql, op.Aql), Ot);
+      if (store) *reinterpret_cast<u32x2*>(out_row + 16 * jj) = pack4(Ot);
+    }
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < NTW; ++jj) {
+      f32x4 acc = mfma_k32(cat(op.Kh[tt], op.Kh[tt]), Uhl[jj], S[tt][jj] * op.gC[tt]);
+      S[tt][jj] = mfma_k32(cat(op.Kl[tt], op.Kl[tt]), Uhl[jj], acc);
+    }
 }
 
 }  // namespace
@@ -142,58 +195,24 @@ __global__ __launch_bounds__(256) void kda_recur_kernel(Problem p, Tables t, con
   const int first_chunk = t.seq_chunk_off[seq];
   const long long seq_tok0 = t.seq_start[seq];
   const int seq_len = t.seq_len[seq];
+  const long long rec_stride = (long long)H * REC_BYTES;
+  const uint8_t* rbase = rec + (long long)h * REC_BYTES;
+  // output element (token c of the chunk, columns 16*ct0 + 4g ..) for chunk ch
+  auto out_row = [&](int ch) -> uint16_t* {
+    const long long tok = seq_tok0 + (long long)C * (ch - first_chunk) + c;
+    return p.out + (tok * H + h) * D + 16 * ct0 + 4 * g;
+  };
+  auto stores = [&](int ch) -> bool { return c < seq_len - C * (ch - first_chunk); };
 
-  ChunkOps ops;
-  if (cb < ce) load_ops(ops, rec + ((long long)cb * H + h) * REC_BYTES, L, g, ct0, want_out, want_ut);
-
-  for (int ch = cb; ch < ce; ++ch) {
-    ChunkOps cur = ops;
-    if (ch + 1 < ce) load_ops(ops, rec + ((long long)(ch + 1) * H + h) * REC_BYTES, L, g, ct0, want_out, want_ut);
-
-    u32x2 Sb[8][NTW];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-      for (int jj = 0; jj < NTW; ++jj) Sb[tt][jj] = pack4(S[tt][jj]);
-
-    // U = Ut - W S   (D layout: rows = tokens 4g+i, column c)
-    u32x2 Ub[NTW];
-#pragma unroll
-    for (int jj = 0; jj < NTW; ++jj) {
-      f32x4 X = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) X = mfma_k32(cur.W[s], cat(Sb[2 * s][jj], Sb[2 * s + 1][jj]), X);
-      f32x4 U;
-      if (want_ut)
-        U = cur.Ut[jj] - X;
-      else
-        U = -X;
-      Ub[jj] = pack4(U);
-    }
-
-    if (want_out) {
-      // O^T = S^T Qbar^T + U^T Aqk^T  (rows = value columns, columns = tokens)
-      const int cis = ch - first_chunk;
-      const int m = min(C, seq_len - C * cis);
-      const long long tok = seq_tok0 + (long long)C * cis + c;
-#pragma unroll
-      for (int jj = 0; jj < NTW; ++jj) {
-        f32x4 Ot = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Ot = mfma_k32(cat(Sb[2 * s][jj], Sb[2 * s + 1][jj]), cur.Q[s], Ot);
-        Ot = mfma_k16(Ub[jj], cur.Aqk, Ot);
-        if (c < m) {
-          const long long off = (tok * H + h) * D + 16 * (ct0 + jj) + 4 * g;
-          *reinterpret_cast<u32x2*>(p.out + off) = pack4(Ot);
-        }
-      }
-    }
-
-    // S <- Diag(gamma_C) S + Khat^T U
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-      for (int jj = 0; jj < NTW; ++jj) S[tt][jj] = mfma_k16(cur.Kh[tt], Ub[jj], S[tt][jj] * cur.gC[tt]);
+  // two operand sets, loaded one chunk ahead of their use
+  ChunkOps opA, opB;
+  if (cb < ce) load_ops(opA, rbase + cb * rec_stride, L, g, ct0, want_out, want_ut);
+  for (int ch = cb; ch < ce; ch += 2) {
+    if (ch + 1 < ce) load_ops(opB, rbase + (ch + 1) * rec_stride, L, g, ct0, want_out, want_ut);
+    chunk_step(S, opA, want_out, want_ut, want_out ? out_row(ch) : nullptr, want_out && stores(ch));
+    if (ch + 1 >= ce) break;
+    if (ch + 2 < ce) load_ops(opA, rbase + (ch + 2) * rec_stride, L, g, ct0, want_out, want_ut);
+    chunk_step(S, opB, want_out, want_ut, want_out ? out_row(ch + 1) : nullptr, want_out && stores(ch + 1));
   }
 
   // ---- write back ----
