@@ -42,28 +42,57 @@ FLOPS_PREP = 4 * 2 * C * C * D // C  # A, Aqk, W, Ut (16x16x128 each) per 16 tok
 FLOPS_RECUR = 6 * D * D + 2 * C * D  # W S, Qbar S, Khat^T U, Aqk U per token
 
 
+def kernel_source_sha() -> str:
+    """Short hash of the HIP sources, to tell whether committed counter data
+    still describes the kernels being run."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kimi_delta_attention_02_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per dispatch from the committed rocprofv3 counter runs
+    (profiles/pmc_traffic.txt), or None when they were taken on other kernel
+    sources or another workload."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_source_sha()
+    for line in open(path):
+        f = line.split()
+        if len(f) == 5 and not line.startswith("#") and f[0] == workload and f[1] == kernel and f[2] == sha:
+            return int(f[3]) + int(f[4])
+    return None
+
+
 _CPU_X = None  # inputs shared with the forked baseline workers
 
 
 def _cpu_worker(args):
-    name, head, L = args
+    head, seqs, reps = args
     from threadpoolctl import threadpool_limits
 
     from oracle import kda_oracle as O
 
     with threadpool_limits(1):
         x = _CPU_X
-        cu = x["cu_seqlens"]
-        t0 = 0 if cu is None else int(cu[0])
-        sl = slice(t0, t0 + L)
-        s0 = None if x["initial_state"] is None else x["initial_state"][:1]
         t = time.perf_counter()
-        O.kda_forward(x["q"][:1, sl], x["k"][:1, sl], x["v"][:1, sl], x["g"][:1, sl], x["beta"][:1, sl], x["A_log"],
-                      x["dt_bias"], x["scale"], x["lower_bound"], s0, None, heads=[head])
+        for _ in range(reps):
+            O.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["A_log"], x["dt_bias"], x["scale"],
+                          x["lower_bound"], x["initial_state"], x["cu_seqlens"], seqs=seqs, heads=[head])
         return time.perf_counter() - t
 
 
 def cpu_baseline(name: str, target_s: float) -> dict:
+    """The oracle, unchanged, over a bounded sample of the workload: whole
+    sequences (all heads, one head per worker process), repeated so that the
+    timed work lasts about target_s seconds."""
     import multiprocessing as mp
 
     import kda_inputs
@@ -71,25 +100,32 @@ def cpu_baseline(name: str, target_s: float) -> dict:
     global _CPU_X
     w = kda_inputs.WORKLOADS[name]
     _CPU_X = kda_inputs.make_inputs(w)
-    first_len = w.T if w.seqlens is None else int(w.seqlens[0])
-    # calibrate on one head, 64 tokens, in this process
-    L0 = min(64, first_len)
-    per_tok = _cpu_worker((name, 0, L0)) / L0
+    lens = [w.T] * w.B if w.seqlens is None else list(w.seqlens)
+    # calibrate on the shortest non-empty sequence, one head, in this process
+    i0 = min((i for i in range(len(lens)) if lens[i] > 0), key=lambda i: lens[i])
+    t_tok = _cpu_worker((0, [i0], 1)) / lens[i0]
     workers = max(1, min(16, os.cpu_count() or 1, w.H))
     rounds = math.ceil(w.H / workers)
-    L = int(max(16, min(first_len, target_s / (per_tok * rounds))))
+    # take sequences in order until the sample is large enough, then repeat it
+    seqs, tokens = [], 0
+    for i, L in enumerate(lens):
+        if tokens and tokens * t_tok * rounds >= target_s:
+            break
+        seqs.append(i)
+        tokens += L
+    reps = max(1, int(target_s / max(tokens * t_tok * rounds, 1e-9)))
     ctx = mp.get_context("fork")
     t = time.perf_counter()
     with ctx.Pool(workers) as pool:
-        pool.map(_cpu_worker, [(name, h, L) for h in range(w.H)])
+        pool.map(_cpu_worker, [(h, seqs, reps) for h in range(w.H)])
     wall = time.perf_counter() - t
     return {
-        "value": L / wall,
+        "value": tokens * reps / wall,
         "unit": "tokens/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"{w.name}: first {L} tokens of sequence 0, all {w.H} heads, fp64 token recurrence, "
-                  f"one head per process ({workers} processes), {wall:.1f} s wall",
+        "sample": f"{w.name}: sequences {seqs} ({tokens} tokens) x {reps} passes, all {w.H} heads, fp64 token "
+                  f"recurrence, one head per process ({workers} processes), {wall:.1f} s wall",
     }
 
 
@@ -101,7 +137,7 @@ def main() -> int:
     ap.add_argument("--config", default="cfg2", help="cfg1..cfg5 (cfg4a/cfg4b)")
     ap.add_argument("--cp", default="auto", help="auto | off | force")
     ap.add_argument("--seg", type=int, default=0, help="segment length in chunks (0 = library choice)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (scale reference for HBM counters)")
@@ -198,6 +234,7 @@ def main() -> int:
                 "frac": round(tfl / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["kernel"] = {"prep": "kda_prep_kernel", "recur0": "kda_recur_kernel", "recur1": "kda_recur_kernel",
                       "index": "kda_index_scan", "merge": "kda_merge_kernel"}[dom]
+    roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     roof["stage"] = dom
     roof["avg_launch_ms"] = round(stage_avg[dom], 4)
 

@@ -107,15 +107,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// fp32 -> bf16 with round to nearest even: one v_cvt_pk_bf16_f32 per pair.
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ u32x2 pack4(f32x4 x) {
@@ -126,7 +123,7 @@ __device__ __forceinline__ u32x2 pack4(f32x4 x) {
 }
 
 // x = hi + lo + O(2^-16 |x|): hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ float hi_part(float x) { return __uint_as_float((uint32_t)f32_to_bf16(x) << 16); }
+__device__ __forceinline__ float hi_part(float x) { return __uint_as_float(pack2(x, 0.f) << 16); }
 
 __device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo) {
   f32x4 h, l;

@@ -124,38 +124,38 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(Problem p, Tables t, uint8
   const float adt0 = a * p.dt_bias[h * D + c0];
   const float adt1 = a * p.dt_bias[h * D + c0 + 1];
 
-  // ---- load the chunk (lane owns channels c0, c0+1; rows past m are zero) ----
+  // ---- load the chunk (lane owns channels c0, c0+1; rows past m are zero).
+  // Every load is issued unconditionally (rows past m re-read row m-1, which
+  // exists since m >= 1) so all 64 are in flight together; padding is zeroed
+  // afterwards with selects.
+  uint32_t qq[C], kk[C], vv[C], gg[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const long long off = ((tok0 + min(i, m - 1)) * H + h) * D + c0;
+    qq[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.q + off));
+    kk[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.k + off));
+    vv[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.v + off));
+    gg[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.g + off));
+  }
   float q0[C], q1[C], k0[C], k1[C], v0[C], v1[C], l0[C], l1[C];
 #pragma unroll
   for (int i = 0; i < C; ++i) {
-    uint32_t qq = 0, kk = 0, vv = 0, gg = 0;
-    if (i < m) {
-      const long long off = ((tok0 + i) * H + h) * D + c0;
-      qq = *reinterpret_cast<const uint32_t*>(p.q + off);
-      kk = *reinterpret_cast<const uint32_t*>(p.k + off);
-      vv = *reinterpret_cast<const uint32_t*>(p.v + off);
-      gg = *reinterpret_cast<const uint32_t*>(p.g + off);
-    }
-    q0[i] = __uint_as_float(qq << 16);
-    q1[i] = __uint_as_float(qq & 0xFFFF0000u);
-    k0[i] = __uint_as_float(kk << 16);
-    k1[i] = __uint_as_float(kk & 0xFFFF0000u);
-    v0[i] = __uint_as_float(vv << 16);
-    v1[i] = __uint_as_float(vv & 0xFFFF0000u);
-    if (i < m) {
-      const float x0 = fmaf(a, __uint_as_float(gg << 16), adt0);
-      const float x1 = fmaf(a, __uint_as_float(gg & 0xFFFF0000u), adt1);
-      l0[i] = p.lower_bound * __builtin_amdgcn_rcpf(1.0f + __expf(-x0));
-      l1[i] = p.lower_bound * __builtin_amdgcn_rcpf(1.0f + __expf(-x1));
-    } else {
-      l0[i] = 0.f;
-      l1[i] = 0.f;
-    }
+    const bool ok = i < m;
+    const uint32_t qi = ok ? qq[i] : 0u, ki = ok ? kk[i] : 0u, vi = ok ? vv[i] : 0u;
+    q0[i] = __uint_as_float(qi << 16);
+    q1[i] = __uint_as_float(qi & 0xFFFF0000u);
+    k0[i] = __uint_as_float(ki << 16);
+    k1[i] = __uint_as_float(ki & 0xFFFF0000u);
+    v0[i] = __uint_as_float(vi << 16);
+    v1[i] = __uint_as_float(vi & 0xFFFF0000u);
+    const float x0 = fmaf(a, __uint_as_float(gg[i] << 16), adt0);
+    const float x1 = fmaf(a, __uint_as_float(gg[i] & 0xFFFF0000u), adt1);
+    l0[i] = ok ? p.lower_bound * __builtin_amdgcn_rcpf(1.0f + __expf(-x0)) : 0.f;
+    l1[i] = ok ? p.lower_bound * __builtin_amdgcn_rcpf(1.0f + __expf(-x1)) : 0.f;
   }
   if (L < C) {
-    float b = 0.f;
-    if (L < m) b = __builtin_amdgcn_rcpf(1.0f + __expf(-bf16_to_f32(p.beta[(tok0 + L) * H + h])));
-    sm.beta[L] = b;
+    const float bl = bf16_to_f32(p.beta[(tok0 + min(L, m - 1)) * H + h]);
+    sm.beta[L] = (L < m) ? __builtin_amdgcn_rcpf(1.0f + __expf(-bl)) : 0.f;
   }
 
   // ---- squared norms of the 16 q rows and 16 k rows: butterfly reduction of
