@@ -2,19 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg2] [--cp auto]
 
-One step = one kda_fwd call (index tables, chunk prep, recurrence and, when the
-plan splits sequences, pre-scan + merge + segment recurrence) over one batch
-of seeded synthetic inputs already resident in HBM.  W untimed steps, then
-exactly K steps timed with HIP events on the stream the library launches on,
-bracketed by device synchronisation.  Prints ONE JSON line.
+One step = one kda_fwd call (index tables, chunk prep fused with the
+recurrence and, when the plan splits sequences, pre-scan + merge + segment
+recurrence) over one batch of seeded synthetic inputs already resident in HBM.
+W untimed steps, then exactly K steps timed with HIP events on the stream the
+library launches on, bracketed by device synchronisation.  Prints ONE JSON
+line.
 
 Per-stage kernel time comes from the library's own event hook
-(kda_profile_enable / kda_profile_collect) over the same timed region; the
-roofline object is computed for the stage that takes the most time.
+(kda_profile_enable / kda_profile_collect, HIP events on the library's
+stream) over the same timed region; the roofline object is computed for the
+chunk kernel (chunk prep + recurrence), summed over its launches in a step.
 
 The CPU baseline times the fp64 oracle (unchanged) on a bounded sample of the
-same workload: the first sequence's first L tokens for every head, one head per
-worker process, before any GPU work starts.
+same workload: whole sequences taken in order, all heads, one head per worker
+process, repeated to about --cpu-seconds, before any GPU work starts.
 """
 from __future__ import annotations
 
@@ -38,8 +40,6 @@ C = 16
 BYTES_IN = 4 * 2 * D + 2  # q, k, v, g bf16 + beta bf16
 BYTES_OUT = 2 * D  # out bf16
 FLOPS_PATH = 6 * D * D + 10 * C * D  # 3 chunk GEMMs of 2*16*128*128 per 16 tokens + five 16x16x128 products
-FLOPS_PREP = 4 * 2 * C * C * D // C  # A, Aqk, W, Ut (16x16x128 each) per 16 tokens
-FLOPS_RECUR = 6 * D * D + 2 * C * D  # W S, Qbar S, Khat^T U, Aqk U per token
 
 
 def kernel_source_sha() -> str:
@@ -57,9 +57,9 @@ def kernel_source_sha() -> str:
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per dispatch from the committed rocprofv3 counter runs
-    (profiles/pmc_traffic.txt), or None when they were taken on other kernel
-    sources or another workload."""
+    """HBM bytes per dispatch of one kernel from the committed rocprofv3 counter
+    runs (profiles/pmc_traffic.txt), or None when they were taken on other
+    kernel sources or another workload."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -143,7 +143,7 @@ def main() -> int:
                     help="also run one plain device copy of this many MiB (scale reference for HBM counters)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); multi-GPU runs are not part of this build",
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the library has no multi-GPU path",
               file=sys.stderr)
         return 2
 
@@ -210,20 +210,20 @@ def main() -> int:
     if final is not None:
         state_bytes += final.numel() * final.element_size()
 
-    # algorithmic work per stage launch
-    stage_work = {
-        "prep": (th * BYTES_IN, th * FLOPS_PREP),
-        "recur0": (th * BYTES_OUT + state_bytes, th * FLOPS_RECUR),
-        "recur1": (th * BYTES_OUT + state_bytes, th * FLOPS_RECUR),
-        "index": (0, 0),
-        "merge": (0, 0),
-    }
-    stage_avg = {n: (t / c if c else 0.0) for n, (t, c) in stages.items()}
-    dom = max(stage_avg, key=lambda n: stages[n][0])
-    bytes_d, flops_d = stage_work[dom]
-    if dom == "recur0" and seg > 0:  # with a split the recurrence work is shared by recur0 and recur1
-        bytes_d, flops_d = bytes_d, flops_d
-    t_s = stage_avg[dom] / 1e3
+    # Roofline of the chunk kernel, the kernel that does the path's work (chunk
+    # prep fused with the recurrence).  It runs once per step on a serial plan
+    # and twice on a segmented one (first pass + segment pass); every
+    # token-head's output is written by exactly one of those launches, so the
+    # algorithmic work of a step (1282 B and 6 D^2 + 10 C D flops per
+    # token-head, plus the state read and write) is set against the summed
+    # duration of the chunk-kernel launches of a step.  Pre-scan, merge and
+    # workspace traffic are overhead and earn nothing.
+    chunk_stages = [n for n in ("recur0", "recur1") if stages.get(n, (0.0, 0))[1]]
+    chunk_ms = sum(stages[n][0] for n in chunk_stages) / a.steps
+    launches = sum(stages[n][1] for n in chunk_stages) / a.steps
+    bytes_d = th * (BYTES_IN + BYTES_OUT) + state_bytes
+    flops_d = th * FLOPS_PATH
+    t_s = chunk_ms / 1e3
     gbs = bytes_d / t_s / 1e9 if t_s > 0 else 0.0
     tfl = flops_d / t_s / 1e12 if t_s > 0 else 0.0
     if bytes_d / (PEAK_HBM_GBS * 1e9) >= flops_d / (PEAK_BF16_TFLOPS * 1e12):
@@ -232,11 +232,13 @@ def main() -> int:
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfl / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = {"prep": "kda_prep_kernel", "recur0": "kda_recur_kernel", "recur1": "kda_recur_kernel",
-                      "index": "kda_index_scan", "merge": "kda_merge_kernel"}[dom]
-    roof["traffic"] = measured_traffic(w.name, roof["kernel"])
-    roof["stage"] = dom
-    roof["avg_launch_ms"] = round(stage_avg[dom], 4)
+    kernels = ["kda_chunk_kernel<1>", "kda_chunk_kernel<0>"] if seg > 0 else ["kda_chunk_kernel<0>"]
+    per_launch = [measured_traffic(w.name, k) for k in kernels]
+    roof["traffic"] = None if any(t is None for t in per_launch) else sum(per_launch)
+    roof["kernel"] = "kda_chunk_kernel"
+    roof["launches_per_step"] = launches
+    roof["kernel_ms_per_step"] = round(chunk_ms, 4)
+    roof["flops_frac"] = round(tfl / PEAK_BF16_TFLOPS, 4)
 
     path_bytes = th * (BYTES_IN + BYTES_OUT) + state_bytes
     path_flops = th * FLOPS_PATH

@@ -107,18 +107,19 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
                 void* stream);
 
 /* Byte offsets of the workspace regions for these sizes and plan, so a caller
- * can inspect the chunk-prep records and index tables a kda_fwd call left in
- * its workspace.  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
+ * can inspect the index tables and segment maps a kda_fwd call left in its
+ * workspace.  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
  * order of kda_ws_offset.  Returns KDA_OK or a negative kda_status. */
 typedef enum {
-  KDA_WS_COUNTERS = 0,      /* int32[4]: n_chunks, n_segs, sanitize flags, reserved */
+  KDA_WS_COUNTERS = 0,      /* int32[4]: n_chunks, n_segs, flags, reserved; flags bits 0x1..0x8 name
+                               repaired cu_seqlens faults (first != 0, decreasing, last != total,
+                               out of range), 0x100 / 0x200 a chunk-kernel wait that gave up */
   KDA_WS_SEQ_START,         /* int32[N+1]   clamped sequence boundaries (last = end of the last sequence) */
   KDA_WS_SEQ_LEN,           /* int32[N]     clamped length */
   KDA_WS_SEQ_CHUNK_OFF,     /* int32[N+1]   prefix sums of ceil(len/16) */
   KDA_WS_SEQ_SEG_OFF,       /* int32[N+1]   prefix sums of max(1, ceil(chunks/seg)) */
   KDA_WS_CHUNK_TAB,         /* int32[max_chunks][2] (sequence, chunk in sequence) */
   KDA_WS_SEG_TAB,           /* int32[max_segs][4] (sequence, chunk begin, chunk end, segment in sequence) */
-  KDA_WS_CHUNK_REC,         /* per (chunk, head) chunk-prep records, KDA_CHUNK_REC_BYTES each */
   KDA_WS_SEG_M,             /* fp32 [max_segs][H][128][128] segment transitions M^T (CP only) */
   KDA_WS_SEG_R,             /* fp32 [max_segs][H][128][128] zero-start segment states R^T (CP only) */
   KDA_WS_SEG_S,             /* fp32 [max_segs][H][128][128] state entering each segment, [v][k] (CP only) */
@@ -127,8 +128,6 @@ typedef enum {
   KDA_WS_TOTAL,             /* total bytes (= kda_get_workspace_size) */
   KDA_WS_NUM_OFFSETS
 } kda_ws_offset;
-
-#define KDA_CHUNK_REC_BYTES 26112
 
 int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
                               int32_t seg_chunks, int64_t* offs);
@@ -139,12 +138,12 @@ int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t n
  * for reuse).  kda_profile_collect waits for the recorded events, adds the
  * elapsed milliseconds of each stage into stage_ms[0..n_stages-1] and the
  * number of timed launches of the stage into stage_calls, and forgets them.
- * Stages: KDA_STAGE_INDEX (index scan + table fill), KDA_STAGE_PREP (chunk
- * prep), KDA_STAGE_RECUR0 (recurrence / pre-scan), KDA_STAGE_MERGE,
- * KDA_STAGE_RECUR1 (segment recurrence).  Returns KDA_OK or KDA_ERR_HIP. */
+ * Stages: KDA_STAGE_INDEX (index scan + table fill), KDA_STAGE_RECUR0 (chunk
+ * prep + recurrence of whole sequences / first segments, and the pre-scan of
+ * middle segments), KDA_STAGE_MERGE, KDA_STAGE_RECUR1 (chunk prep + recurrence
+ * of segments >= 1).  Returns KDA_OK or KDA_ERR_HIP. */
 typedef enum {
   KDA_STAGE_INDEX = 0,
-  KDA_STAGE_PREP,
   KDA_STAGE_RECUR0,
   KDA_STAGE_MERGE,
   KDA_STAGE_RECUR1,

@@ -33,7 +33,6 @@ __all__ = [
     "load_library",
     "KdaError",
     "WS_FIELDS",
-    "CHUNK_REC_BYTES",
     "STAGES",
     "profile_enable",
     "profile_collect",
@@ -45,11 +44,10 @@ _lib = None
 
 HEAD_DIM = 128
 CHUNK = 16
-CHUNK_REC_BYTES = 26112
 WS_ALIGN = 256
 WS_FIELDS = [
     "counters", "seq_start", "seq_len", "seq_chunk_off", "seq_seg_off", "chunk_tab", "seg_tab",
-    "chunk_rec", "seg_m", "seg_r", "seg_s", "max_chunks", "max_segs", "total",
+    "seg_m", "seg_r", "seg_s", "max_chunks", "max_segs", "total",
 ]
 _CP = {"auto": 0, "off": 1, "force": 2, None: 0, False: 1, True: 2}
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP error"}
@@ -149,7 +147,7 @@ def workspace_offsets(total_tokens: int, num_heads: int, num_seqs: int = 1, cp_m
     return dict(zip(WS_FIELDS, [int(x) for x in arr]))
 
 
-STAGES = ["index", "prep", "recur0", "merge", "recur1"]
+STAGES = ["index", "recur0", "merge", "recur1"]
 
 
 def profile_enable(on: bool = True) -> None:

@@ -3,11 +3,15 @@
 //
 // Launch sequence of one kda_fwd call, all on the caller's stream, with no
 // host synchronisation, allocation or device-to-host copy:
-//   index scan + table fill  ->  chunk prep (every chunk x head)
-//   -> recurrence phase 0 (serial sequences / segment 0, and the pre-scan of
-//      middle segments)  [-> merge -> recurrence phase 1 (segments >= 1)]
-// The bracketed part runs only when the plan splits sequences into segments
-// (cuLA PR #106 commit list: "K1 once -> pre_scan -> merge -> segment-K2").
+//   index scan + table fill
+//   -> chunk kernel, first pass: chunk prep fused with the recurrence of whole
+//      sequences / first segments, and with the pre-scan of middle segments
+//   [-> merge -> chunk kernel, second pass: segments >= 1 from merged states]
+// The bracketed part runs only when the plan splits sequences into segments.
+// It follows the segment scheme on the cuLA PR #106 page (pre-scan, merge,
+// segment recurrence), except that chunk prep is recomputed in each pass from
+// the inputs rather than stored once: a stored prep record is larger than the
+// inputs it is computed from.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -133,7 +137,6 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
   take(KDA_WS_SEQ_SEG_OFF, 4 * ((int64_t)N + 1));
   take(KDA_WS_CHUNK_TAB, 8 * mc);
   take(KDA_WS_SEG_TAB, 16 * ms);
-  take(KDA_WS_CHUNK_REC, mc * H * (int64_t)kda::REC_BYTES);
   const int64_t seg_bytes = seg > 0 ? ms * H * (int64_t)kda::D * kda::D * 4 : 0;
   take(KDA_WS_SEG_M, seg_bytes);
   take(KDA_WS_SEG_R, seg_bytes);
@@ -226,7 +229,6 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   t.seq_seg_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_SEG_OFF]);
   t.chunk_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_CHUNK_TAB]);
   t.seg_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_TAB]);
-  uint8_t* rec = ws + lay.off[KDA_WS_CHUNK_REC];
   const bool cp = lay.seg > 0;
   float* segM = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;
   float* segR = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
@@ -259,12 +261,8 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
     e = kda::launch_index(cu_seqlens, N, T, total, lay.seg, mc, ms, t, s);
   }
   if (e == hipSuccess) {
-    StageTimer tm(KDA_STAGE_PREP, s);
-    e = kda::launch_prep(p, t, rec, mc, s);
-  }
-  if (e == hipSuccess) {
     StageTimer tm(KDA_STAGE_RECUR0, s);
-    e = kda::launch_recur(p, t, rec, segM, segR, segS, ms, 0, s);
+    e = kda::launch_chunks(p, t, segM, segR, segS, ms, 0, cp, s);
   }
   if (cp) {
     if (e == hipSuccess) {
@@ -273,7 +271,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
     }
     if (e == hipSuccess) {
       StageTimer tm(KDA_STAGE_RECUR1, s);
-      e = kda::launch_recur(p, t, rec, segM, segR, segS, ms, 1, s);
+      e = kda::launch_chunks(p, t, segM, segR, segS, ms, 1, cp, s);
     }
   }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));

@@ -1,18 +1,13 @@
 // Internal definitions shared by the HIP kernels and the host library.
 //
-// Chunk-prep -> recurrence hand-off (one record per chunk and head), written by
-// the chunk-prep kernel in the exact register order the recurrence kernel's
-// MFMA operands use, so the recurrence reads it with plain 16-byte loads.
-//
 // MFMA lane layouts used throughout (wave64, lane L, g = L / 16, c = L % 16):
 //   v_mfma_f32_16x16x32_bf16 : A[c][8g+e], B[8g+e][c] (e = 0..7), D[4g+i][c]
-//   v_mfma_f32_16x16x16_bf16 : A[c][4g+e], B[4g+e][c] (e = 0..3), D[4g+i][c]
 //   v_mfma_f32_16x16x4_f32   : A[c][g],    B[g][c],                D[4g+i][c]
 // A 16x16 fp32 accumulator tile therefore holds rows 4g..4g+3 of column c in
-// lane L, which is also the B-operand layout of the 16x16x16 MFMA.  For the
-// 16x16x32 MFMA over a K range made of two 16-row tiles (a, b), lane group g
-// supplies rows {16a+4g+0..3, 16b+4g+0..3}: the reduction index is permuted,
-// and every operand that meets the state uses the same permutation.
+// lane L.  For the 16x16x32 MFMA over a K range made of two 16-row tiles
+// (a, b), lane group g supplies rows {16a+4g+0..3, 16b+4g+0..3}: the reduction
+// index is permuted, and every operand that meets the state uses the same
+// permutation.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,27 +19,6 @@ namespace kda {
 
 constexpr int D = KDA_HEAD_DIM;  // K = V = 128
 constexpr int C = KDA_CHUNK;     // 16 tokens per chunk
-
-// ---- chunk record layout (bytes) ----
-// W    : 4 k-steps x 64 lanes x 16 B (bf16x8: W[c][32s+4g+0..3], W[c][32s+16+4g+0..3])
-// Q    : 4 k-steps x 64 lanes x 16 B (same arrangement for Qbar)
-// KH_HI: 8 row tiles x 64 lanes x 8 B (bf16x4: Khat[4g+0..3][16t+c], high part)
-// KH_LO: same, low part (Khat - bf16(Khat), rounded to bf16)
-// UT   : 8 col tiles x 64 lanes x 16 B (fp32x4: Ut[4g+0..3][16j+c])
-// AQK_HI / AQK_LO : 64 lanes x 8 B (bf16x4: Aqk[c][4g+0..3], lower-inclusive, high / low part)
-// GC   : 128 x fp32 (gamma_C per key channel)
-// A value x stored as a high/low pair is x_hi = bf16(x), x_lo = bf16(x - x_hi);
-// products with such an operand carry ~16 mantissa bits instead of 8.
-constexpr int REC_W = 0;
-constexpr int REC_Q = 4096;
-constexpr int REC_KH_HI = 8192;
-constexpr int REC_KH_LO = 12288;
-constexpr int REC_UT = 16384;
-constexpr int REC_AQK_HI = 24576;
-constexpr int REC_AQK_LO = 25088;
-constexpr int REC_GC = 25600;
-constexpr int REC_BYTES = 26112;
-static_assert(REC_BYTES == KDA_CHUNK_REC_BYTES, "record size");
 
 // ---- counters block ----
 constexpr int CNT_N_CHUNKS = 0;
@@ -84,11 +58,9 @@ struct Problem {
 // ---- launchers (host functions defined next to their kernels) ----
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
-hipError_t launch_prep(const Problem& p, Tables t, uint8_t* rec, int64_t max_chunks, hipStream_t st);
-// phase 0: serial or first pass (segment 0 recurrence + pre-scan of middle segments)
-// phase 1: recurrence of segments >= 1 from the merged states
-hipError_t launch_recur(const Problem& p, Tables t, const uint8_t* rec, float* segM, float* segR, float* segS,
-                        int64_t max_segs, int phase, hipStream_t st);
+// producer/consumer chunk kernel: prep + recurrence / pre-scan in one launch per phase
+hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, float* segS, int64_t max_segs,
+                         int phase, bool segmented, hipStream_t st);
 hipError_t launch_merge(const Problem& p, Tables t, const float* segM, const float* segR, float* segS,
                         hipStream_t st);
 
@@ -98,8 +70,6 @@ hipError_t launch_merge(const Problem& p, Tables t, const float* segM, const flo
 namespace kda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -136,7 +106,6 @@ __device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo) {
   lo = pack4(l);
 }
 
-__device__ __forceinline__ i16x4 as_i16x4(u32x2 x) { return __builtin_bit_cast(i16x4, x); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) {
@@ -150,10 +119,6 @@ __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) {
 
 __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(a), as_i16x4(b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {

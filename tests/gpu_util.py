@@ -1,5 +1,5 @@
 """Helpers for the GPU tests: move seeded inputs to the device, call the
-library through its binding, decode workspace records, compare to the oracle."""
+library through its binding, read workspace tables, compare to the oracle."""
 from __future__ import annotations
 
 import sys
@@ -17,6 +17,8 @@ from oracle import kda_oracle as O
 # 0.04 x RMS, so the bound is applied to the computed value before the store.)
 REL_L2 = 1e-2
 MAX_ABS_RMS = 3e-2
+# counters[2] bits the chunk kernel sets when a producer / consumer wait gives up
+WAIT_FLAGS = 0x300
 
 
 def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
@@ -74,6 +76,9 @@ def run_gpu(w, x, d, cp_mode="auto", seg_chunks=0, want_final=True, init=True, w
             lower_bound=x["lower_bound"], workspace=workspace, initial_state=init_t, final_state=final,
             cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode, seg_chunks=seg_chunks)
     torch.cuda.synchronize()
+    offs = kda.workspace_offsets(w.B * w.T, w.H, N, cp_mode, seg_chunks)
+    flags = int(read_ws(workspace, offs, "counters", 4, np.int32)[2])
+    assert flags & WAIT_FLAGS == 0, f"a chunk-kernel wait gave up (counters flags {flags:#x})"
     return out, final, workspace
 
 
@@ -109,20 +114,6 @@ def assert_close(got, ref, what, stored="bf16"):
     assert excess <= MAX_ABS_RMS * rms, f"{what}: max-abs beyond the store rounding {excess:.3e} > {MAX_ABS_RMS} x rms {rms:.3e}"
 
 
-def assert_close_scaled(got, ref, what, rel_l2=REL_L2, max_frac=1e-2):
-    """For chunk intermediates that span many decades (decays down to e^-80):
-    relative L2 plus a max-abs bound scaled by the largest reference entry,
-    the size of a bf16 operand error on the dominant terms."""
-    diff = got - ref
-    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
-    mx = float(np.max(np.abs(diff))) if diff.size else 0.0
-    top = float(np.max(np.abs(ref))) if ref.size else 0.0
-    say(f"{what}: rel_l2={rel:.3e} max_abs={mx:.3e} max_ref={top:.3e}")
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    assert rel <= rel_l2, f"{what}: relative L2 {rel:.3e} > {rel_l2}"
-    assert mx <= max_frac * top, f"{what}: max-abs {mx:.3e} > {max_frac} x max|ref| {top:.3e}"
-
-
 def check_against_oracle(w, x, out, final, seqs=None, heads=None, init=True, final_dtype=None):
     """Compare the selected chains with the fp64 oracle (token recurrence)."""
     outs, finals = O.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["A_log"], x["dt_bias"], x["scale"],
@@ -154,35 +145,3 @@ def read_ws(ws, offs, name, count, dtype):
     nbytes = count * np.dtype(dtype).itemsize
     a = ws[offs[name]:offs[name] + nbytes].cpu().numpy()
     return a.view(dtype)
-
-
-def decode_record(buf: np.ndarray) -> dict:
-    """Decode one chunk record (bytes) into plain [token][channel] arrays; the
-    high/low pairs (Khat, Aqk) are summed."""
-    W = np.zeros((16, 128))
-    Q = np.zeros((16, 128))
-    Kh = np.zeros((16, 128))
-    Ut = np.zeros((16, 128))
-    Aqk = np.zeros((16, 16))
-    w16 = O.widen(buf[0:4096].view(np.uint16).reshape(4, 64, 8))
-    q16 = O.widen(buf[4096:8192].view(np.uint16).reshape(4, 64, 8))
-    kh16 = O.widen(buf[8192:12288].view(np.uint16).reshape(8, 64, 4)) + \
-        O.widen(buf[12288:16384].view(np.uint16).reshape(8, 64, 4))
-    ut = buf[16384:24576].view(np.float32).reshape(8, 64, 4).astype(np.float64)
-    aq = O.widen(buf[24576:25088].view(np.uint16).reshape(64, 4)) + O.widen(buf[25088:25600].view(np.uint16).reshape(64, 4))
-    gc = buf[25600:26112].view(np.float32).astype(np.float64)
-    for L in range(64):
-        g, c = L // 16, L % 16
-        for s in range(4):
-            for e in range(4):
-                W[c, 32 * s + 4 * g + e] = w16[s, L, e]
-                W[c, 32 * s + 16 + 4 * g + e] = w16[s, L, 4 + e]
-                Q[c, 32 * s + 4 * g + e] = q16[s, L, e]
-                Q[c, 32 * s + 16 + 4 * g + e] = q16[s, L, 4 + e]
-        for t in range(8):
-            for e in range(4):
-                Kh[4 * g + e, 16 * t + c] = kh16[t, L, e]
-                Ut[4 * g + e, 16 * t + c] = ut[t, L, e]
-        for e in range(4):
-            Aqk[c, 4 * g + e] = aq[L, e]
-    return dict(W=W, Qbar=Q, Khat=Kh, Ut=Ut, Aqk=Aqk, gamma_C=gc)

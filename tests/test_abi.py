@@ -63,7 +63,7 @@ def test_workspace_layout_consistent():
         off = kda.workspace_offsets(*args)
         assert off["total"] == size
         prev = -1
-        for name in kda.WS_FIELDS[:11]:
+        for name in kda.WS_FIELDS[:10]:
             assert off[name] % kda.WS_ALIGN == 0
             assert off[name] >= prev
             prev = off[name]
@@ -71,9 +71,13 @@ def test_workspace_layout_consistent():
         assert off["max_chunks"] == (total + 15 * N) // 16
         seg = kda.plan_seg_chunks(*args)
         assert off["max_segs"] == (off["max_chunks"] // seg + N if seg else N)
-        assert off["seg_m"] - off["chunk_rec"] >= off["max_chunks"] * H * kda.CHUNK_REC_BYTES
+        assert off["seg_m"] - off["seg_tab"] >= 16 * off["max_segs"]
+        mat = off["max_segs"] * H * 128 * 128 * 4
         if seg == 0:
-            assert off["seg_s"] == off["seg_r"] == off["seg_m"]
+            assert off["seg_s"] == off["seg_r"] == off["seg_m"] == off["total"]
+        else:
+            assert off["seg_r"] - off["seg_m"] >= mat and off["seg_s"] - off["seg_r"] >= mat
+            assert off["total"] - off["seg_s"] >= mat
 
 
 def _call(lib, **kw):

@@ -6,7 +6,7 @@ import pytest
 
 import kda_inputs
 from oracle import kda_oracle as O
-from tests.gpu_util import (assert_close, assert_close_scaled, check_against_oracle, decode_record, dev_inputs, read_ws, run_gpu, say,
+from tests.gpu_util import (assert_close, check_against_oracle, dev_inputs, read_ws, run_gpu, say,
                             to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -80,37 +80,19 @@ def test_zero_tokens_with_final_state():
     np.testing.assert_array_equal(to_f64(final), O.widen(x["initial_state"]))
 
 
-# ------------------------------------------------------------------- K1 records against the oracle's chunk quantities
-def test_chunk_records_match_oracle():
-    w = kda_inputs.custom(seqlens=[40, 16, 7], H=2, lower_bound=-5.0, seed=27, name="records")
+# ------------------------------------------------------------------- chunk prep at every chunk size
+@pytest.mark.parametrize("lb,init_std", [(-5.0, 0.05), (-0.5, 0.5)])
+def test_every_chunk_tail(lb, init_std):
+    """Sequences of 1..16 tokens are one chunk of each possible size, 17..32 a
+    full chunk then a ragged one.  A one-chunk output is the chunk prep (norms,
+    decays, beta, the WY inverse, Aqk) applied to the initial state and V, so
+    each tail size of the prep is checked on its own sequence."""
+    w = kda_inputs.custom(seqlens=list(range(1, 33)), H=2, lower_bound=lb, init_std=init_std, seed=27,
+                          name=f"tails lb={lb}")
     x = kda_inputs.make_inputs(w)
     d = dev_inputs(x)
-    _, _, ws = run_gpu(w, x, d, cp_mode="off")
-    import kimi_delta_attention_02_amd as kda
-
-    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, "off", 0)
-    rec = ws[offs["chunk_rec"]:].cpu().numpy()
-    sp = O.sequence_spans(w.B, w.T, x["cu_seqlens"])
-    gchunk = 0
-    for i, (b, t0, L) in enumerate(sp):
-        for c0 in range(0, L, 16):
-            m = min(16, L - c0)
-            for h in range(w.H):
-                sl = (b, slice(t0 + c0, t0 + c0 + m), h)
-                qh = O.l2_normalize(O.widen(x["q"][sl]))
-                kh = O.l2_normalize(O.widen(x["k"][sl]))
-                lam = O.log_decay(O.widen(x["g"][sl])[:, None, :], x["A_log"][h:h + 1], x["dt_bias"][h:h + 1],
-                                  x["lower_bound"])[:, 0]
-                bt = O.sigmoid(O.widen(x["beta"][sl]))
-                ref = O.chunk_quantities(qh, kh, O.widen(x["v"][sl]), lam, bt, x["scale"])
-                base = (gchunk * w.H + h) * kda.CHUNK_REC_BYTES
-                got = decode_record(rec[base:base + kda.CHUNK_REC_BYTES])
-                for name in ("W", "Qbar", "Khat", "Ut", "Aqk"):
-                    g_ = got[name][:m, :m] if name == "Aqk" else got[name][:m]
-                    assert_close_scaled(g_.reshape(-1), ref[name].reshape(-1), f"chunk {gchunk} h{h} {name}")
-                    assert np.all(got[name][m:] == 0), f"{name} rows past the chunk end must be zero"
-                np.testing.assert_allclose(got["gamma_C"], ref["gamma_C"], rtol=2e-5, atol=0)
-            gchunk += 1
+    out, final, _ = run_gpu(w, x, d, cp_mode="off")
+    check_against_oracle(w, x, out, final)
 
 
 # ------------------------------------------------------------------- index tables, bit-exact
