@@ -27,11 +27,11 @@
 //   Aqk = LowerInclusive(Qbar Ktil^T)
 // and the consumers, with S the K x V state entering the chunk:
 //   Y = Kbar S;  X = T' Y (= W S, W = T' Kbar);  Ut = T' V;  U = Ut - X
-//   O = Qbar S + Aqk U;  S <- Diag(gamma_C) S + Khat^T U
+//   O = Qbar S + Aqk U;  S <- Diag(gamma_C) (S + Ktil^T U)  (Khat = Ktil gamma_C)
 // (pre-scan: M starts at I with Ut = 0, R starts at 0; neither writes O).
 //
-// Every product is a 16x16x32 bf16 MFMA with fp32 accumulation; A, Aqk, T', U
-// and Khat enter as bf16 high/low pairs (x = x_hi + x_lo, ~16 significant
+// Every product is a 16x16x32 bf16 MFMA with fp32 accumulation; Aqk (and its
+// factors Qbar, Ktil), T', U and Ktil in the update enter as bf16 high/low pairs (x = x_hi + x_lo, ~16 significant
 // bits) packed into the 32-long K dimension: the largest outputs and state
 // entries are ~10x their RMS, where plain bf16 operands cost more than 3% of
 // the RMS.  A 16x16 accumulator tile holds rows 4g..4g+3 of column c in lane
@@ -45,32 +45,42 @@ namespace {
 
 enum Role { RECUR = 0, PRE = 1 };
 
+constexpr int NPW = 4;                  // producer wavefronts
+constexpr int NCW = 8;                  // consumer wavefronts
+constexpr int TPW = (D / 16) / NCW;     // 16-column state tiles per consumer wavefront
+constexpr int NTHREADS = 64 * (NPW + NCW);
 constexpr int NSLOT = 6;
-constexpr int MP = 20;                 // fp32 16x16 matrix pitch
-constexpr int SPIN_LIMIT = 1 << 24;    // polls (each with s_sleep) before a wait gives up
+constexpr int MP = 20;               // fp32 16x16 matrix pitch
+constexpr int SPIN_LIMIT = 1 << 24;  // polls (each with s_sleep) before a wait gives up
+constexpr float LOG2E = 1.4426950408889634f;
 
+// One prepared chunk.  Every fragment is stored in the register order of the
+// MFMA operand that reads it, so the consumers read 16 bytes per lane and use
+// them as they are.
 struct Slot {
-  u32x4 kbf[4][64];       // Kbar (bf16) operand fragment per k-step s
-  u32x4 qbf[4][64];       // Qbar (bf16) operand fragment per k-step s
-  uint16_t khT[2][D][C];  // Khat^T high / low part, [channel][token]
-  float gC[D];            // gamma_C per key channel
-  u32x4 tf[64];           // [T'_hi | T'_lo] fragment: T'[c][4g..4g+3]
-  u32x4 aq[64];           // (Aqk_hi, Aqk_lo) fragment: Aqk[c][4g..4g+3]
+  u32x4 kbf[4][64];   // Kbar bf16, A operand of Kbar S: k-step s, lane (g, c) = token c
+  u32x4 qbf[4][64];   // Qbar bf16, B operand of S^T Qbar^T, same arrangement
+  u32x4 ktp[D][4];    // [channel][g]: Ktil high part of tokens 4g..4g+3, then the low part
+  float gC[D];        // gamma_C per key channel
+  u32x4 tf[64];       // [T'_hi | T'_lo] of row c, columns 4g..4g+3
+  u32x4 aqa[64];      // [Aqk_hi | Aqk_hi] of row c, columns 4g..4g+3
+  u32x4 aqb[64];      // [Aqk_lo | 0]
 };
 
 struct Smem {
   Slot slot[NSLOT];
-  float Aq[4][C][16];     // per producer: A rows arranged for the quad-parallel solve
-  float Tp[4][C * MP];    // per producer: T'
-  float bt[4][C];         // per producer: beta of the chunk's tokens
-  float adt[D];           // exp(A_log) * dt_bias of the head
+  float Aq[4][C][16];   // per producer: A rows arranged for the quad-parallel solve
+  float Tp[4][C * MP];  // per producer: T'
+  float bt[4][C];       // per producer: beta of the chunk's tokens
+  float adt[D];         // log2(e) exp(A_log) dt_bias of the head
   int ready[NSLOT];
-  int done[NSLOT][4];
+  int done[NSLOT][NCW];
 };
 
-// raw inputs of one chunk for one producer lane
+// raw inputs of one chunk for one producer lane: q[s], k[s], g[s] hold token c,
+// channels 32s+4g+0..3 then 32s+16+4g+0..3 (the k-step-s MFMA operand order)
 struct ProdIn {
-  u32x2 q[8], k[8], g[8];  // index 2s+h: channels 32s+16h+4g+0..3 of token c
+  u32x4 q[4], k[4], g[4];
   uint32_t b;
 };
 
@@ -115,27 +125,44 @@ __device__ __forceinline__ void unpack4(u32x2 v, float* f) {
   f[3] = __uint_as_float(v.y & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
-  float h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = hi_part(x[e]);
-    l[e] = x[e] - h[e];
-  }
-  hi = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-  lo = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+// x0 = h0 + l0, x1 = h1 + l1 with h = bf16(x) (round to nearest even) and
+// l = bf16(x - h): hi = (h0, h1), lo = (l0, l1) as packed bf16 pairs
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack2(x0, x1);
+  lo = pack2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
 }
 
-__device__ __forceinline__ void load_prod(ProdIn& in, const Problem& p, long long tok0, int m, int h, int g, int c) {
-  const long long row = ((tok0 + min(c, m - 1)) * p.H + h) * D + 4 * g;
+// Where one chunk's producer inputs are: wavefront-uniform bases (chunk start,
+// head) plus 32-bit lane offsets; rows past the chunk end repeat its last row.
+struct InAddr {
+  const uint16_t *q, *k, *g, *b;
+  uint32_t row, brow;
+};
+
+__device__ __forceinline__ InAddr in_addr(const Problem& p, long long tok0, int m, int h, int g, int c) {
+  const long long base = (tok0 * p.H + h) * D;
+  InAddr a;
+  a.q = p.q + base;
+  a.k = p.k + base;
+  a.g = p.g + base;
+  a.b = p.beta + tok0 * p.H + h;
+  a.row = __umul24((uint32_t)min(c, m - 1), (uint32_t)(p.H * D)) + 4 * g;
+  a.brow = __umul24((uint32_t)min(c, m - 1), (uint32_t)p.H);
+  return a;
+}
+
+// k-step s of q, k and g: channels 32s+4g+0..3, then 32s+16+4g+0..3
+__device__ __forceinline__ void load_part(ProdIn& in, const InAddr& a, int s) {
+  const uint32_t o = a.row + 32 * s;
+  in.q[s] = cat(*reinterpret_cast<const u32x2*>(a.q + o), *reinterpret_cast<const u32x2*>(a.q + o + 16));
+  in.k[s] = cat(*reinterpret_cast<const u32x2*>(a.k + o), *reinterpret_cast<const u32x2*>(a.k + o + 16));
+  in.g[s] = cat(*reinterpret_cast<const u32x2*>(a.g + o), *reinterpret_cast<const u32x2*>(a.g + o + 16));
+}
+
+__device__ __forceinline__ void load_prod(ProdIn& in, const InAddr& a) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int off = 32 * (i >> 1) + 16 * (i & 1);
-    in.q[i] = *reinterpret_cast<const u32x2*>(p.q + row + off);
-    in.k[i] = *reinterpret_cast<const u32x2*>(p.k + row + off);
-    in.g[i] = *reinterpret_cast<const u32x2*>(p.g + row + off);
-  }
-  in.b = p.beta[(tok0 + min(c, m - 1)) * p.H + h];
+  for (int s = 0; s < 4; ++s) load_part(in, a, s);
+  in.b = a.b[a.brow];
 }
 
 // V[4g+0..3][col] of one 16-column tile as raw bf16 values; masked and packed
@@ -145,8 +172,9 @@ struct VRaw {
 };
 
 __device__ __forceinline__ void load_v(VRaw& x, const Problem& p, long long tok0, int m, int h, int g, int col) {
+  const uint16_t* v = p.v + (tok0 * p.H + h) * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) x.r[i] = p.v[((tok0 + min(4 * g + i, m - 1)) * p.H + h) * D + col];
+  for (int i = 0; i < 4; ++i) x.r[i] = v[__umul24((uint32_t)min(4 * g + i, m - 1), (uint32_t)(p.H * D)) + col];
 }
 
 __device__ __forceinline__ u32x2 pack_v(const VRaw& x, int m, int g) {
@@ -157,88 +185,101 @@ __device__ __forceinline__ u32x2 pack_v(const VRaw& x, int m, int g) {
 }
 
 // ---------------------------------------------------------------- producer
-// Prepares one chunk into a ring slot.  want_q: also Qbar and Aqk (RECUR).
-__device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, const ProdIn& in, const Problem& p, int m,
-                                        float a, bool want_q, int L, int g, int c) {
-  const bool ok = c < m;
-  // squared norms of q_c, k_c over the 128 channels
-  float sq = 0.f, sk = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float qf[4], kf[4];
-    unpack4(in.q[i], qf);
-    unpack4(in.k[i], kf);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sq = fmaf(qf[e], qf[e], sq);
-      sk = fmaf(kf[e], kf[e], sk);
-    }
-  }
-  sq += __shfl_xor(sq, 16, 64);
-  sq += __shfl_xor(sq, 32, 64);
-  sk += __shfl_xor(sk, 16, 64);
-  sk += __shfl_xor(sk, 32, 64);
-  const float rq = ok ? p.scale * __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;  // zero rows past m
-  const float rk = ok ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 0.f;
-  const float bt = ok ? __builtin_amdgcn_rcpf(1.0f + __expf(-__uint_as_float(in.b << 16))) : 0.f;
-  sm.bt[pw][c] = bt;  // the four lanes of a token store the same value
-  wave_lds_sync();
+__device__ __forceinline__ float pick4(f32x4 v, int i) { return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3]; }
 
+// Prepares one chunk into a ring slot.  want_q: also Qbar and Aqk (RECUR).
+// a2 = log2(e) exp(A_log); the log decays are kept in base 2 (G2 = G log2 e),
+// so every exponential is one v_exp_f32.
+// Each part of `in` is reloaded from `next` (the producer's next chunk) as soon
+// as it has been used, so the inputs of one chunk are in flight while the
+// previous one is prepared, in the same registers.
+__device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, const InAddr& next,
+                                        const Problem& p, int m, float a2, bool want_q, int L, int g, int c) {
+  const bool ok = c < m;
+  // |q_c|^2, |k_c|^2: diagonals of the Gram matrices q q^T, k k^T from bf16 MFMAs
+  // (bf16 products are exact in fp32); token c's entry is element c%4 of lane
+  // 16(c/4)+c
+  f32x4 gq = zero4(), gk = zero4();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    gq = mfma_k32(in.q[s], in.q[s], gq);
+    gk = mfma_k32(in.k[s], in.k[s], gk);
+  }
+  const int diag = 16 * (c >> 2) + c;
+  const float sq = __shfl(pick4(gq, c & 3), diag, 64);
+  const float sk = __shfl(pick4(gk, c & 3), diag, 64);
+  // rows past the chunk end: zero key, query, beta and log decay
+  const float rq = ok ? p.scale * __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;
+  const float rk = ok ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 0.f;
+  const float lb2 = ok ? p.lower_bound * LOG2E : 0.f;
+  const float bt =
+      ok ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * __uint_as_float(in.b << 16))) : 0.f;
+  sm.bt[pw][c] = bt;  // the four lanes of a token store the same value
+  in.b = next.b[next.brow];
+
+  // A_raw = Kbar Ktil^T from bf16 operands (one MFMA per k-step), Aqk^T =
+  // Ktil Qbar^T from bf16 high/low operands (hi.hi + hi.lo + lo.hi)
+  uint16_t* ktp16 = reinterpret_cast<uint16_t*>(&sl.ktp[0][0]) + 8 * (c >> 2) + (c & 3);
   f32x4 Araw = zero4(), AqkT = zero4();
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    float qf[8], kf[8], gf[8];
-    unpack4(in.q[2 * s], qf);
-    unpack4(in.q[2 * s + 1], qf + 4);
-    unpack4(in.k[2 * s], kf);
-    unpack4(in.k[2 * s + 1], kf + 4);
-    unpack4(in.g[2 * s], gf);
-    unpack4(in.g[2 * s + 1], gf + 4);
-    float Kb[8], Kt[8], Qb[8], Kh[8], gce[8], adt[8];
-    *reinterpret_cast<f32x4*>(&adt[0]) = *reinterpret_cast<const f32x4*>(&sm.adt[32 * s + 4 * g]);
-    *reinterpret_cast<f32x4*>(&adt[4]) = *reinterpret_cast<const f32x4*>(&sm.adt[32 * s + 16 + 4 * g]);
+    const f32x4 adt0 = *reinterpret_cast<const f32x4*>(&sm.adt[32 * s + 4 * g]);
+    const f32x4 adt1 = *reinterpret_cast<const f32x4*>(&sm.adt[32 * s + 16 + 4 * g]);
+    uint32_t kbh[4], kth[4], ktl[4], qbh[4], qbl[4];
+    float gce[8];
+    // element pairs (2i, 2i+1): channels 32s + 16(i/2) + 4g + 2(i%2) + 0, 1,
+    // split into bf16 high/low pairs as soon as both are formed
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = fmaf(a, gf[e], adt[e]);
-      const float l = ok ? p.lower_bound * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) : 0.f;
-      const float G = row_scan(l);
-      const float ep = __expf(G), em = __expf(-G);
-      gce[e] = row_last(ep);
-      const float kh = kf[e] * rk;
-      Kb[e] = kh * ep;
-      Kt[e] = kh * em;
-      Qb[e] = qf[e] * rq * ep;
-      Kh[e] = Kt[e] * gce[e];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qw = in.q[s][i], kw = in.k[s][i], gw = in.g[s][i];
+      float Kb[2], Kt[2], Qb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float qv = __uint_as_float(h ? (qw & 0xFFFF0000u) : (qw << 16));
+        const float kv = __uint_as_float(h ? (kw & 0xFFFF0000u) : (kw << 16));
+        const float gv = __uint_as_float(h ? (gw & 0xFFFF0000u) : (gw << 16));
+        const int e = 2 * i + h;
+        const float ad = (e < 4) ? adt0[e] : adt1[e - 4];
+        // l2 = log2(e) lower_bound sigmoid(exp(A_log) (g + dt_bias))
+        const float x2 = fmaf(a2, gv, ad);
+        const float l2 = lb2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x2));
+        const float G2 = row_scan(l2);
+        const float ep = __builtin_amdgcn_exp2f(G2), em = __builtin_amdgcn_exp2f(-G2);
+        gce[e] = row_last(ep);
+        const float kr = kv * rk;
+        Kb[h] = kr * ep;
+        Kt[h] = kr * em;
+        Qb[h] = (qv * rq) * ep;
+      }
+      kbh[i] = pack2(Kb[0], Kb[1]);
+      split_pair(Kt[0], Kt[1], kth[i], ktl[i]);
+      if (want_q) split_pair(Qb[0], Qb[1], qbh[i], qbl[i]);
+      // Ktil, channel-major: ktp[ch][c/4] holds tokens 4(c/4)..+3, high parts
+      // then low parts
+      const int ch = 32 * s + 16 * (i >> 1) + 4 * g + 2 * (i & 1);
+      ktp16[32 * ch] = (uint16_t)(kth[i] & 0xFFFFu);
+      ktp16[32 * (ch + 1)] = (uint16_t)(kth[i] >> 16);
+      ktp16[32 * ch + 4] = (uint16_t)(ktl[i] & 0xFFFFu);
+      ktp16[32 * (ch + 1) + 4] = (uint16_t)(ktl[i] >> 16);
     }
-    u32x4 kbh, kbl, kth, ktl;
-    split8(Kb, kbh, kbl);
-    split8(Kt, kth, ktl);
-    Araw = mfma_k32(kbh, kth, Araw);  // D[4g+i][c] += Kbar_{4g+i} . Ktil_c over this k-step
-    Araw = mfma_k32(kbh, ktl, Araw);
-    Araw = mfma_k32(kbl, kth, Araw);
-    sl.kbf[s][L] = kbh;
+    const u32x4 kbh4 = {kbh[0], kbh[1], kbh[2], kbh[3]};
+    const u32x4 kth4 = {kth[0], kth[1], kth[2], kth[3]}, ktl4 = {ktl[0], ktl[1], ktl[2], ktl[3]};
+    Araw = mfma_k32(kbh4, kth4, Araw);  // D[4g+i][c] += Kbar_{4g+i} . Ktil_c over this k-step
+    sl.kbf[s][L] = kbh4;
     if (want_q) {
-      u32x4 qbh, qbl;
-      split8(Qb, qbh, qbl);
-      AqkT = mfma_k32(kth, qbh, AqkT);  // D[4g+i][c] += Ktil_{4g+i} . Qbar_c = Aqk[c][4g+i]
-      AqkT = mfma_k32(kth, qbl, AqkT);
-      AqkT = mfma_k32(ktl, qbh, AqkT);
-      sl.qbf[s][L] = qbh;
-    }
-    // Khat^T (channel-major) high / low, and gamma_C
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int ch = 32 * s + 16 * (e >> 2) + 4 * g + (e & 3);
-      const float hh = hi_part(Kh[e]);
-      const uint32_t pk = pack2(hh, Kh[e] - hh);
-      sl.khT[0][ch][c] = (uint16_t)(pk & 0xFFFFu);
-      sl.khT[1][ch][c] = (uint16_t)(pk >> 16);
+      const u32x4 qbh4 = {qbh[0], qbh[1], qbh[2], qbh[3]}, qbl4 = {qbl[0], qbl[1], qbl[2], qbl[3]};
+      AqkT = mfma_k32(kth4, qbh4, AqkT);  // D[4g+i][c] += Ktil_{4g+i} . Qbar_c = Aqk[c][4g+i]
+      AqkT = mfma_k32(kth4, qbl4, AqkT);
+      AqkT = mfma_k32(ktl4, qbh4, AqkT);
+      sl.qbf[s][L] = qbh4;
     }
     if (c == 0) {
       *reinterpret_cast<f32x4*>(&sl.gC[32 * s + 4 * g]) = f32x4{gce[0], gce[1], gce[2], gce[3]};
       *reinterpret_cast<f32x4*>(&sl.gC[32 * s + 16 + 4 * g]) = f32x4{gce[4], gce[5], gce[6], gce[7]};
     }
+    load_part(in, next, s);
   }
+  wave_lds_sync();
 
   // A = StrictLower(Diag(b) A_raw) into the solve layout Aq[i][4(p%4) + p/4] = A[i][p]
 #pragma unroll
@@ -252,7 +293,8 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, const ProdIn
     for (int i = 0; i < 4; ++i) aq[i] = (4 * g + i <= c) ? AqkT[i] : 0.f;
     u32x2 ah, al;
     split4(aq, ah, al);
-    sl.aq[L] = cat(ah, al);
+    sl.aqa[L] = cat(ah, ah);
+    sl.aqb[L] = u32x4{al.x, al.y, 0u, 0u};
   }
 
   wave_lds_sync();
@@ -264,10 +306,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, const ProdIn
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const f32x4 ar = *reinterpret_cast<const f32x4*>(&sm.Aq[pw][i][4 * q]);  // A[i][q+4k], k = 0..3
-      float part = ar[0] * t0;
-      part = fmaf(ar[1], t1, part);
-      part = fmaf(ar[2], t2, part);
-      part = fmaf(ar[3], t3, part);
+      float part = fmaf(ar[1], t1, ar[0] * t0) + fmaf(ar[3], t3, ar[2] * t2);
       part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0xB1, 0xF, 0xF, false));  // quad xor 1
       part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0x4E, 0xF, 0xF, false));  // quad xor 2
       const float tij = (i == j) ? 1.f : ((i < j) ? 0.f : -part);
@@ -292,41 +331,61 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, const ProdIn
 
 // ---------------------------------------------------------------- consumer
 // A state column tile is f32x4 S[8]: S[t] holds rows 16t+4g+0..3 of column c.
+// U of a column tile is carried as three MFMA operands built from its
+// high/low parts: ua = [U_hi | U_lo] (A operand, for Aqk U), and the B
+// operands b1 = [U_hi ; U_hi], b2 = [U_lo ; 0] of the state update
+//   [Ktil_hi | Ktil_lo] b1 + [Ktil_hi | Ktil_lo] b2 = Ktil_hi U_hi + Ktil_lo U_hi + Ktil_hi U_lo.
+struct UOps {
+  u32x4 ua, b1, b2;
+};
 
-// U = Ut - T'(Kbar S) of one column tile as a high/low pair (Ut = T'V, or 0 when v is null)
-__device__ __forceinline__ u32x4 tile_u(const u32x2 (&Sb)[8], const u32x4 (&kb)[4], u32x4 tf, const u32x2* v) {
-  f32x4 Y = zero4();
+__device__ __forceinline__ void pack_tile(const f32x4 (&S)[8], u32x2 (&Sb)[8]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) Y = mfma_k32(kb[s], cat(Sb[2 * s], Sb[2 * s + 1]), Y);
+  for (int tt = 0; tt < 8; ++tt) Sb[tt] = pack4(S[tt]);
+}
+
+// Y = Kbar S for NT column tiles, interleaved so consecutive MFMAs are independent
+template <int NT>
+__device__ __forceinline__ void tiles_y(const u32x2 (&Sb)[NT][8], const u32x4 (&kb)[4], f32x4 (&Y)[NT]) {
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj) Y[jj] = zero4();
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int jj = 0; jj < NT; ++jj) Y[jj] = mfma_k32(kb[s], cat(Sb[jj][2 * s], Sb[jj][2 * s + 1]), Y[jj]);
+}
+
+// U = Ut - T' Y (Ut = T' V, or 0 when v is null) as MFMA operands
+__device__ __forceinline__ UOps tile_u(f32x4 Y, u32x4 tf, const u32x2* v) {
   const u32x2 Yb = pack4(Y);
   const f32x4 X = mfma_k32(tf, cat(Yb, Yb), zero4());
   const f32x4 U = v ? mfma_k32(tf, cat(*v, *v), zero4()) - X : -X;
   u32x2 uh, ul;
   split4(U, uh, ul);
-  return cat(uh, ul);
+  UOps o;
+  o.ua = cat(uh, ul);
+  o.b1 = cat(uh, uh);
+  o.b2 = u32x4{ul.x, ul.y, 0u, 0u};
+  return o;
 }
 
-// S <- Diag(gamma_C) S + Khat^T U for NT column tiles; the Khat / gamma_C
-// fragments of a row tile are read once and used by every column tile
+// S <- Diag(gamma_C) (S + Ktil^T U) (= Diag(gamma_C) S + Khat^T U) for NT column
+// tiles; the Ktil / gamma_C fragments of a row tile are read once and used by
+// every column tile.  Ktil = k^ e^-G reaches e^80 where gamma_C is e^-80, and
+// the sum is formed at that scale before the decay: its fp32 rounding is then
+// relative to the Khat^T U term, as in the unscaled form.
 template <int NT>
-__device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const u32x4 (&Uhl)[NT], const Slot& sl, int g, int c) {
+__device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const UOps (&u)[NT], const Slot& sl, int g, int c) {
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    const int ch = 16 * tt + c;
-    const u32x2 kh = *reinterpret_cast<const u32x2*>(&sl.khT[0][ch][4 * g]);
-    const u32x2 kl = *reinterpret_cast<const u32x2*>(&sl.khT[1][ch][4 * g]);
+    const u32x4 kp = sl.ktp[16 * tt + c][g];
     const f32x4 gc = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
 #pragma unroll
     for (int jj = 0; jj < NT; ++jj) {
-      const f32x4 acc = mfma_k32(cat(kh, kh), Uhl[jj], S[jj][tt] * gc);
-      S[jj][tt] = mfma_k32(cat(kl, kl), Uhl[jj], acc);
+      const f32x4 acc = mfma_k32(kp, u[jj].b1, S[jj][tt]);
+      S[jj][tt] = mfma_k32(kp, u[jj].b2, acc) * gc;
     }
   }
-}
-
-__device__ __forceinline__ void pack_tile(const f32x4 (&S)[8], u32x2 (&Sb)[8]) {
-#pragma unroll
-  for (int tt = 0; tt < 8; ++tt) Sb[tt] = pack4(S[tt]);
 }
 
 // All loads are issued before any value is converted, so they overlap.
@@ -409,23 +468,30 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   auto chunk_m = [&](int lc) { return min(C, seq_len - C * (cb + lc - first_chunk)); };
   auto chunk_tok0 = [&](int lc) { return seq_tok0 + (long long)C * (cb + lc - first_chunk); };
 
-  if (threadIdx.x < D) sm.adt[threadIdx.x] = expf(p.A_log[h]) * p.dt_bias[h * D + threadIdx.x];
+  const float a2 = LOG2E * expf(p.A_log[h]);
+  if (threadIdx.x < D) sm.adt[threadIdx.x] = a2 * p.dt_bias[h * D + threadIdx.x];
   if (threadIdx.x < NSLOT) sm.ready[threadIdx.x] = -1;
-  if (threadIdx.x < NSLOT * 4) sm.done[threadIdx.x >> 2][threadIdx.x & 3] = -1;
+  if (threadIdx.x < NSLOT * NCW) sm.done[threadIdx.x / NCW][threadIdx.x % NCW] = -1;
   __syncthreads();
 
-  if (wave < 4) {
+  if (wave < NPW) {
     // ======================= producer =======================
     const int pw = wave;
-    const float a = expf(p.A_log[h]);
-    ProdIn inA, inB;
-    auto run = [&](const ProdIn& in, int lc) -> bool {
+    ProdIn in;
+    // past the last chunk the next-chunk address repeats the current one
+    // (always in bounds, loaded and unused)
+    auto addr = [&](int lc) {
+      const int lcc = lc < nch ? lc : lc - NPW;
+      return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, g, c);
+    };
+    auto run = [&](int lc) -> bool {
       const int slot = lc % NSLOT;
       if (lc >= NSLOT) {  // wait until every consumer is done with chunk lc - NSLOT
         int it = 0;
         while (true) {
-          const int d = min(min(wg_load(&sm.done[slot][0]), wg_load(&sm.done[slot][1])),
-                            min(wg_load(&sm.done[slot][2]), wg_load(&sm.done[slot][3])));
+          int d = wg_load(&sm.done[slot][0]);
+#pragma unroll
+          for (int w = 1; w < NCW; ++w) d = min(d, wg_load(&sm.done[slot][w]));
           if (d >= lc - NSLOT) break;
           if (++it > SPIN_LIMIT) {
             if (L == 0) atomicOr(&t.counters[CNT_FLAGS], 0x100);
@@ -434,37 +500,32 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      produce(sm, sm.slot[slot], pw, in, p, chunk_m(lc), a, ROLE == RECUR, L, g, c);
+      produce(sm, sm.slot[slot], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, ROLE == RECUR, L, g, c);
       wg_store(&sm.ready[slot], lc);
       return true;
     };
-    // the next chunk's inputs are loaded before this one is prepared; past the
-    // last chunk the load repeats the current one (always in bounds, unused)
-    auto load = [&](ProdIn& in, int lc) {
-      const int lcc = lc < nch ? lc : lc - 4;
-      load_prod(in, p, chunk_tok0(lcc), chunk_m(lcc), h, g, c);
-    };
-    int lc = pw;
-    if (lc < nch) load(inA, lc);
-    while (lc < nch) {
-      load(inB, lc + 4);
-      if (!run(inA, lc)) break;
-      lc += 4;
-      if (lc >= nch) break;
-      load(inA, lc + 4);
-      if (!run(inB, lc)) break;
-      lc += 4;
-    }
+    if (pw < nch) load_prod(in, addr(pw));
+    for (int lc = pw; lc < nch; lc += NPW)
+      if (!run(lc)) break;
     return;
   }
 
   // ======================= consumer =======================
-  const int cw = wave - 4;
-  const int col0 = 32 * cw;
+  const int cw = wave - NPW;
+  const int col0 = 16 * TPW * cw;
   const long long state_base = ((long long)seq * H + h) * D * D;
   const long long seg_base = ((long long)sidx * H + h) * D * D;
 
+  // The next chunk's ready flag is read early (relaxed) and looked at only
+  // after this chunk is done; a chunk seen ready there needs no wait.  The
+  // slot reads stay behind that load: a signal fence keeps the compiler from
+  // moving them, and LDS performs one wavefront's accesses in order.
+  int seen = -1;
+  auto peek_ready = [&](int lc) {
+    return __hip_atomic_load(&sm.ready[lc % NSLOT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
   auto wait_ready = [&](int slot, int lc) -> bool {
+    if (ROLE == RECUR && seen == lc) return true;  // seen by the early read
     int it = 0;
     while (wg_load(&sm.ready[slot]) != lc) {
       if (++it > SPIN_LIMIT) {
@@ -478,24 +539,26 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 
   // V of the next chunk is loaded before this one is applied; past the last
   // chunk the load repeats the last one (always in bounds, unused)
-  VRaw vA[2], vB[2];
-  auto loadv = [&](VRaw (&v)[2], int lc) {
+  VRaw vA[TPW], vB[TPW];
+  auto loadv = [&](VRaw (&v)[TPW], int lc) {
     const int lcc = min(lc, nch - 1);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) load_v(v[jj], p, chunk_tok0(lcc), chunk_m(lcc), h, g, col0 + 16 * jj + c);
+    for (int jj = 0; jj < TPW; ++jj) load_v(v[jj], p, chunk_tok0(lcc), chunk_m(lcc), h, g, col0 + 16 * jj + c);
   };
 
   if (ROLE == RECUR) {
-    f32x4 S[2][8];
+    f32x4 S[TPW][8];
     {
       const bool from_seg = (phase == 1);
-      load_state<2>(S, from_seg ? (const void*)(segS + seg_base) : p.init_state, from_seg || p.state_fp32,
-                    from_seg ? 0 : state_base, col0, g, c);
+      load_state<TPW>(S, from_seg ? (const void*)(segS + seg_base) : p.init_state, from_seg || p.state_fp32,
+                      from_seg ? 0 : state_base, col0, g, c);
     }
-    auto step = [&](const VRaw (&vr)[2], int lc) -> bool {
+    auto step = [&](const VRaw (&vr)[TPW], int lc) -> bool {
       const int slot = lc % NSLOT;
       if (!wait_ready(slot, lc)) return false;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       const Slot& sl = sm.slot[slot];
+      const int peek = peek_ready(lc + 1);
       u32x4 kb[4], qb[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -503,28 +566,40 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         qb[s] = sl.qbf[s][L];
       }
       const u32x4 tf = sl.tf[L];
-      const u32x4 aqf = sl.aq[L];
-      const u32x4 aqh = u32x4{aqf.x, aqf.y, aqf.x, aqf.y};
-      const u32x4 aql = u32x4{aqf.z, aqf.w, aqf.z, aqf.w};
       const int m = chunk_m(lc);
-      const long long tok = chunk_tok0(lc) + c;
-      const u32x2 v[2] = {pack_v(vr[0], m, g), pack_v(vr[1], m, g)};
-      u32x4 Uhl[2];
+      u32x2 v[TPW];
+      u32x2 Sb[TPW][8];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        u32x2 Sb[8];
-        pack_tile(S[jj], Sb);
-        Uhl[jj] = tile_u(Sb, kb, tf, &v[jj]);
-        // O^T = S^T Qbar^T + U^T Aqk^T
-        f32x4 Ot = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Ot = mfma_k32(cat(Sb[2 * s], Sb[2 * s + 1]), qb[s], Ot);
-        Ot = mfma_k32(Uhl[jj], aqh, Ot);
-        Ot = mfma_k32(Uhl[jj], aql, Ot);
-        if (c < m) *reinterpret_cast<u32x2*>(p.out + (tok * H + h) * D + col0 + 16 * jj + 4 * g) = pack4(Ot);
+      for (int jj = 0; jj < TPW; ++jj) {
+        v[jj] = pack_v(vr[jj], m, g);
+        pack_tile(S[jj], Sb[jj]);
       }
-      tiles_update<2>(S, Uhl, sl, g, c);
+      // O^T = S^T Qbar^T + U^T Aqk^T, Y = Kbar S: independent MFMA chains
+      f32x4 Y[TPW], Ot[TPW];
+      tiles_y<TPW>(Sb, kb, Y);
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(cat(Sb[jj][2 * s], Sb[jj][2 * s + 1]), qb[s], Ot[jj]);
+      UOps u[TPW];
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) u[jj] = tile_u(Y[jj], tf, &v[jj]);
+      const u32x4 aqa = sl.aqa[L], aqb = sl.aqb[L];
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqa, Ot[jj]);
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqb, Ot[jj]);
+      tiles_update<TPW>(S, u, sl, g, c);
       wg_store(&sm.done[slot][cw], lc);
+      seen = __builtin_amdgcn_readfirstlane(peek);
+      if (c < m) {
+        uint16_t* o = p.out + (chunk_tok0(lc) * H + h) * D;
+        const uint32_t off = (uint32_t)c * (uint32_t)(H * D) + col0 + 4 * g;
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) *reinterpret_cast<u32x2*>(o + off + 16 * jj) = pack4(Ot[jj]);
+      }
       return true;
     };
     if (nch > 0) loadv(vA, 0);
@@ -550,21 +625,21 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       dst32 = segS;  // start state of the next segment of this sequence (slot sidx + 1)
       base = seg_base + (long long)H * D * D;
     }
-    store_state<2>(S, dst32, dst16, base, col0, g, c);
+    store_state<TPW>(S, dst32, dst16, base, col0, g, c);
   } else {
-    // pre-scan on the same columns: X[0..1] = R (start 0, with Ut), X[2..3] = M (start I, Ut = 0)
-    f32x4 X[4][8];
+    // pre-scan on the same columns: X[0..TPW) = R (start 0, with Ut), X[TPW..2TPW) = M (start I, Ut = 0)
+    f32x4 X[2 * TPW][8];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         X[jj][tt] = zero4();
         f32x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (16 * tt + 4 * g + i == col0 + 16 * jj + c) ? 1.f : 0.f;
-        X[2 + jj][tt] = x;
+        X[TPW + jj][tt] = x;
       }
-    auto step = [&](const VRaw (&vr)[2], int lc) -> bool {
+    auto step = [&](const VRaw (&vr)[TPW], int lc) -> bool {
       const int slot = lc % NSLOT;
       if (!wait_ready(slot, lc)) return false;
       const Slot& sl = sm.slot[slot];
@@ -573,18 +648,22 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
       const u32x4 tf = sl.tf[L];
       const int m = chunk_m(lc);
-      const u32x2 v[2] = {pack_v(vr[0], m, g), pack_v(vr[1], m, g)};
-      u32x4 Uhl[4];
+      u32x2 v[TPW];
 #pragma unroll
-      for (int x = 0; x < 4; x += 2) {  // two tiles at a time: enough independent MFMAs, bounded live range
-        u32x2 Sb0[8], Sb1[8];
-        pack_tile(X[x], Sb0);
-        pack_tile(X[x + 1], Sb1);
-        Uhl[x] = tile_u(Sb0, kb, tf, x < 2 ? &v[0] : nullptr);
-        Uhl[x + 1] = tile_u(Sb1, kb, tf, x < 2 ? &v[1] : nullptr);
+      for (int jj = 0; jj < TPW; ++jj) v[jj] = pack_v(vr[jj], m, g);
+      UOps u[2 * TPW];
+#pragma unroll
+      for (int x = 0; x < 2 * TPW; x += 2) {  // two tiles at a time: bounded live range of the packed tiles
+        u32x2 Sb[2][8];
+        pack_tile(X[x], Sb[0]);
+        pack_tile(X[x + 1], Sb[1]);
+        f32x4 Y[2];
+        tiles_y<2>(Sb, kb, Y);
+        u[x] = tile_u(Y[0], tf, x < TPW ? &v[x] : nullptr);
+        u[x + 1] = tile_u(Y[1], tf, x + 1 < TPW ? &v[x + 1] : nullptr);
         __builtin_amdgcn_sched_barrier(0);
       }
-      tiles_update<4>(X, Uhl, sl, g, c);
+      tiles_update<2 * TPW>(X, u, sl, g, c);
       wg_store(&sm.done[slot][cw], lc);
       return true;
     };
@@ -596,8 +675,8 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       loadv(vA, lc + 2);
       if (!step(vB, lc + 1)) break;
     }
-    store_state<2>(*reinterpret_cast<f32x4(*)[2][8]>(&X[0]), segR, nullptr, seg_base, col0, g, c);
-    store_state<2>(*reinterpret_cast<f32x4(*)[2][8]>(&X[2]), segM, nullptr, seg_base, col0, g, c);
+    store_state<TPW>(*reinterpret_cast<f32x4(*)[TPW][8]>(&X[0]), segR, nullptr, seg_base, col0, g, c);
+    store_state<TPW>(*reinterpret_cast<f32x4(*)[TPW][8]>(&X[TPW]), segM, nullptr, seg_base, col0, g, c);
   }
 }
 
@@ -605,7 +684,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 // MODE 1: first pass of a segmented call, blocks [0, n) pre-scan the middle
 // segments and blocks [n, 2n) run the recurrence over the first segments.
 template <int MODE>
-__global__ __launch_bounds__(512) void kda_chunk_kernel(Problem p, Tables t, float* __restrict__ segM,
+__global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, float* __restrict__ segM,
                                                         float* __restrict__ segR, float* __restrict__ segS,
                                                         int phase) {
   __shared__ Smem sm;
@@ -624,10 +703,10 @@ hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, f
                          int phase, bool segmented, hipStream_t st) {
   if (max_segs <= 0) return hipSuccess;
   if (phase == 0 && segmented) {
-    hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3((unsigned)(2 * max_segs), (unsigned)p.H), dim3(512), 0, st, p, t,
+    hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3((unsigned)(2 * max_segs), (unsigned)p.H), dim3(NTHREADS), 0, st, p, t,
                        segM, segR, segS, 0);
   } else {
-    hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3((unsigned)max_segs, (unsigned)p.H), dim3(512), 0, st, p, t, segM,
+    hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3((unsigned)max_segs, (unsigned)p.H), dim3(NTHREADS), 0, st, p, t, segM,
                        segR, segS, phase);
   }
   return hipGetLastError();
