@@ -123,6 +123,9 @@ typedef enum {
   KDA_WS_SEG_M,             /* fp32 [max_segs][H][128][128] segment transitions M^T (CP only) */
   KDA_WS_SEG_R,             /* fp32 [max_segs][H][128][128] zero-start segment states R^T (CP only) */
   KDA_WS_SEG_S,             /* fp32 [max_segs][H][128][128] state entering each segment, [v][k] (CP only) */
+  KDA_WS_SEG_MNZ,           /* int32 [max_segs][H][8]: per 16-column block of a middle segment's M, 1 if
+                               any entry is nonzero, 0 if the block underflowed to exactly zero (its M
+                               entries are then not stored) (CP only) */
   KDA_WS_MAX_CHUNKS,        /* (count, not an offset) chunk-table capacity */
   KDA_WS_MAX_SEGS,          /* (count, not an offset) segment-table capacity */
   KDA_WS_TOTAL,             /* total bytes (= kda_get_workspace_size) */

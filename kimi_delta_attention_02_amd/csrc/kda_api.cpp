@@ -141,6 +141,7 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
   take(KDA_WS_SEG_M, seg_bytes);
   take(KDA_WS_SEG_R, seg_bytes);
   take(KDA_WS_SEG_S, seg_bytes);
+  take(KDA_WS_SEG_MNZ, seg > 0 ? ms * H * (kda::D / 16) * 4 : 0);
   out->off[KDA_WS_MAX_CHUNKS] = mc;
   out->off[KDA_WS_MAX_SEGS] = ms;
   out->off[KDA_WS_TOTAL] = o;
@@ -233,6 +234,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   float* segM = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;
   float* segR = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
   float* segS = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_S]) : nullptr;
+  int32_t* segMnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
   const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
   const int64_t ms = lay.off[KDA_WS_MAX_SEGS];
 
@@ -262,16 +264,16 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   }
   if (e == hipSuccess) {
     StageTimer tm(KDA_STAGE_RECUR0, s);
-    e = kda::launch_chunks(p, t, segM, segR, segS, ms, 0, cp, s);
+    e = kda::launch_chunks(p, t, segM, segR, segS, segMnz, ms, 0, cp, s);
   }
   if (cp) {
     if (e == hipSuccess) {
       StageTimer tm(KDA_STAGE_MERGE, s);
-      e = kda::launch_merge(p, t, segM, segR, segS, s);
+      e = kda::launch_merge(p, t, segM, segR, segS, segMnz, s);
     }
     if (e == hipSuccess) {
       StageTimer tm(KDA_STAGE_RECUR1, s);
-      e = kda::launch_chunks(p, t, segM, segR, segS, ms, 1, cp, s);
+      e = kda::launch_chunks(p, t, segM, segR, segS, segMnz, ms, 1, cp, s);
     }
   }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));

@@ -3,14 +3,14 @@
 // pre-scan ("pre_scan"), in one workgroup, with the prepared operands handed
 // from producer to consumer wavefronts through an LDS ring (no HBM hand-off).
 //
-// Workgroup = 8 wavefronts for one (segment, head):
-//   producers 0..3 : wavefront p prepares chunks p, p+4, p+8, ... of the
-//                    segment, each one alone (lane (g, c) = token c with key
-//                    channels {32s+4g+0..3, 32s+16+4g+0..3}, s = 0..3, the
-//                    consumers' own operand order), into ring slot (chunk % 6)
-//   consumers 4..7 : wavefront 4+w walks the chunks in order and applies them
-//                    to value columns 32w..32w+31 of the state (RECUR), or of
-//                    both R and M (pre-scan), held in MFMA accumulators.
+// Workgroup = 12 wavefronts (3 per SIMD) for one (segment, head):
+//   producers 0..3  : wavefront p prepares chunks p, p+4, p+8, ... of the
+//                     segment, each one alone (lane (g, c) = token c with key
+//                     channels {32s+4g+0..3, 32s+16+4g+0..3}, s = 0..3, the
+//                     consumers' own operand order), into ring slot chunk % 7
+//   consumers 4..11 : wavefront 4+w walks the chunks in order and applies them
+//                     to value columns 16w..16w+15 of the state (RECUR), or of
+//                     both R and M (pre-scan), held in MFMA accumulators.
 // Producers and consumers meet at per-slot flags in LDS (ready: the chunk a
 // slot holds; done: the last chunk each consumer finished with it).  Every
 // wait is bounded, so a wavefront always exits; a wait that gives up sets an
@@ -49,7 +49,7 @@ constexpr int NPW = 4;                  // producer wavefronts
 constexpr int NCW = 8;                  // consumer wavefronts
 constexpr int TPW = (D / 16) / NCW;     // 16-column state tiles per consumer wavefront
 constexpr int NTHREADS = 64 * (NPW + NCW);
-constexpr int NSLOT = 6;
+constexpr int NSLOT = 7;
 constexpr int MP = 20;               // fp32 16x16 matrix pitch
 constexpr int SPIN_LIMIT = 1 << 24;  // polls (each with s_sleep) before a wait gives up
 constexpr float LOG2E = 1.4426950408889634f;
@@ -114,9 +114,6 @@ __device__ __forceinline__ float row_scan(float x) {
   x += dppz<0x118>(x);  // row_shr:8
   return x;
 }
-
-// value of lane 15 of each row, broadcast to the row (row_newbcast:15)
-__device__ __forceinline__ float row_last(float x) { return dppz<0x15F>(x); }
 
 __device__ __forceinline__ void unpack4(u32x2 v, float* f) {
   f[0] = __uint_as_float(v.x << 16);
@@ -226,7 +223,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
     const f32x4 adt0 = *reinterpret_cast<const f32x4*>(&sm.adt[32 * s + 4 * g]);
     const f32x4 adt1 = *reinterpret_cast<const f32x4*>(&sm.adt[32 * s + 16 + 4 * g]);
     uint32_t kbh[4], kth[4], ktl[4], qbh[4], qbl[4];
-    float gce[8];
+    float ep_last[8];  // e^G of token 15 = gamma_C (rows past the chunk end add no decay)
     // element pairs (2i, 2i+1): channels 32s + 16(i/2) + 4g + 2(i%2) + 0, 1,
     // split into bf16 high/low pairs as soon as both are formed
 #pragma unroll
@@ -245,7 +242,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
         const float l2 = lb2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x2));
         const float G2 = row_scan(l2);
         const float ep = __builtin_amdgcn_exp2f(G2), em = __builtin_amdgcn_exp2f(-G2);
-        gce[e] = row_last(ep);
+        ep_last[e] = ep;
         const float kr = kv * rk;
         Kb[h] = kr * ep;
         Kt[h] = kr * em;
@@ -273,9 +270,9 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
       AqkT = mfma_k32(ktl4, qbh4, AqkT);
       sl.qbf[s][L] = qbh4;
     }
-    if (c == 0) {
-      *reinterpret_cast<f32x4*>(&sl.gC[32 * s + 4 * g]) = f32x4{gce[0], gce[1], gce[2], gce[3]};
-      *reinterpret_cast<f32x4*>(&sl.gC[32 * s + 16 + 4 * g]) = f32x4{gce[4], gce[5], gce[6], gce[7]};
+    if (c == C - 1) {
+      *reinterpret_cast<f32x4*>(&sl.gC[32 * s + 4 * g]) = f32x4{ep_last[0], ep_last[1], ep_last[2], ep_last[3]};
+      *reinterpret_cast<f32x4*>(&sl.gC[32 * s + 16 + 4 * g]) = f32x4{ep_last[4], ep_last[5], ep_last[6], ep_last[7]};
     }
     load_part(in, next, s);
   }
@@ -302,20 +299,22 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
   // rows p = q, q+4, q+8, q+12; row i's dot product is split over the quad
   {
     const int j = L >> 2, q = L & 3;
-    float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;  // T[q+4k][j]
+    // T[p][j] = 0 for p < j, so a row above the diagonal sums to zero and the
+    // diagonal entry (which also sums to zero) is set to 1 beforehand and kept
+    const bool d0 = (j == q), d1 = (j == q + 4), d2 = (j == q + 8), d3 = (j == q + 12);
+    float t0 = d0 ? 1.f : 0.f, t1 = d1 ? 1.f : 0.f, t2 = d2 ? 1.f : 0.f, t3 = d3 ? 1.f : 0.f;  // T[q+4k][j]
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
+    for (int i = 1; i < C; ++i) {
       const f32x4 ar = *reinterpret_cast<const f32x4*>(&sm.Aq[pw][i][4 * q]);  // A[i][q+4k], k = 0..3
       float part = fmaf(ar[1], t1, ar[0] * t0) + fmaf(ar[3], t3, ar[2] * t2);
       part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0xB1, 0xF, 0xF, false));  // quad xor 1
       part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0x4E, 0xF, 0xF, false));  // quad xor 2
-      const float tij = (i == j) ? 1.f : ((i < j) ? 0.f : -part);
-      if ((i & 3) == q) {
-        if ((i >> 2) == 0) t0 = tij;
-        else if ((i >> 2) == 1) t1 = tij;
-        else if ((i >> 2) == 2) t2 = tij;
-        else t3 = tij;
-      }
+      // row i is held by the lanes with q = i % 4, as t_{i/4}
+      const bool own = ((i & 3) == q) && (i != j);
+      if ((i >> 2) == 0) t0 = own ? -part : t0;
+      else if ((i >> 2) == 1) t1 = own ? -part : t1;
+      else if ((i >> 2) == 2) t2 = own ? -part : t2;
+      else t3 = own ? -part : t3;
     }
     const float bj = sm.bt[pw][j];
     sm.Tp[pw][(q + 0) * MP + j] = t0 * bj;  // T' = T Diag(b)
@@ -388,6 +387,29 @@ __device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const UOps (&u)[
   }
 }
 
+// The same update for two sets of column tiles (R and M of the pre-scan);
+// returns the OR of the bit patterns of the new S2 entries
+template <int NT>
+__device__ __forceinline__ uint32_t tiles_update2(f32x4 (&S1)[NT][8], const UOps (&u1)[NT], f32x4 (&S2)[NT][8],
+                                                  const UOps (&u2)[NT], const Slot& sl, int g, int c) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    const u32x4 kp = sl.ktp[16 * tt + c][g];
+    const f32x4 gc = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
+#pragma unroll
+    for (int jj = 0; jj < NT; ++jj) {
+      const f32x4 a1 = mfma_k32(kp, u1[jj].b1, S1[jj][tt]);
+      const f32x4 a2 = mfma_k32(kp, u2[jj].b1, S2[jj][tt]);
+      S1[jj][tt] = mfma_k32(kp, u1[jj].b2, a1) * gc;
+      S2[jj][tt] = mfma_k32(kp, u2[jj].b2, a2) * gc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bits |= __float_as_uint(S2[jj][tt][i]);
+    }
+  }
+  return bits;
+}
+
 // All loads are issued before any value is converted, so they overlap.
 template <int NT>
 __device__ __forceinline__ void load_state(f32x4 (&S)[NT][8], const void* src, bool f32, long long base, int col0,
@@ -442,8 +464,8 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[NT][8], float* dst3
 
 template <int ROLE>
 __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, float* __restrict__ segM,
-                                           float* __restrict__ segR, float* __restrict__ segS, int phase,
-                                           int sidx, int h) {
+                                           float* __restrict__ segR, float* __restrict__ segS,
+                                           int32_t* __restrict__ segMnz, int phase, int sidx, int h) {
   if (sidx >= t.counters[CNT_N_SEGS]) return;
   const int seq = t.seg_tab[4 * sidx + 0];
   const int cb = t.seg_tab[4 * sidx + 1];
@@ -627,19 +649,25 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     }
     store_state<TPW>(S, dst32, dst16, base, col0, g, c);
   } else {
-    // pre-scan on the same columns: X[0..TPW) = R (start 0, with Ut), X[TPW..2TPW) = M (start I, Ut = 0)
-    f32x4 X[2 * TPW][8];
+    // pre-scan on the same columns: X[0..TPW) = R (start 0, with Ut), X[TPW..2TPW) = M (start I, Ut = 0).
+    // A column of M evolves on its own (U = -T' Kbar M needs only that
+    // column), and a column that is exactly zero stays zero (every product
+    // with it is zero and gamma_C is finite).  Once this wavefront's columns
+    // of M have underflowed to zero they are no longer computed or stored.
+    f32x4 Rs[TPW][8], Ms[TPW][8];
+    bool mzero = false;
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        X[jj][tt] = zero4();
+        Rs[jj][tt] = zero4();
         f32x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (16 * tt + 4 * g + i == col0 + 16 * jj + c) ? 1.f : 0.f;
-        X[TPW + jj][tt] = x;
+        Ms[jj][tt] = x;
       }
-    auto step = [&](const VRaw (&vr)[TPW], int lc) -> bool {
+    // both R and M, until this wavefront's columns of M are zero
+    auto step_rm = [&](const VRaw (&vr)[TPW], int lc) -> bool {
       const int slot = lc % NSLOT;
       if (!wait_ready(slot, lc)) return false;
       const Slot& sl = sm.slot[slot];
@@ -648,35 +676,74 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
       const u32x4 tf = sl.tf[L];
       const int m = chunk_m(lc);
-      u32x2 v[TPW];
+      UOps ur[TPW], um[TPW];
 #pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) v[jj] = pack_v(vr[jj], m, g);
-      UOps u[2 * TPW];
-#pragma unroll
-      for (int x = 0; x < 2 * TPW; x += 2) {  // two tiles at a time: bounded live range of the packed tiles
+      for (int jj = 0; jj < TPW; ++jj) {  // one R and one M tile at a time: bounded live range
+        const u32x2 v = pack_v(vr[jj], m, g);
         u32x2 Sb[2][8];
-        pack_tile(X[x], Sb[0]);
-        pack_tile(X[x + 1], Sb[1]);
+        pack_tile(Rs[jj], Sb[0]);
+        pack_tile(Ms[jj], Sb[1]);
         f32x4 Y[2];
         tiles_y<2>(Sb, kb, Y);
-        u[x] = tile_u(Y[0], tf, x < TPW ? &v[x] : nullptr);
-        u[x + 1] = tile_u(Y[1], tf, x + 1 < TPW ? &v[x + 1] : nullptr);
+        ur[jj] = tile_u(Y[0], tf, &v);
+        um[jj] = tile_u(Y[1], tf, nullptr);
         __builtin_amdgcn_sched_barrier(0);
       }
-      tiles_update<2 * TPW>(X, u, sl, g, c);
+      const uint32_t bits = tiles_update2<TPW>(Rs, ur, Ms, um, sl, g, c);
+      wg_store(&sm.done[slot][cw], lc);
+      mzero = __builtin_amdgcn_ballot_w64((bits & 0x7FFFFFFFu) != 0u) == 0;
+      return true;
+    };
+    // R alone
+    auto step_r = [&](const VRaw (&vr)[TPW], int lc) -> bool {
+      const int slot = lc % NSLOT;
+      if (!wait_ready(slot, lc)) return false;
+      const Slot& sl = sm.slot[slot];
+      u32x4 kb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
+      const u32x4 tf = sl.tf[L];
+      const int m = chunk_m(lc);
+      u32x2 Sb[TPW][8];
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) pack_tile(Rs[jj], Sb[jj]);
+      f32x4 Y[TPW];
+      tiles_y<TPW>(Sb, kb, Y);
+      UOps ur[TPW];
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) {
+        const u32x2 v = pack_v(vr[jj], m, g);
+        ur[jj] = tile_u(Y[jj], tf, &v);
+      }
+      tiles_update<TPW>(Rs, ur, sl, g, c);
       wg_store(&sm.done[slot][cw], lc);
       return true;
     };
+    // V of chunk lc + 1 is loaded while chunk lc is applied
+    int lc = 0;
+    bool ok_run = true;
     if (nch > 0) loadv(vA, 0);
-    for (int lc = 0; lc < nch; lc += 2) {
+    for (; lc < nch && !mzero; ++lc) {
       loadv(vB, lc + 1);
-      if (!step(vA, lc)) break;
-      if (lc + 1 >= nch) break;
-      loadv(vA, lc + 2);
-      if (!step(vB, lc + 1)) break;
+      if (!step_rm(vA, lc)) {
+        ok_run = false;
+        break;
+      }
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) vA[jj] = vB[jj];
     }
-    store_state<TPW>(*reinterpret_cast<f32x4(*)[TPW][8]>(&X[0]), segR, nullptr, seg_base, col0, g, c);
-    store_state<TPW>(*reinterpret_cast<f32x4(*)[TPW][8]>(&X[TPW]), segM, nullptr, seg_base, col0, g, c);
+    for (; ok_run && lc < nch; ++lc) {
+      loadv(vB, lc + 1);
+      if (!step_r(vA, lc)) break;
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) vA[jj] = vB[jj];
+    }
+    store_state<TPW>(Rs, segR, nullptr, seg_base, col0, g, c);
+    if (!mzero) store_state<TPW>(Ms, segM, nullptr, seg_base, col0, g, c);
+    if (L == 0) {
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) segMnz[((long long)sidx * H + h) * (D / 16) + col0 / 16 + jj] = mzero ? 0 : 1;
+    }
   }
 }
 
@@ -685,29 +752,29 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 // segments and blocks [n, 2n) run the recurrence over the first segments.
 template <int MODE>
 __global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, float* __restrict__ segM,
-                                                        float* __restrict__ segR, float* __restrict__ segS,
-                                                        int phase) {
+                                                             float* __restrict__ segR, float* __restrict__ segS,
+                                                             int32_t* __restrict__ segMnz, int phase) {
   __shared__ Smem sm;
   if (MODE == 0) {
-    chunk_body<RECUR>(sm, p, t, segM, segR, segS, phase, blockIdx.x, blockIdx.y);
+    chunk_body<RECUR>(sm, p, t, segM, segR, segS, segMnz, phase, blockIdx.x, blockIdx.y);
   } else {
     const int half = gridDim.x / 2;
     if ((int)blockIdx.x < half)
-      chunk_body<PRE>(sm, p, t, segM, segR, segS, 0, blockIdx.x, blockIdx.y);
+      chunk_body<PRE>(sm, p, t, segM, segR, segS, segMnz, 0, blockIdx.x, blockIdx.y);
     else
-      chunk_body<RECUR>(sm, p, t, segM, segR, segS, 0, blockIdx.x - half, blockIdx.y);
+      chunk_body<RECUR>(sm, p, t, segM, segR, segS, segMnz, 0, blockIdx.x - half, blockIdx.y);
   }
 }
 
-hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, float* segS, int64_t max_segs,
-                         int phase, bool segmented, hipStream_t st) {
+hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, float* segS, int32_t* segMnz,
+                         int64_t max_segs, int phase, bool segmented, hipStream_t st) {
   if (max_segs <= 0) return hipSuccess;
   if (phase == 0 && segmented) {
     hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3((unsigned)(2 * max_segs), (unsigned)p.H), dim3(NTHREADS), 0, st, p, t,
-                       segM, segR, segS, 0);
+                       segM, segR, segS, segMnz, 0);
   } else {
     hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3((unsigned)max_segs, (unsigned)p.H), dim3(NTHREADS), 0, st, p, t, segM,
-                       segR, segS, phase);
+                       segR, segS, segMnz, phase);
   }
   return hipGetLastError();
 }

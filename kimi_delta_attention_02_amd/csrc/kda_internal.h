@@ -59,10 +59,12 @@ struct Problem {
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
 // producer/consumer chunk kernel: prep + recurrence / pre-scan in one launch per phase
-hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, float* segS, int64_t max_segs,
-                         int phase, bool segmented, hipStream_t st);
+// segMnz: per (segment, head, 16-column block) flag, 0 when that block of the
+// segment's transition M underflowed to exactly zero (written by the pre-scan)
+hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, float* segS, int32_t* segMnz,
+                         int64_t max_segs, int phase, bool segmented, hipStream_t st);
 hipError_t launch_merge(const Problem& p, Tables t, const float* segM, const float* segR, float* segS,
-                        hipStream_t st);
+                        const int32_t* segMnz, hipStream_t st);
 
 }  // namespace kda
 

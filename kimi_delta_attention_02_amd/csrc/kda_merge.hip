@@ -6,9 +6,11 @@
 // exact affine map of middle segment i produced by the pre-scan and S_1 was
 // written by the recurrence over segment 0.  Value columns are independent, so
 // each workgroup owns 16 of them and walks the segments of its sequence in
-// order; the products use v_mfma_f32_16x16x4_f32.  When M_i has underflowed to
-// zero the result is R_i exactly, which is what makes the segmented path
-// reproduce the serial bits once the zero-start chain has converged.
+// order; the products use v_mfma_f32_16x16x4_f32.  Column blocks of M_i that
+// underflowed to exactly zero are skipped (the pre-scan flags them and does not
+// store them); when all are zero the result is R_i exactly, which is what makes
+// the segmented path reproduce the serial bits once the zero-start chain has
+// converged.
 //
 // All matrices are stored transposed ([v][k], like the state tensors).
 #include "kda_internal.h"
@@ -20,7 +22,8 @@ constexpr int SP = 17;  // LDS pitch of the 128 x 16 column block
 }
 
 __global__ __launch_bounds__(256) void kda_merge_kernel(Problem p, Tables t, const float* __restrict__ segM,
-                                                        const float* __restrict__ segR, float* __restrict__ segS) {
+                                                        const float* __restrict__ segR, float* __restrict__ segS,
+                                                        const int32_t* __restrict__ segMnz) {
   __shared__ float Sl[D * SP];
   const int seq = blockIdx.x;
   const int h = blockIdx.y;
@@ -50,18 +53,26 @@ __global__ __launch_bounds__(256) void kda_merge_kernel(Problem p, Tables t, con
     const long long base = ((long long)(s0 + i) * H + h) * mat;
     const float* Mt = segM + base;  // Mt[p][k] = M[k][p]
     const float* Rt = segR + base;
+    // 16-row blocks of the reduction index whose columns of M are nonzero (the
+    // pre-scan leaves zero blocks unstored); all zero: S_{i+1} = R_i
+    const int32_t* nzf = segMnz + ((long long)(s0 + i) * H + h) * (D / 16);
+    uint32_t nz = 0;
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b) nz |= (nzf[b] != 0 ? 1u : 0u) << b;
     f32x4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int to = 2 * w + u;  // output row tile
       acc[u] = *reinterpret_cast<const f32x4*>(Rt + (long long)v * D + 16 * to + 4 * g);
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
+      for (int tt = 0; tt < 8; ++tt) {
+        if (!((nz >> tt) & 1u)) continue;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int pr = 16 * tt + 4 * g + ii;  // reduction index supplied by lane group g
           acc[u] = mfma_f32_k4(Mt[(long long)pr * D + 16 * to + c], Sl[pr * SP + c], acc[u]);
         }
+      }
     }
     __syncthreads();
     float* dst = segS + ((long long)(s0 + i + 1) * H + h) * mat;
@@ -77,10 +88,10 @@ __global__ __launch_bounds__(256) void kda_merge_kernel(Problem p, Tables t, con
 }
 
 hipError_t launch_merge(const Problem& p, Tables t, const float* segM, const float* segR, float* segS,
-                        hipStream_t st) {
+                        const int32_t* segMnz, hipStream_t st) {
   if (p.N <= 0) return hipSuccess;
   hipLaunchKernelGGL(kda_merge_kernel, dim3((unsigned)p.N, (unsigned)p.H, D / 16), dim3(256), 0, st, p, t, segM, segR,
-                     segS);
+                     segS, segMnz);
   return hipGetLastError();
 }
 

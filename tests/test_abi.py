@@ -63,7 +63,7 @@ def test_workspace_layout_consistent():
         off = kda.workspace_offsets(*args)
         assert off["total"] == size
         prev = -1
-        for name in kda.WS_FIELDS[:10]:
+        for name in kda.WS_FIELDS[:11]:
             assert off[name] % kda.WS_ALIGN == 0
             assert off[name] >= prev
             prev = off[name]
@@ -74,10 +74,11 @@ def test_workspace_layout_consistent():
         assert off["seg_m"] - off["seg_tab"] >= 16 * off["max_segs"]
         mat = off["max_segs"] * H * 128 * 128 * 4
         if seg == 0:
-            assert off["seg_s"] == off["seg_r"] == off["seg_m"] == off["total"]
+            assert off["seg_s"] == off["seg_r"] == off["seg_m"] == off["seg_mnz"] == off["total"]
         else:
             assert off["seg_r"] - off["seg_m"] >= mat and off["seg_s"] - off["seg_r"] >= mat
-            assert off["total"] - off["seg_s"] >= mat
+            assert off["seg_mnz"] - off["seg_s"] >= mat
+            assert off["total"] - off["seg_mnz"] >= off["max_segs"] * H * 8 * 4
 
 
 def _call(lib, **kw):
