@@ -52,8 +52,8 @@ typedef enum {
 
 typedef enum { KDA_STATE_BF16 = 0, KDA_STATE_FP32 = 1 } kda_state_dtype;
 
-/* Segment split of long sequences ("intracard context parallel" on the cuLA
- * PR #106 page: use_intracard_cp = "auto" | False | True). */
+/* Segment split of long sequences (the intracard context-parallel switch of
+ * the cuLA PR #106 page, with its automatic, off and on settings). */
 typedef enum { KDA_CP_AUTO = 0, KDA_CP_OFF = 1, KDA_CP_FORCE = 2 } kda_cp_mode;
 
 /* Segment length, in chunks of 16 tokens, that kda_fwd will use for these

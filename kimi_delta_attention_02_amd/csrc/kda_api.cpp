@@ -39,7 +39,7 @@ int32_t fail(int32_t status, const char* fmt, ...) {
 
 constexpr int64_t kMaxTokens = (int64_t)INT32_MAX - 16;  // tables are int32
 constexpr int kTargetUnits = 512;   // (segment, head) units the automatic plan aims for
-constexpr int kMinSegChunks = 32;   // shortest automatic segment (512 tokens)
+constexpr int kMinSegChunks = 16;   // shortest automatic segment (256 tokens)
 constexpr int kSerialChains = 256;  // chains that already fill the chip without splitting
 
 // ---- optional per-stage event timing (benchmarks) ----
@@ -102,13 +102,13 @@ int32_t plan(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg_c
   if (cp_mode == KDA_CP_OFF) return 0;
   if (seg_chunks > 0) return seg_chunks;
   const int64_t mc = max_chunks_for(total, N);
-  int64_t seg = (mc * H + kTargetUnits - 1) / kTargetUnits;
+  int64_t seg = mc * H / kTargetUnits;
   if (seg < kMinSegChunks) seg = kMinSegChunks;
   if (cp_mode == KDA_CP_FORCE) return (int32_t)seg;
   // automatic: keep serial when the chains already fill the chip or the
   // sequences are too short for the pre-scan and merge to pay off
   if ((int64_t)N * H >= kSerialChains) return 0;
-  if (mc < 4 * seg) return 0;
+  if (mc < 8 * seg) return 0;
   return (int32_t)seg;
 }
 
