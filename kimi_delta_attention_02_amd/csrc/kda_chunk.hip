@@ -572,7 +572,17 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     f32x4 S[TPW][8];
     {
       const bool from_seg = (phase == 1);
-      load_state<TPW>(S, from_seg ? (const void*)(segS + seg_base) : p.init_state, from_seg || p.state_fp32,
+      // start state of segment j >= 1: the merged S_j, or R_{j-1} itself when the
+      // previous middle segment's M is all zero (the merge then writes nothing)
+      const float* seg_start = segS + seg_base;
+      if (from_seg && j >= 2) {
+        const int32_t* nzf = segMnz + ((long long)(sidx - 1) * H + h) * (D / 16);
+        int nz = 0;
+#pragma unroll
+        for (int b = 0; b < D / 16; ++b) nz |= nzf[b];
+        if (nz == 0) seg_start = segR + seg_base - (long long)H * D * D;
+      }
+      load_state<TPW>(S, from_seg ? (const void*)seg_start : p.init_state, from_seg || p.state_fp32,
                       from_seg ? 0 : state_base, col0, g, c);
     }
     auto step = [&](const VRaw (&vr)[TPW], int lc) -> bool {

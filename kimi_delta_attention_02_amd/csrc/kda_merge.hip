@@ -8,9 +8,10 @@
 // each workgroup owns 16 of them and walks the segments of its sequence in
 // order; the products use v_mfma_f32_16x16x4_f32.  Column blocks of M_i that
 // underflowed to exactly zero are skipped (the pre-scan flags them and does not
-// store them); when all are zero the result is R_i exactly, which is what makes
-// the segmented path reproduce the serial bits once the zero-start chain has
-// converged.
+// store them); when all are zero S_{i+1} = R_i exactly: the merge writes nothing
+// for that boundary and the segment pass starts from R_i.  That equality is what
+// makes the segmented path reproduce the serial bits once the zero-start chain
+// has converged.
 //
 // All matrices are stored transposed ([v][k], like the state tensors).
 #include "kda_internal.h"
@@ -39,26 +40,48 @@ __global__ __launch_bounds__(256) void kda_merge_kernel(Problem p, Tables t, con
   const int v = 16 * vb + c;
   const long long mat = (long long)D * D;
 
-  {  // S_1 -> LDS
-    const float* src = segS + ((long long)(s0 + 1) * H + h) * mat;
+  // column block vb of a [v][k] matrix -> Sl[k][v - 16 vb]
+  auto to_lds = [&](const float* src) {
     for (int e = threadIdx.x; e < D * 16; e += 256) {
       const int k = e & (D - 1);
       const int vv = e >> 7;
       Sl[k * SP + vv] = src[(long long)(16 * vb + vv) * D + k];
     }
-  }
-  __syncthreads();
+  };
 
+  // Sl holds S_i when `have` is true.  When M_i is zero, S_{i+1} = R_i: nothing
+  // is computed or written, and the segment pass reads R_i as its start state.
+  // The nonzero masks of 256 boundaries at a time are read in parallel first:
+  // bit b set when the 16-row block b of the reduction index (columns of M) is
+  // nonzero (the pre-scan leaves zero blocks unstored).
+  __shared__ uint32_t nzl[256];
+  bool have = false;
   for (int i = 1; i <= ns - 2; ++i) {
+    if ((i - 1) % 256 == 0) {
+      __syncthreads();
+      const int ii = i + (int)threadIdx.x;
+      uint32_t m = 0;
+      if (ii <= ns - 2) {
+        const int32_t* f = segMnz + ((long long)(s0 + ii) * H + h) * (D / 16);
+#pragma unroll
+        for (int b = 0; b < D / 16; ++b) m |= (f[b] != 0 ? 1u : 0u) << b;
+      }
+      nzl[threadIdx.x] = m;
+      __syncthreads();
+    }
+    const uint32_t nz = nzl[(i - 1) % 256];
     const long long base = ((long long)(s0 + i) * H + h) * mat;
+    if (nz == 0) {
+      have = false;
+      continue;
+    }
+    if (!have) {  // S_i: the recurrence's output for segment 0, or R_{i-1}
+      to_lds(i == 1 ? segS + ((long long)(s0 + 1) * H + h) * mat
+                    : segR + ((long long)(s0 + i - 1) * H + h) * mat);
+      __syncthreads();
+    }
     const float* Mt = segM + base;  // Mt[p][k] = M[k][p]
     const float* Rt = segR + base;
-    // 16-row blocks of the reduction index whose columns of M are nonzero (the
-    // pre-scan leaves zero blocks unstored); all zero: S_{i+1} = R_i
-    const int32_t* nzf = segMnz + ((long long)(s0 + i) * H + h) * (D / 16);
-    uint32_t nz = 0;
-#pragma unroll
-    for (int b = 0; b < D / 16; ++b) nz |= (nzf[b] != 0 ? 1u : 0u) << b;
     f32x4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -84,6 +107,7 @@ __global__ __launch_bounds__(256) void kda_merge_kernel(Problem p, Tables t, con
       *reinterpret_cast<f32x4*>(dst + (long long)v * D + 16 * to + 4 * g) = acc[u];
     }
     __syncthreads();
+    have = true;
   }
 }
 
