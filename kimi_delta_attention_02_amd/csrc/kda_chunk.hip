@@ -7,10 +7,14 @@
 //   producers 0..3  : wavefront p prepares chunks p, p+4, p+8, ... of the
 //                     segment, each one alone (lane (g, c) = token c with key
 //                     channels {32s+4g+0..3, 32s+16+4g+0..3}, s = 0..3, the
-//                     consumers' own operand order), into ring slot chunk % 7
+//                     consumers' own operand order), into ring slot chunk % 6
 //   consumers 4..11 : wavefront 4+w walks the chunks in order and applies them
 //                     to value columns 16w..16w+15 of the state (RECUR), or of
 //                     both R and M (pre-scan), held in MFMA accumulators.
+// V goes through the slot as whole rows (the producer loads 256-byte token rows
+// with the chunk's other inputs); each consumer reads its 16-column slice and
+// overwrites it with its slice of the output, and the producer that next reuses
+// the slot writes the output rows out whole, so HBM sees full rows both ways.
 // Producers and consumers meet at per-slot flags in LDS (ready: the chunk a
 // slot holds; done: the last chunk each consumer finished with it).  Every
 // wait is bounded, so a wavefront always exits; a wait that gives up sets an
@@ -49,7 +53,7 @@ constexpr int NPW = 4;                  // producer wavefronts
 constexpr int NCW = 8;                  // consumer wavefronts
 constexpr int TPW = (D / 16) / NCW;     // 16-column state tiles per consumer wavefront
 constexpr int NTHREADS = 64 * (NPW + NCW);
-constexpr int NSLOT = 7;
+constexpr int NSLOT = 6;
 constexpr int MP = 20;               // fp32 16x16 matrix pitch
 constexpr int SPIN_LIMIT = 1 << 24;  // polls (each with s_sleep) before a wait gives up
 constexpr float LOG2E = 1.4426950408889634f;
@@ -65,6 +69,8 @@ struct Slot {
   u32x4 tf[64];       // [T'_hi | T'_lo] of row c, columns 4g..4g+3
   u32x4 aqa[64];      // [Aqk_hi | Aqk_hi] of row c, columns 4g..4g+3
   u32x4 aqb[64];      // [Aqk_lo | 0]
+  uint16_t vo[C][D];  // V rows of the chunk (producer), overwritten column slice by column slice
+                      // with O by the consumer owning those columns; written out whole rows
 };
 
 struct Smem {
@@ -82,6 +88,7 @@ struct Smem {
 struct ProdIn {
   u32x4 q[4], k[4], g[4];
   uint32_t b;
+  u32x4 v[4];  // V of token L/4, columns 32(L%4) .. 32(L%4)+31
 };
 
 // Orders this wavefront's LDS writes before its later LDS reads by other lanes
@@ -132,8 +139,8 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
 // Where one chunk's producer inputs are: wavefront-uniform bases (chunk start,
 // head) plus 32-bit lane offsets; rows past the chunk end repeat its last row.
 struct InAddr {
-  const uint16_t *q, *k, *g, *b;
-  uint32_t row, brow;
+  const uint16_t *q, *k, *g, *b, *v;
+  uint32_t row, brow, vrow;
 };
 
 __device__ __forceinline__ InAddr in_addr(const Problem& p, long long tok0, int m, int h, int g, int c) {
@@ -145,7 +152,16 @@ __device__ __forceinline__ InAddr in_addr(const Problem& p, long long tok0, int 
   a.b = p.beta + tok0 * p.H + h;
   a.row = __umul24((uint32_t)min(c, m - 1), (uint32_t)(p.H * D)) + 4 * g;
   a.brow = __umul24((uint32_t)min(c, m - 1), (uint32_t)p.H);
+  const int L = threadIdx.x & 63;
+  a.v = p.v + base;
+  a.vrow = __umul24((uint32_t)min(L >> 2, m - 1), (uint32_t)(p.H * D)) + 32 * (L & 3);
   return a;
+}
+
+// V rows of a chunk, 64 bytes per lane (coalesced 256-byte rows)
+__device__ __forceinline__ void load_vrows(ProdIn& in, const InAddr& a) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) in.v[i] = *reinterpret_cast<const u32x4*>(a.v + a.vrow + 8 * i);
 }
 
 // k-step s of q, k and g: channels 32s+4g+0..3, then 32s+16+4g+0..3
@@ -160,24 +176,14 @@ __device__ __forceinline__ void load_prod(ProdIn& in, const InAddr& a) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) load_part(in, a, s);
   in.b = a.b[a.brow];
+  load_vrows(in, a);
 }
 
-// V[4g+0..3][col] of one 16-column tile as raw bf16 values; masked and packed
-// only where they are used, so a prefetch is not waited for where it is issued
-struct VRaw {
-  uint32_t r[4];
-};
-
-__device__ __forceinline__ void load_v(VRaw& x, const Problem& p, long long tok0, int m, int h, int g, int col) {
-  const uint16_t* v = p.v + (tok0 * p.H + h) * D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x.r[i] = v[__umul24((uint32_t)min(4 * g + i, m - 1), (uint32_t)(p.H * D)) + col];
-}
-
-__device__ __forceinline__ u32x2 pack_v(const VRaw& x, int m, int g) {
+// V[4g+0..3][col] of a chunk from its slot, rows past the chunk end as zero
+__device__ __forceinline__ u32x2 slot_v(const Slot& sl, int m, int g, int col) {
   uint32_t t[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t[i] = (4 * g + i < m) ? x.r[i] : 0u;  // rows past the chunk end are zero
+  for (int i = 0; i < 4; ++i) t[i] = (4 * g + i < m) ? (uint32_t)sl.vo[4 * g + i][col] : 0u;
   return u32x2{t[0] | (t[1] << 16), t[2] | (t[3] << 16)};
 }
 
@@ -193,6 +199,12 @@ __device__ __forceinline__ float pick4(f32x4 v, int i) { return i == 0 ? v[0] : 
 __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, const InAddr& next,
                                         const Problem& p, int m, float a2, bool want_q, int L, int g, int c) {
   const bool ok = c < m;
+  {  // V rows into the slot, then the next chunk's V into the same registers
+    const int L = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sl.vo[L >> 2][32 * (L & 3) + 8 * i]) = in.v[i];
+    load_vrows(in, next);
+  }
   // |q_c|^2, |k_c|^2: diagonals of the Gram matrices q q^T, k k^T from bf16 MFMAs
   // (bf16 products are exact in fp32); token c's entry is element c%4 of lane
   // 16(c/4)+c
@@ -506,29 +518,60 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       const int lcc = lc < nch ? lc : lc - NPW;
       return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, g, c);
     };
+    // wait until every consumer is done with chunk lc (bounded)
+    auto wait_done = [&](int lc) -> bool {
+      const int slot = lc % NSLOT;
+      int it = 0;
+      while (true) {
+        int d = wg_load(&sm.done[slot][0]);
+#pragma unroll
+        for (int w = 1; w < NCW; ++w) d = min(d, wg_load(&sm.done[slot][w]));
+        if (d >= lc) return true;
+        if (++it > SPIN_LIMIT) {
+          if (L == 0) atomicOr(&t.counters[CNT_FLAGS], 0x100);
+          return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    };
+    // the output rows of chunk lc, left in its slot by the consumers: whole
+    // 256-byte rows, 64 bytes per lane
+    auto flush = [&](int lc) {
+      const Slot& sl = sm.slot[lc % NSLOT];
+      const int tok = L >> 2;
+      if (tok < chunk_m(lc)) {
+        uint16_t* o = p.out + ((chunk_tok0(lc) + tok) * H + h) * D + 32 * (L & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x4*>(o + 8 * i) = *reinterpret_cast<const u32x4*>(&sl.vo[tok][32 * (L & 3) + 8 * i]);
+      }
+    };
     auto run = [&](int lc) -> bool {
       const int slot = lc % NSLOT;
-      if (lc >= NSLOT) {  // wait until every consumer is done with chunk lc - NSLOT
-        int it = 0;
-        while (true) {
-          int d = wg_load(&sm.done[slot][0]);
-#pragma unroll
-          for (int w = 1; w < NCW; ++w) d = min(d, wg_load(&sm.done[slot][w]));
-          if (d >= lc - NSLOT) break;
-          if (++it > SPIN_LIMIT) {
-            if (L == 0) atomicOr(&t.counters[CNT_FLAGS], 0x100);
-            return false;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
+      if (lc >= NSLOT) {  // the slot's previous chunk must be consumed (and its output written out)
+        if (!wait_done(lc - NSLOT)) return false;
+        if (ROLE == RECUR) flush(lc - NSLOT);
       }
       produce(sm, sm.slot[slot], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, ROLE == RECUR, L, g, c);
       wg_store(&sm.ready[slot], lc);
       return true;
     };
     if (pw < nch) load_prod(in, addr(pw));
+    bool ok_run = true;
     for (int lc = pw; lc < nch; lc += NPW)
-      if (!run(lc)) break;
+      if (!run(lc)) {
+        ok_run = false;
+        break;
+      }
+    // the last NSLOT chunks' outputs: chunk lc goes to the producer that would
+    // have produced chunk lc + NSLOT
+    if (ROLE == RECUR && ok_run) {
+      for (int lc = max(0, nch - NSLOT); lc < nch; ++lc) {
+        if ((lc + NSLOT) % NPW != pw) continue;
+        if (!wait_done(lc)) break;
+        flush(lc);
+      }
+    }
     return;
   }
 
@@ -559,14 +602,6 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     return true;
   };
 
-  // V of the next chunk is loaded before this one is applied; past the last
-  // chunk the load repeats the last one (always in bounds, unused)
-  VRaw vA[TPW], vB[TPW];
-  auto loadv = [&](VRaw (&v)[TPW], int lc) {
-    const int lcc = min(lc, nch - 1);
-#pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) load_v(v[jj], p, chunk_tok0(lcc), chunk_m(lcc), h, g, col0 + 16 * jj + c);
-  };
 
   if (ROLE == RECUR) {
     f32x4 S[TPW][8];
@@ -585,7 +620,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       load_state<TPW>(S, from_seg ? (const void*)seg_start : p.init_state, from_seg || p.state_fp32,
                       from_seg ? 0 : state_base, col0, g, c);
     }
-    auto step = [&](const VRaw (&vr)[TPW], int lc) -> bool {
+    auto step = [&](int lc) -> bool {
       const int slot = lc % NSLOT;
       if (!wait_ready(slot, lc)) return false;
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -603,7 +638,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       u32x2 Sb[TPW][8];
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj) {
-        v[jj] = pack_v(vr[jj], m, g);
+        v[jj] = slot_v(sl, m, g, col0 + 16 * jj + c);
         pack_tile(S[jj], Sb[jj]);
       }
       // O^T = S^T Qbar^T + U^T Aqk^T, Y = Kbar S: independent MFMA chains
@@ -623,25 +658,18 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqa, Ot[jj]);
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqb, Ot[jj]);
+      // O^T tile: token c, columns col0 + 16jj + 4g..+3, into the slot's V rows
+      // (this wavefront has read its V columns); written out by a producer
+      Slot& slw = sm.slot[slot];
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot[jj]);
       tiles_update<TPW>(S, u, sl, g, c);
       wg_store(&sm.done[slot][cw], lc);
       seen = __builtin_amdgcn_readfirstlane(peek);
-      if (c < m) {
-        uint16_t* o = p.out + (chunk_tok0(lc) * H + h) * D;
-        const uint32_t off = (uint32_t)c * (uint32_t)(H * D) + col0 + 4 * g;
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) *reinterpret_cast<u32x2*>(o + off + 16 * jj) = pack4(Ot[jj]);
-      }
       return true;
     };
-    if (nch > 0) loadv(vA, 0);
-    for (int lc = 0; lc < nch; lc += 2) {
-      loadv(vB, lc + 1);
-      if (!step(vA, lc)) break;
-      if (lc + 1 >= nch) break;
-      loadv(vA, lc + 2);
-      if (!step(vB, lc + 1)) break;
-    }
+    for (int lc = 0; lc < nch; ++lc)
+      if (!step(lc)) break;
     float* dst32 = nullptr;
     uint16_t* dst16 = nullptr;
     long long base = 0;
@@ -677,7 +705,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         Ms[jj][tt] = x;
       }
     // both R and M, until this wavefront's columns of M are zero
-    auto step_rm = [&](const VRaw (&vr)[TPW], int lc) -> bool {
+    auto step_rm = [&](int lc) -> bool {
       const int slot = lc % NSLOT;
       if (!wait_ready(slot, lc)) return false;
       const Slot& sl = sm.slot[slot];
@@ -689,7 +717,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       UOps ur[TPW], um[TPW];
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj) {  // one R and one M tile at a time: bounded live range
-        const u32x2 v = pack_v(vr[jj], m, g);
+        const u32x2 v = slot_v(sl, m, g, col0 + 16 * jj + c);
         u32x2 Sb[2][8];
         pack_tile(Rs[jj], Sb[0]);
         pack_tile(Ms[jj], Sb[1]);
@@ -705,7 +733,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       return true;
     };
     // R alone
-    auto step_r = [&](const VRaw (&vr)[TPW], int lc) -> bool {
+    auto step_r = [&](int lc) -> bool {
       const int slot = lc % NSLOT;
       if (!wait_ready(slot, lc)) return false;
       const Slot& sl = sm.slot[slot];
@@ -722,32 +750,22 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       UOps ur[TPW];
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj) {
-        const u32x2 v = pack_v(vr[jj], m, g);
+        const u32x2 v = slot_v(sl, m, g, col0 + 16 * jj + c);
         ur[jj] = tile_u(Y[jj], tf, &v);
       }
       tiles_update<TPW>(Rs, ur, sl, g, c);
       wg_store(&sm.done[slot][cw], lc);
       return true;
     };
-    // V of chunk lc + 1 is loaded while chunk lc is applied
     int lc = 0;
     bool ok_run = true;
-    if (nch > 0) loadv(vA, 0);
-    for (; lc < nch && !mzero; ++lc) {
-      loadv(vB, lc + 1);
-      if (!step_rm(vA, lc)) {
+    for (; lc < nch && !mzero; ++lc)
+      if (!step_rm(lc)) {
         ok_run = false;
         break;
       }
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) vA[jj] = vB[jj];
-    }
-    for (; ok_run && lc < nch; ++lc) {
-      loadv(vB, lc + 1);
-      if (!step_r(vA, lc)) break;
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) vA[jj] = vB[jj];
-    }
+    for (; ok_run && lc < nch; ++lc)
+      if (!step_r(lc)) break;
     store_state<TPW>(Rs, segR, nullptr, seg_base, col0, g, c);
     if (!mzero) store_state<TPW>(Ms, segM, nullptr, seg_base, col0, g, c);
     if (L == 0) {
