@@ -111,9 +111,11 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
  * workspace.  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
  * order of kda_ws_offset.  Returns KDA_OK or a negative kda_status. */
 typedef enum {
-  KDA_WS_COUNTERS = 0,      /* int32[4]: n_chunks, n_segs, flags, reserved; flags bits 0x1..0x8 name
+  KDA_WS_COUNTERS = 0,      /* int32[4]: n_chunks, n_segs, flags, early_stops; flags bits 0x1..0x8 name
                                repaired cu_seqlens faults (first != 0, decreasing, last != total,
-                               out of range), 0x100 / 0x200 a chunk-kernel wait that gave up */
+                               out of range), 0x100 / 0x200 a chunk-kernel wait that gave up;
+                               early_stops counts the (segment, head) pairs whose second pass
+                               matched the checkpoint and stopped there */
   KDA_WS_SEQ_START,         /* int32[N+1]   clamped sequence boundaries (last = end of the last sequence) */
   KDA_WS_SEQ_LEN,           /* int32[N]     clamped length */
   KDA_WS_SEQ_CHUNK_OFF,     /* int32[N+1]   prefix sums of ceil(len/16) */
@@ -128,6 +130,8 @@ typedef enum {
   KDA_WS_SEG_MNZ,           /* int32 [max_segs][H][8]: per 16-column block of a middle segment's M, 1 if
                                any entry is nonzero, 0 if the block underflowed to exactly zero (its M
                                entries are then not stored) (CP only) */
+  KDA_WS_SEG_CHK,           /* fp32 [max_segs][H][128][128] zero-start state R^T of a segment >= 1 after
+                               its first 4 chunks (segments longer than that; CP only) */
   KDA_WS_MAX_CHUNKS,        /* (count, not an offset) chunk-table capacity */
   KDA_WS_MAX_SEGS,          /* (count, not an offset) segment-table capacity */
   KDA_WS_TOTAL,             /* total bytes (= kda_get_workspace_size) */

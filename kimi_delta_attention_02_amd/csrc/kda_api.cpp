@@ -5,13 +5,19 @@
 // host synchronisation, allocation or device-to-host copy:
 //   index scan + table fill
 //   -> chunk kernel, first pass: chunk prep fused with the recurrence of whole
-//      sequences / first segments, and with the pre-scan of middle segments
-//   [-> merge -> chunk kernel, second pass: segments >= 1 from merged states]
+//      sequences / first segments from the initial state, and of segments >= 1
+//      from a zero state (their transitions M while nonzero, their output
+//      after the first kCheckChunks chunks, a checkpoint of the state there)
+//   [-> merge -> chunk kernel, second pass: the first kCheckChunks chunks of
+//      segments >= 1 from their merged start states, continued to the
+//      segment's end only where the state differs from the checkpoint]
 // The bracketed part runs only when the plan splits sequences into segments.
 // It follows the segment scheme on the cuLA PR #106 page (pre-scan, merge,
-// segment recurrence), except that chunk prep is recomputed in each pass from
-// the inputs rather than stored once: a stored prep record is larger than the
-// inputs it is computed from.
+// segment recurrence), with two changes: chunk prep is recomputed in each pass
+// from the inputs rather than stored once (a stored prep record is larger than
+// the inputs it is computed from), and the zero-start pass also produces the
+// output, so that the second pass only redoes a segment's first chunks where
+// the start state's influence has decayed to nothing in fp32 by then.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -38,8 +44,9 @@ int32_t fail(int32_t status, const char* fmt, ...) {
 }
 
 constexpr int64_t kMaxTokens = (int64_t)INT32_MAX - 16;  // tables are int32
-constexpr int kTargetUnits = 512;   // (segment, head) units the automatic plan aims for
+constexpr int kTargetUnits = 256;   // (segment, head) units the automatic plan aims for: one per CU
 constexpr int kMinSegChunks = 16;   // shortest automatic segment (256 tokens)
+constexpr int kCheckChunks = 4;     // chunks the second pass redoes before comparing with the checkpoint
 constexpr int kSerialChains = 256;  // chains that already fill the chip without splitting
 
 // ---- optional per-stage event timing (benchmarks) ----
@@ -101,8 +108,10 @@ int32_t plan(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg_c
   if (seg_chunks < 0) return fail(KDA_ERR_INVALID_ARG, "seg_chunks %d must be >= 0", seg_chunks);
   if (cp_mode == KDA_CP_OFF) return 0;
   if (seg_chunks > 0) return seg_chunks;
-  const int64_t mc = max_chunks_for(total, N);
-  int64_t seg = mc * H / kTargetUnits;
+  // the work in chunks: ceil(total / 16), what equal-length sequences give
+  // (the tables are sized for the worst split, max_chunks_for)
+  const int64_t mc = (total + kda::C - 1) / kda::C;
+  int64_t seg = (mc * H + kTargetUnits - 1) / kTargetUnits;
   if (seg < kMinSegChunks) seg = kMinSegChunks;
   if (cp_mode == KDA_CP_FORCE) return (int32_t)seg;
   // automatic: keep serial when the chains already fill the chip or the
@@ -122,7 +131,7 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
   if (seg < 0) return seg;
   const int64_t mc = max_chunks_for(total, N);
   const int64_t ms = seg > 0 ? mc / seg + N : N;
-  if (mc > INT32_MAX / 2 || ms > INT32_MAX / 2)
+  if (mc > INT32_MAX / 2 || ms > INT32_MAX / 2 || ms * H > INT32_MAX)
     return fail(KDA_ERR_INVALID_ARG, "problem too large for the index tables");
   const int64_t A = KDA_WORKSPACE_ALIGN;
   int64_t o = 0;
@@ -142,6 +151,7 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
   take(KDA_WS_SEG_R, seg_bytes);
   take(KDA_WS_SEG_S, seg_bytes);
   take(KDA_WS_SEG_MNZ, seg > 0 ? ms * H * (kda::D / 16) * 4 : 0);
+  take(KDA_WS_SEG_CHK, seg_bytes);
   out->off[KDA_WS_MAX_CHUNKS] = mc;
   out->off[KDA_WS_MAX_SEGS] = ms;
   out->off[KDA_WS_TOTAL] = o;
@@ -231,10 +241,13 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   t.chunk_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_CHUNK_TAB]);
   t.seg_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_TAB]);
   const bool cp = lay.seg > 0;
-  float* segM = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;
-  float* segR = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
-  float* segS = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_S]) : nullptr;
-  int32_t* segMnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
+  kda::Seg sg;
+  sg.M = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;
+  sg.R = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
+  sg.S = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_S]) : nullptr;
+  sg.chk = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_CHK]) : nullptr;
+  sg.mnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
+  sg.chk_chunks = cp ? kCheckChunks : 0;
   const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
   const int64_t ms = lay.off[KDA_WS_MAX_SEGS];
 
@@ -264,16 +277,16 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   }
   if (e == hipSuccess) {
     StageTimer tm(KDA_STAGE_RECUR0, s);
-    e = kda::launch_chunks(p, t, segM, segR, segS, segMnz, ms, 0, cp, s);
+    e = kda::launch_chunks(p, t, sg, ms, 0, cp, s);
   }
   if (cp) {
     if (e == hipSuccess) {
       StageTimer tm(KDA_STAGE_MERGE, s);
-      e = kda::launch_merge(p, t, segM, segR, segS, segMnz, s);
+      e = kda::launch_merge(p, t, sg, s);
     }
     if (e == hipSuccess) {
       StageTimer tm(KDA_STAGE_RECUR1, s);
-      e = kda::launch_chunks(p, t, segM, segR, segS, segMnz, ms, 1, cp, s);
+      e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
     }
   }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));

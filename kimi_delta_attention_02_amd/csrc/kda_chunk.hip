@@ -1,7 +1,7 @@
 // Chunk kernel: chunk preparation ("K1" on the cuLA PR #106 page: decayed q/k,
-// beta and the WY inverse) and the inter-chunk recurrence ("K2") or the segment
-// pre-scan ("pre_scan"), in one workgroup, with the prepared operands handed
-// from producer to consumer wavefronts through an LDS ring (no HBM hand-off).
+// beta and the WY inverse) and the inter-chunk recurrence ("K2") in one
+// workgroup, with the prepared operands handed from producer to consumer
+// wavefronts through an LDS ring (no HBM hand-off).
 //
 // Workgroup = 12 wavefronts (3 per SIMD) for one (segment, head):
 //   producers 0..3  : wavefront p prepares chunks p, p+4, p+8, ... of the
@@ -9,8 +9,10 @@
 //                     channels {32s+4g+0..3, 32s+16+4g+0..3}, s = 0..3, the
 //                     consumers' own operand order), into ring slot chunk % 6
 //   consumers 4..11 : wavefront 4+w walks the chunks in order and applies them
-//                     to value columns 16w..16w+15 of the state (RECUR), or of
-//                     both R and M (pre-scan), held in MFMA accumulators.
+//                     to value columns 16w..16w+15 of the state, held in MFMA
+//                     accumulators (first pass of a segment >= 1: the
+//                     zero-start state R, plus the transition M while it is
+//                     nonzero).
 // V goes through the slot as whole rows (the producer loads 256-byte token rows
 // with the chunk's other inputs); each consumer reads its 16-column slice and
 // overwrites it with its slice of the output, and the producer that next reuses
@@ -32,7 +34,7 @@
 // and the consumers, with S the K x V state entering the chunk:
 //   Y = Kbar S;  X = T' Y (= W S, W = T' Kbar);  Ut = T' V;  U = Ut - X
 //   O = Qbar S + Aqk U;  S <- Diag(gamma_C) (S + Ktil^T U)  (Khat = Ktil gamma_C)
-// (pre-scan: M starts at I with Ut = 0, R starts at 0; neither writes O).
+// (M starts at I with Ut = 0 and writes no output).
 //
 // Every product is a 16x16x32 bf16 MFMA with fp32 accumulation; Aqk (and its
 // factors Qbar, Ktil), T', U and Ktil in the update enter as bf16 high/low pairs (x = x_hi + x_lo, ~16 significant
@@ -41,6 +43,8 @@
 // the RMS.  A 16x16 accumulator tile holds rows 4g..4g+3 of column c in lane
 // 16g+c, which is also the bf16 operand layout of the next chunk's products,
 // so the state never leaves registers within a segment.
+#include <type_traits>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -81,6 +85,7 @@ struct Smem {
   float adt[D];         // log2(e) exp(A_log) dt_bias of the head
   int ready[NSLOT];
   int done[NSLOT][NCW];
+  int vote;  // second pass at the checkpoint: +1 per consumer whose columns match, +0x100 per mismatch
 };
 
 // raw inputs of one chunk for one producer lane: q[s], k[s], g[s] hold token c,
@@ -475,19 +480,20 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[NT][8], float* dst3
 }  // namespace
 
 template <int ROLE>
-__device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, float* __restrict__ segM,
-                                           float* __restrict__ segR, float* __restrict__ segS,
-                                           int32_t* __restrict__ segMnz, int phase, int sidx, int h) {
-  if (sidx >= t.counters[CNT_N_SEGS]) return;
+__device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, const Seg& sg, int phase,
+                                           int sidx, int h) {
   const int seq = t.seg_tab[4 * sidx + 0];
   const int cb = t.seg_tab[4 * sidx + 1];
   const int ce = t.seg_tab[4 * sidx + 2];
   const int j = t.seg_tab[4 * sidx + 3];
   const int ns = t.seq_seg_off[seq + 1] - t.seq_seg_off[seq];
+  // RECUR, phase 0: segment 0 of every sequence from the initial state;
+  // RECUR, phase 1: segments >= 1 from their merged start states;
+  // PRE (first pass of a segmented call): segments >= 1 from a zero state.
   if (ROLE == RECUR) {
     if (phase == 0 ? (j != 0) : (j == 0)) return;
   } else {
-    if (!(j > 0 && j < ns - 1)) return;
+    if (j == 0) return;
   }
 
   const int H = p.H;
@@ -502,10 +508,26 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   auto chunk_m = [&](int lc) { return min(C, seq_len - C * (cb + lc - first_chunk)); };
   auto chunk_tok0 = [&](int lc) { return seq_tok0 + (long long)C * (cb + lc - first_chunk); };
 
+  // Segments >= 1 longer than K = chk_chunks chunks: the first pass (PRE)
+  // writes the output of chunks >= K from its zero-start state R and keeps R
+  // after K chunks; the second pass redoes chunks < K from the true start
+  // state and stops there if its state equals that checkpoint bit for bit
+  // (the rest is then the same computation on the same bits, already done),
+  // else it runs to the end.  The state's value columns evolve independently,
+  // so each consumer compares its own columns; the block stops when all agree.
+  const int K = sg.chk_chunks;
+  const bool has_chk = j > 0 && K > 0 && nch > K;
+  const int o_from = ROLE == PRE ? (has_chk ? K : nch) : 0;  // first chunk whose output this pass writes
+  const bool may_stop = ROLE == RECUR && phase == 1 && has_chk;
+  // a last segment without a checkpoint: the first pass has nothing to hand on
+  // (no merge after it, and the second pass runs it whole)
+  if (ROLE == PRE && j == ns - 1 && !has_chk) return;
+
   const float a2 = LOG2E * expf(p.A_log[h]);
   if (threadIdx.x < D) sm.adt[threadIdx.x] = a2 * p.dt_bias[h * D + threadIdx.x];
   if (threadIdx.x < NSLOT) sm.ready[threadIdx.x] = -1;
   if (threadIdx.x < NSLOT * NCW) sm.done[threadIdx.x / NCW][threadIdx.x % NCW] = -1;
+  if (threadIdx.x == 0) sm.vote = 0;
   __syncthreads();
 
   if (wave < NPW) {
@@ -518,18 +540,31 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       const int lcc = lc < nch ? lc : lc - NPW;
       return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, g, c);
     };
-    // wait until every consumer is done with chunk lc (bounded)
-    auto wait_done = [&](int lc) -> bool {
-      const int slot = lc % NSLOT;
+    // chunks the block runs: nch, or K once the consumers agreed to stop
+    // there; -1 while their vote is incomplete
+    auto n_run = [&sm, may_stop, K, nch]() -> int {
+      if (!may_stop) return nch;
+      const int v = wg_load(&sm.vote);
+      if ((v & 0xFF) + (v >> 8) < NCW) return -1;
+      return v == NCW ? K : nch;
+    };
+    // 1 once every consumer is done with chunk y, 0 if the block stopped
+    // before y, -1 when the (bounded) wait gives up
+    auto wait_done = [&](int y) -> int {
+      const int slot = y % NSLOT;
       int it = 0;
       while (true) {
         int d = wg_load(&sm.done[slot][0]);
 #pragma unroll
         for (int w = 1; w < NCW; ++w) d = min(d, wg_load(&sm.done[slot][w]));
-        if (d >= lc) return true;
+        if (d >= y) return 1;
+        if (may_stop) {
+          const int n = n_run();
+          if (n >= 0 && y >= n) return 0;
+        }
         if (++it > SPIN_LIMIT) {
           if (L == 0) atomicOr(&t.counters[CNT_FLAGS], 0x100);
-          return false;
+          return -1;
         }
         __builtin_amdgcn_s_sleep(1);
       }
@@ -546,30 +581,39 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
           *reinterpret_cast<u32x4*>(o + 8 * i) = *reinterpret_cast<const u32x4*>(&sl.vo[tok][32 * (L & 3) + 8 * i]);
       }
     };
-    auto run = [&](int lc) -> bool {
-      const int slot = lc % NSLOT;
-      if (lc >= NSLOT) {  // the slot's previous chunk must be consumed (and its output written out)
-        if (!wait_done(lc - NSLOT)) return false;
-        if (ROLE == RECUR) flush(lc - NSLOT);
-      }
-      produce(sm, sm.slot[slot], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, ROLE == RECUR, L, g, c);
-      wg_store(&sm.ready[slot], lc);
-      return true;
-    };
+    // Producer pw takes chunks lc = pw, pw + NPW, ...: before preparing chunk
+    // lc it waits until the slot's previous chunk lc - NSLOT is consumed and
+    // writes that chunk's output rows; past the last chunk it goes on only to
+    // write out the outputs of the last NSLOT chunks.
     if (pw < nch) load_prod(in, addr(pw));
-    bool ok_run = true;
-    for (int lc = pw; lc < nch; lc += NPW)
-      if (!run(lc)) {
-        ok_run = false;
-        break;
+    for (int lc = pw; lc < nch + NSLOT; lc += NPW) {
+      const int y = lc - NSLOT;
+      if (y >= 0) {
+        if (wait_done(y) <= 0) break;
+        if (y >= o_from) flush(y);
       }
-    // the last NSLOT chunks' outputs: chunk lc goes to the producer that would
-    // have produced chunk lc + NSLOT
-    if (ROLE == RECUR && ok_run) {
-      for (int lc = max(0, nch - NSLOT); lc < nch; ++lc) {
-        if ((lc + NSLOT) % NPW != pw) continue;
-        if (!wait_done(lc)) break;
-        flush(lc);
+      if (lc < nch) {
+        // chunks past the checkpoint wait for the vote (the block usually stops
+        // there, and a chunk prepared meanwhile would slow the consumers)
+        int n = n_run();
+        if (may_stop && lc >= K) {
+          int it = 0;
+          while (n < 0) {
+            if (++it > SPIN_LIMIT) {
+              if (L == 0) atomicOr(&t.counters[CNT_FLAGS], 0x100);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            n = n_run();
+          }
+          if (n < 0) break;
+        }
+        if (n >= 0 && lc >= n) continue;  // stopped before this chunk
+        if (ROLE == RECUR || lc >= o_from)
+          produce(sm, sm.slot[lc % NSLOT], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, true, L, g, c);
+        else
+          produce(sm, sm.slot[lc % NSLOT], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, false, L, g, c);
+        wg_store(&sm.ready[lc % NSLOT], lc);
       }
     }
     return;
@@ -590,7 +634,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     return __hip_atomic_load(&sm.ready[lc % NSLOT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
   auto wait_ready = [&](int slot, int lc) -> bool {
-    if (ROLE == RECUR && seen == lc) return true;  // seen by the early read
+    if (seen == lc) return true;  // seen by the early read
     int it = 0;
     while (wg_load(&sm.ready[slot]) != lc) {
       if (++it > SPIN_LIMIT) {
@@ -601,7 +645,65 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     }
     return true;
   };
+  using NoOut = std::integral_constant<bool, false>;
+  using WithOut = std::integral_constant<bool, true>;
 
+  // One chunk applied to the state columns S; with the output (WithOut):
+  //   O^T = S^T Qbar^T + U^T Aqk^T into the slot's V rows (this wavefront has
+  //   read its V columns), written out by a producer.
+  // The state update is the same instruction sequence with or without it.
+  auto step_s = [&](int lc, f32x4 (&S)[TPW][8], auto wo) -> bool {
+    constexpr bool WO = decltype(wo)::value;
+    const int slot = lc % NSLOT;
+    if (!wait_ready(slot, lc)) return false;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const Slot& sl = sm.slot[slot];
+    const int peek = peek_ready(lc + 1);
+    u32x4 kb[4], qb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kb[s] = sl.kbf[s][L];
+      if (WO) qb[s] = sl.qbf[s][L];
+    }
+    const u32x4 tf = sl.tf[L];
+    const int m = chunk_m(lc);
+    u32x2 v[TPW];
+    u32x2 Sb[TPW][8];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+      v[jj] = slot_v(sl, m, g, col0 + 16 * jj + c);
+      pack_tile(S[jj], Sb[jj]);
+    }
+    // Y = Kbar S and O^T: independent MFMA chains
+    f32x4 Y[TPW], Ot[TPW];
+    tiles_y<TPW>(Sb, kb, Y);
+    if constexpr (WO) {
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(cat(Sb[jj][2 * s], Sb[jj][2 * s + 1]), qb[s], Ot[jj]);
+    }
+    UOps u[TPW];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) u[jj] = tile_u(Y[jj], tf, &v[jj]);
+    if constexpr (WO) {
+      const u32x4 aqa = sl.aqa[L], aqb = sl.aqb[L];
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqa, Ot[jj]);
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqb, Ot[jj]);
+      // O^T tile: token c, columns col0 + 16jj + 4g..+3
+      Slot& slw = sm.slot[slot];
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot[jj]);
+    }
+    tiles_update<TPW>(S, u, sl, g, c);
+    wg_store(&sm.done[slot][cw], lc);
+    seen = __builtin_amdgcn_readfirstlane(peek);
+    return true;
+  };
 
   if (ROLE == RECUR) {
     f32x4 S[TPW][8];
@@ -609,67 +711,50 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       const bool from_seg = (phase == 1);
       // start state of segment j >= 1: the merged S_j, or R_{j-1} itself when the
       // previous middle segment's M is all zero (the merge then writes nothing)
-      const float* seg_start = segS + seg_base;
+      const float* seg_start = sg.S + seg_base;
       if (from_seg && j >= 2) {
-        const int32_t* nzf = segMnz + ((long long)(sidx - 1) * H + h) * (D / 16);
+        const int32_t* nzf = sg.mnz + ((long long)(sidx - 1) * H + h) * (D / 16);
         int nz = 0;
 #pragma unroll
         for (int b = 0; b < D / 16; ++b) nz |= nzf[b];
-        if (nz == 0) seg_start = segR + seg_base - (long long)H * D * D;
+        if (nz == 0) seg_start = sg.R + seg_base - (long long)H * D * D;
       }
       load_state<TPW>(S, from_seg ? (const void*)seg_start : p.init_state, from_seg || p.state_fp32,
                       from_seg ? 0 : state_base, col0, g, c);
     }
-    auto step = [&](int lc) -> bool {
-      const int slot = lc % NSLOT;
-      if (!wait_ready(slot, lc)) return false;
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const Slot& sl = sm.slot[slot];
-      const int peek = peek_ready(lc + 1);
-      u32x4 kb[4], qb[4];
+    int lc = 0;
+    bool ok = true;
+    const int lim = may_stop ? K : nch;
+    // the checkpoint is loaded first: its latency hides behind the first chunks
+    f32x4 Ck[TPW][8];
+    if (may_stop) load_state<TPW>(Ck, sg.chk, true, seg_base, col0, g, c);
+    for (; ok && lc < lim; ++lc) ok = step_s(lc, S, WithOut{});
+    bool stopped = false;
+    if (ok && may_stop) {
+      uint32_t diff = 0;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        kb[s] = sl.kbf[s][L];
-        qb[s] = sl.qbf[s][L];
+      for (int jj = 0; jj < TPW; ++jj)
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) diff |= __float_as_uint(S[jj][tt][i]) ^ __float_as_uint(Ck[jj][tt][i]);
+      const bool same = __builtin_amdgcn_ballot_w64(diff != 0u) == 0;
+      if (L == 0) atomicAdd(&sm.vote, same ? 1 : 0x100);
+      int it = 0, v;
+      while (true) {
+        v = wg_load(&sm.vote);
+        if ((v & 0xFF) + (v >> 8) == NCW) break;
+        if (++it > SPIN_LIMIT) {
+          if (L == 0) atomicOr(&t.counters[CNT_FLAGS], 0x200);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      const u32x4 tf = sl.tf[L];
-      const int m = chunk_m(lc);
-      u32x2 v[TPW];
-      u32x2 Sb[TPW][8];
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) {
-        v[jj] = slot_v(sl, m, g, col0 + 16 * jj + c);
-        pack_tile(S[jj], Sb[jj]);
-      }
-      // O^T = S^T Qbar^T + U^T Aqk^T, Y = Kbar S: independent MFMA chains
-      f32x4 Y[TPW], Ot[TPW];
-      tiles_y<TPW>(Sb, kb, Y);
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(cat(Sb[jj][2 * s], Sb[jj][2 * s + 1]), qb[s], Ot[jj]);
-      UOps u[TPW];
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) u[jj] = tile_u(Y[jj], tf, &v[jj]);
-      const u32x4 aqa = sl.aqa[L], aqb = sl.aqb[L];
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqa, Ot[jj]);
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqb, Ot[jj]);
-      // O^T tile: token c, columns col0 + 16jj + 4g..+3, into the slot's V rows
-      // (this wavefront has read its V columns); written out by a producer
-      Slot& slw = sm.slot[slot];
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot[jj]);
-      tiles_update<TPW>(S, u, sl, g, c);
-      wg_store(&sm.done[slot][cw], lc);
-      seen = __builtin_amdgcn_readfirstlane(peek);
-      return true;
-    };
-    for (int lc = 0; lc < nch; ++lc)
-      if (!step(lc)) break;
+      stopped = ok && v == NCW;
+      if (stopped && cw == 0 && L == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
+      for (; ok && !stopped && lc < nch; ++lc) ok = step_s(lc, S, WithOut{});
+    }
     float* dst32 = nullptr;
     uint16_t* dst16 = nullptr;
     long long base = 0;
@@ -680,16 +765,21 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
           dst32 = static_cast<float*>(p.final_state);
         else
           dst16 = static_cast<uint16_t*>(p.final_state);
+        // stopped: the end state is the first pass's R of this segment
+        if (stopped) load_state<TPW>(S, sg.R, true, seg_base, col0, g, c);
       }
-    } else {
-      dst32 = segS;  // start state of the next segment of this sequence (slot sidx + 1)
+    } else if (phase == 0) {
+      // segment 0's end state is S_1, the merge's starting point (slot sidx + 1).
+      // The second pass stores nothing here: the next segment's start state
+      // was already merged, and that block may be reading it in this launch.
+      dst32 = sg.S;
       base = seg_base + (long long)H * D * D;
     }
     store_state<TPW>(S, dst32, dst16, base, col0, g, c);
   } else {
-    // pre-scan on the same columns: X[0..TPW) = R (start 0, with Ut), X[TPW..2TPW) = M (start I, Ut = 0).
-    // A column of M evolves on its own (U = -T' Kbar M needs only that
-    // column), and a column that is exactly zero stays zero (every product
+    // first pass on the same columns: R (start 0, with Ut) and M (start I,
+    // Ut = 0).  A column of M evolves on its own (U = -T' Kbar M needs only
+    // that column), and a column that is exactly zero stays zero (every product
     // with it is zero and gamma_C is finite).  Once this wavefront's columns
     // of M have underflowed to zero they are no longer computed or stored.
     f32x4 Rs[TPW][8], Ms[TPW][8];
@@ -704,8 +794,9 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         for (int i = 0; i < 4; ++i) x[i] = (16 * tt + 4 * g + i == col0 + 16 * jj + c) ? 1.f : 0.f;
         Ms[jj][tt] = x;
       }
-    // both R and M, until this wavefront's columns of M are zero
-    auto step_rm = [&](int lc) -> bool {
+    // R and M, with R's output when wo is set (R updated as step_s does)
+    auto step_rm = [&](int lc, auto wo) -> bool {
+      constexpr bool WO = decltype(wo)::value;
       const int slot = lc % NSLOT;
       if (!wait_ready(slot, lc)) return false;
       const Slot& sl = sm.slot[slot];
@@ -725,6 +816,15 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         tiles_y<2>(Sb, kb, Y);
         ur[jj] = tile_u(Y[0], tf, &v);
         um[jj] = tile_u(Y[1], tf, nullptr);
+        if constexpr (WO) {
+          f32x4 Ot = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) Ot = mfma_k32(cat(Sb[0][2 * s], Sb[0][2 * s + 1]), sl.qbf[s][L], Ot);
+          Ot = mfma_k32(ur[jj].ua, sl.aqa[L], Ot);
+          Ot = mfma_k32(ur[jj].ua, sl.aqb[L], Ot);
+          Slot& slw = sm.slot[slot];
+          *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       const uint32_t bits = tiles_update2<TPW>(Rs, ur, Ms, um, sl, g, c);
@@ -732,78 +832,52 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       mzero = __builtin_amdgcn_ballot_w64((bits & 0x7FFFFFFFu) != 0u) == 0;
       return true;
     };
-    // R alone
-    auto step_r = [&](int lc) -> bool {
-      const int slot = lc % NSLOT;
-      if (!wait_ready(slot, lc)) return false;
-      const Slot& sl = sm.slot[slot];
-      u32x4 kb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
-      const u32x4 tf = sl.tf[L];
-      const int m = chunk_m(lc);
-      u32x2 Sb[TPW][8];
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) pack_tile(Rs[jj], Sb[jj]);
-      f32x4 Y[TPW];
-      tiles_y<TPW>(Sb, kb, Y);
-      UOps ur[TPW];
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) {
-        const u32x2 v = slot_v(sl, m, g, col0 + 16 * jj + c);
-        ur[jj] = tile_u(Y[jj], tf, &v);
-      }
-      tiles_update<TPW>(Rs, ur, sl, g, c);
-      wg_store(&sm.done[slot][cw], lc);
-      return true;
-    };
     int lc = 0;
-    bool ok_run = true;
-    for (; lc < nch && !mzero; ++lc)
-      if (!step_rm(lc)) {
-        ok_run = false;
-        break;
-      }
-    for (; ok_run && lc < nch; ++lc)
-      if (!step_r(lc)) break;
-    store_state<TPW>(Rs, segR, nullptr, seg_base, col0, g, c);
-    if (!mzero) store_state<TPW>(Ms, segM, nullptr, seg_base, col0, g, c);
-    if (L == 0) {
+    bool ok = true;
+    const int k1 = min(nch, o_from);
+    for (; ok && lc < k1 && !mzero; ++lc) ok = step_rm(lc, NoOut{});
+    for (; ok && lc < k1; ++lc) ok = step_s(lc, Rs, NoOut{});
+    if (ok && has_chk) store_state<TPW>(Rs, sg.chk, nullptr, seg_base, col0, g, c);
+    for (; ok && lc < nch && !mzero; ++lc) ok = step_rm(lc, WithOut{});
+    for (; ok && lc < nch; ++lc) ok = step_s(lc, Rs, WithOut{});
+    store_state<TPW>(Rs, sg.R, nullptr, seg_base, col0, g, c);
+    if (j < ns - 1) {  // the merge reads the transitions of middle segments
+      if (!mzero) store_state<TPW>(Ms, sg.M, nullptr, seg_base, col0, g, c);
+      if (L == 0) {
 #pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) segMnz[((long long)sidx * H + h) * (D / 16) + col0 / 16 + jj] = mzero ? 0 : 1;
+        for (int jj = 0; jj < TPW; ++jj) sg.mnz[((long long)sidx * H + h) * (D / 16) + col0 / 16 + jj] = mzero ? 0 : 1;
+      }
     }
   }
 }
 
-// MODE 0: recurrence of the segments the phase selects (one block per segment).
-// MODE 1: first pass of a segmented call, blocks [0, n) pre-scan the middle
-// segments and blocks [n, 2n) run the recurrence over the first segments.
+// One block per (segment, head) unit, numbered u = segment * H + head, so the
+// units that exist (the segment count is known only on the device) take the
+// first blocks and the rest exit at once: blocks are dealt to the XCDs in
+// turn, and this keeps their shares of the work equal.
+// MODE 0: the recurrence of the segments the phase selects.
+// MODE 1: first pass of a segmented call: segment 0 of each sequence from the
+// initial state, the others from a zero state.
 template <int MODE>
-__global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, float* __restrict__ segM,
-                                                             float* __restrict__ segR, float* __restrict__ segS,
-                                                             int32_t* __restrict__ segMnz, int phase) {
+__global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, Seg sg, int phase) {
   __shared__ Smem sm;
-  if (MODE == 0) {
-    chunk_body<RECUR>(sm, p, t, segM, segR, segS, segMnz, phase, blockIdx.x, blockIdx.y);
-  } else {
-    const int half = gridDim.x / 2;
-    if ((int)blockIdx.x < half)
-      chunk_body<PRE>(sm, p, t, segM, segR, segS, segMnz, 0, blockIdx.x, blockIdx.y);
-    else
-      chunk_body<RECUR>(sm, p, t, segM, segR, segS, segMnz, 0, blockIdx.x - half, blockIdx.y);
-  }
+  const int sidx = (int)blockIdx.x / p.H;
+  const int h = (int)blockIdx.x - sidx * p.H;
+  if (sidx >= t.counters[CNT_N_SEGS]) return;
+  if (MODE == 0 || t.seg_tab[4 * sidx + 3] == 0)
+    chunk_body<RECUR>(sm, p, t, sg, phase, sidx, h);
+  else
+    chunk_body<PRE>(sm, p, t, sg, 0, sidx, h);
 }
 
-hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, float* segS, int32_t* segMnz,
-                         int64_t max_segs, int phase, bool segmented, hipStream_t st) {
+hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
+                         hipStream_t st) {
   if (max_segs <= 0) return hipSuccess;
-  if (phase == 0 && segmented) {
-    hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3((unsigned)(2 * max_segs), (unsigned)p.H), dim3(NTHREADS), 0, st, p, t,
-                       segM, segR, segS, segMnz, 0);
-  } else {
-    hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3((unsigned)max_segs, (unsigned)p.H), dim3(NTHREADS), 0, st, p, t, segM,
-                       segR, segS, segMnz, phase);
-  }
+  const unsigned blocks = (unsigned)(max_segs * p.H);
+  if (phase == 0 && segmented)
+    hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg, 0);
+  else
+    hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg, phase);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ constexpr int C = KDA_CHUNK;     // 16 tokens per chunk
 constexpr int CNT_N_CHUNKS = 0;
 constexpr int CNT_N_SEGS = 1;
 constexpr int CNT_FLAGS = 2;
+constexpr int CNT_EARLY_STOPS = 3;  // (segment, head) pairs whose second pass stopped at the checkpoint
 
 // Pointers into a carved workspace (device addresses).
 struct Tables {
@@ -55,16 +56,28 @@ struct Problem {
   int64_t total_tokens;
 };
 
+// Segment buffers of a segmented call (all null when serial), [segment][head][v][k] fp32:
+//   M, R : transition and zero-start state of segments >= 1 (first pass);
+//   S    : merged state entering a segment;
+//   chk  : R after the first chk_chunks chunks of segments >= 1 (first pass);
+//   mnz  : per (segment, head, 16-column block of M) 1 if nonzero, 0 if exactly zero.
+struct Seg {
+  float* M;
+  float* R;
+  float* S;
+  float* chk;
+  int32_t* mnz;
+  int chk_chunks;
+};
+
 // ---- launchers (host functions defined next to their kernels) ----
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
-// producer/consumer chunk kernel: prep + recurrence / pre-scan in one launch per phase
-// segMnz: per (segment, head, 16-column block) flag, 0 when that block of the
-// segment's transition M underflowed to exactly zero (written by the pre-scan)
-hipError_t launch_chunks(const Problem& p, Tables t, float* segM, float* segR, float* segS, int32_t* segMnz,
-                         int64_t max_segs, int phase, bool segmented, hipStream_t st);
-hipError_t launch_merge(const Problem& p, Tables t, const float* segM, const float* segR, float* segS,
-                        const int32_t* segMnz, hipStream_t st);
+// producer/consumer chunk kernel: one launch per pass (phase 0: every segment,
+// phase 1: the start of segments >= 1 from their merged states)
+hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
+                         hipStream_t st);
+hipError_t launch_merge(const Problem& p, Tables t, const Seg& sg, hipStream_t st);
 
 }  // namespace kda
 

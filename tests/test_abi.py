@@ -52,6 +52,9 @@ def test_plan_modes():
     assert kda.plan_seg_chunks(8 * 8192, 32, 8, "auto") == 0  # 256 chains fill the chip
     assert kda.plan_seg_chunks(1023, 16, 1, "auto") == 0  # too short to split
     assert kda.plan_seg_chunks(65536, 16, 1, "auto", 64) == 64
+    # about one (segment, head) unit per CU: ceil(chunks * heads / 256) chunks per segment
+    assert kda.plan_seg_chunks(65536, 16, 1, "auto") == 256
+    assert kda.plan_seg_chunks(2 * 4096, 16, 2, "auto") == 32
     assert kda.plan_seg_chunks(65536, 16, 1, "off", 64) == 0
     with pytest.raises(kda.KdaError):
         kda.plan_seg_chunks(100, 0, 1)
@@ -63,7 +66,7 @@ def test_workspace_layout_consistent():
         off = kda.workspace_offsets(*args)
         assert off["total"] == size
         prev = -1
-        for name in kda.WS_FIELDS[:11]:
+        for name in kda.WS_FIELDS[:12]:
             assert off[name] % kda.WS_ALIGN == 0
             assert off[name] >= prev
             prev = off[name]
@@ -74,11 +77,12 @@ def test_workspace_layout_consistent():
         assert off["seg_m"] - off["seg_tab"] >= 16 * off["max_segs"]
         mat = off["max_segs"] * H * 128 * 128 * 4
         if seg == 0:
-            assert off["seg_s"] == off["seg_r"] == off["seg_m"] == off["seg_mnz"] == off["total"]
+            assert off["seg_s"] == off["seg_r"] == off["seg_m"] == off["seg_mnz"] == off["seg_chk"] == off["total"]
         else:
             assert off["seg_r"] - off["seg_m"] >= mat and off["seg_s"] - off["seg_r"] >= mat
             assert off["seg_mnz"] - off["seg_s"] >= mat
-            assert off["total"] - off["seg_mnz"] >= off["max_segs"] * H * 8 * 4
+            assert off["seg_chk"] - off["seg_mnz"] >= off["max_segs"] * H * 8 * 4
+            assert off["total"] - off["seg_chk"] >= mat
 
 
 def _call(lib, **kw):

@@ -72,6 +72,32 @@ def test_segment_path_slow_decay():
     _case(w, cp_mode="force", seg_chunks=4)
 
 
+def _early_stops(w, ws, cp_mode, seg_chunks):
+    """(segment, head) pairs whose second pass stopped at the checkpoint."""
+    import kimi_delta_attention_02_amd as kda
+
+    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, cp_mode, seg_chunks)
+    return int(read_ws(ws, offs, "counters", 4, np.int32)[3])
+
+
+@pytest.mark.parametrize("seg,lb", [(5, -5.0), (9, -1.0), (12, 0.0)])
+def test_segment_checkpoint(seg, lb):
+    """Segments longer than the 4-chunk checkpoint.  The first pass writes their
+    output from the zero-start state; the second pass redoes the first 4 chunks
+    from the true start state and stops there only if its state equals the
+    zero-start one bit for bit, else it runs to the segment's end.  Strong decay
+    (lb = -5) reaches that equality; no decay (lb = 0) never does.  Both are
+    checked against the oracle."""
+    w = kda_inputs.custom(seqlens=[300, 16, 90, 1, 257], H=2, lower_bound=lb, seed=28, name=f"segchk{seg}/{lb}")
+    x, d, out, final, ws = _case(w, cp_mode="force", seg_chunks=seg)
+    stops = _early_stops(w, ws, "force", seg)
+    say(f"{w.name}: early stops {stops}")
+    if lb == 0.0:
+        assert stops == 0
+    if lb == -5.0:
+        assert stops > 0
+
+
 def test_zero_tokens_with_final_state():
     w = kda_inputs.custom(seqlens=[0, 0], H=2, seed=26, name="empty")
     x = kda_inputs.make_inputs(w)
@@ -208,8 +234,10 @@ def test_config4_segmented_bit_identical_to_serial(name):
     check_against_oracle(w, x, out_s, fin_s, seqs=[0] if name == "cfg4a" else [0, 5], heads=[5],
                          final_dtype=w.state_dtype)
     for seg in (0, 64):
-        out_c, fin_c, _ = run_gpu(w, x, d, cp_mode="force", seg_chunks=seg)
+        out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="force", seg_chunks=seg)
         same_o = torch.equal(out_c.view(torch.int16), out_s.view(torch.int16))
         same_f = torch.equal(fin_c, fin_s)
-        say(f"{name} seg={seg}: out identical={same_o} final identical={same_f}")
+        stops = _early_stops(w, ws, "force", seg)
+        say(f"{name} seg={seg}: out identical={same_o} final identical={same_f} early stops={stops}")
         assert same_o and same_f
+        assert stops > 0  # the checkpoint path is the one measured at this size
