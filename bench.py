@@ -11,8 +11,10 @@ line.
 
 Per-stage kernel time comes from the library's own event hook
 (kda_profile_enable / kda_profile_collect, HIP events on the library's
-stream) over the same timed region; the roofline object is computed for the
-chunk kernel (chunk prep + recurrence), summed over its launches in a step.
+stream) over a second run of K steps: its events sit between the kernels of
+a step and lengthen it, so the step time comes from the first, uninstrumented
+run.  The roofline object is computed for the chunk kernel (chunk prep +
+recurrence), summed over its launches in a step.
 
 The CPU baseline times the fp64 oracle (unchanged) on a bounded sample of the
 same workload: whole sequences taken in order, all heads, one head per worker
@@ -189,12 +191,20 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    # Timed region 1: the K steps as a caller runs them (events only around
+    # whole steps).  Timed region 2: the same K steps again with the library's
+    # per-stage events on, for the stage split and the chunk kernel's own
+    # duration (the roofline); those events sit between the kernels of a step
+    # and lengthen it, so region 2 does not feed ms_per_step.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    kda.profile_enable(True)
     evs[0].record(stream)
     for i in range(a.steps):
         step()
         evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    kda.profile_enable(True)
+    for i in range(a.steps):
+        step()
     torch.cuda.synchronize()
     kda.profile_enable(False)
     stages = kda.profile_collect()
