@@ -68,18 +68,21 @@ constexpr float LOG2E = 1.4426950408889634f;
 struct Slot {
   u32x4 kbf[4][64];   // Kbar bf16, A operand of Kbar S: k-step s, lane (g, c) = token c
   u32x4 qbf[4][64];   // Qbar bf16, B operand of S^T Qbar^T, same arrangement
-  u32x4 ktp[D][4];    // [channel][g]: Ktil high part of tokens 4g..4g+3, then the low part
+  u32x4 ktp[D][4];    // [channel][(g + channel/2) % 4]: Ktil high part of tokens 4g..4g+3, then the
+                      // low part (the rotation spreads a column read over all LDS banks)
   float gC[D];        // gamma_C per key channel
   u32x4 tf[64];       // [T'_hi | T'_lo] of row c, columns 4g..4g+3
   u32x4 aqa[64];      // [Aqk_hi | Aqk_hi] of row c, columns 4g..4g+3
   u32x4 aqb[64];      // [Aqk_lo | 0]
-  uint16_t vo[C][D];  // V rows of the chunk (producer), overwritten column slice by column slice
-                      // with O by the consumer owning those columns; written out whole rows
+  uint16_t vo[C][D + 8];  // V rows of the chunk (producer), overwritten column slice by column slice
+                          // with O by the consumer owning those columns; written out whole rows
+                          // (16 bytes of padding per row move consecutive rows to other banks)
 };
 
 struct Smem {
   Slot slot[NSLOT];
-  float Aq[4][C][16];   // per producer: A rows arranged for the quad-parallel solve
+  float Aq[4][C][20];   // per producer: A rows arranged for the quad-parallel solve (pitch 20:
+                        // the two halves of a wavefront write to different banks)
   float Tp[4][C * MP];  // per producer: T'
   float bt[4][C];       // per producer: beta of the chunk's tokens
   float adt[D];         // log2(e) exp(A_log) dt_bias of the head
@@ -233,7 +236,10 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
 
   // A_raw = Kbar Ktil^T from bf16 operands (one MFMA per k-step), Aqk^T =
   // Ktil Qbar^T from bf16 high/low operands (hi.hi + hi.lo + lo.hi)
-  uint16_t* ktp16 = reinterpret_cast<uint16_t*>(&sl.ktp[0][0]) + 8 * (c >> 2) + (c & 3);
+  // Ktil of token c, channel ch goes to ktp[ch][(c/4 + ch/2) % 4], element c % 4 (high part)
+  // or 4 + c % 4 (low part); ch/2 % 4 = (2g + i % 2) % 4 for the channels this lane holds
+  uint16_t* ktp16 = reinterpret_cast<uint16_t*>(&sl.ktp[0][0]) + (c & 3);
+  const int kpos0 = 8 * (((c >> 2) + 2 * g) & 3), kpos1 = 8 * (((c >> 2) + 2 * g + 1) & 3);
   f32x4 Araw = zero4(), AqkT = zero4();
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -268,13 +274,14 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
       kbh[i] = pack2(Kb[0], Kb[1]);
       split_pair(Kt[0], Kt[1], kth[i], ktl[i]);
       if (want_q) split_pair(Qb[0], Qb[1], qbh[i], qbl[i]);
-      // Ktil, channel-major: ktp[ch][c/4] holds tokens 4(c/4)..+3, high parts
-      // then low parts
+      // Ktil, channel-major: ktp[ch][(c/4 + ch/2) % 4] holds tokens 4(c/4)..+3,
+      // high parts then low parts
       const int ch = 32 * s + 16 * (i >> 1) + 4 * g + 2 * (i & 1);
-      ktp16[32 * ch] = (uint16_t)(kth[i] & 0xFFFFu);
-      ktp16[32 * (ch + 1)] = (uint16_t)(kth[i] >> 16);
-      ktp16[32 * ch + 4] = (uint16_t)(ktl[i] & 0xFFFFu);
-      ktp16[32 * (ch + 1) + 4] = (uint16_t)(ktl[i] >> 16);
+      const int kp = (i & 1) ? kpos1 : kpos0;
+      ktp16[32 * ch + kp] = (uint16_t)(kth[i] & 0xFFFFu);
+      ktp16[32 * (ch + 1) + kp] = (uint16_t)(kth[i] >> 16);
+      ktp16[32 * ch + kp + 4] = (uint16_t)(ktl[i] & 0xFFFFu);
+      ktp16[32 * (ch + 1) + kp + 4] = (uint16_t)(ktl[i] >> 16);
     }
     const u32x4 kbh4 = {kbh[0], kbh[1], kbh[2], kbh[3]};
     const u32x4 kth4 = {kth[0], kth[1], kth[2], kth[3]}, ktl4 = {ktl[0], ktl[1], ktl[2], ktl[3]};
@@ -394,7 +401,7 @@ template <int NT>
 __device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const UOps (&u)[NT], const Slot& sl, int g, int c) {
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    const u32x4 kp = sl.ktp[16 * tt + c][g];
+    const u32x4 kp = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
     const f32x4 gc = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
 #pragma unroll
     for (int jj = 0; jj < NT; ++jj) {
@@ -412,7 +419,7 @@ __device__ __forceinline__ uint32_t tiles_update2(f32x4 (&S1)[NT][8], const UOps
   uint32_t bits = 0;
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    const u32x4 kp = sl.ktp[16 * tt + c][g];
+    const u32x4 kp = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
     const f32x4 gc = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
 #pragma unroll
     for (int jj = 0; jj < NT; ++jj) {
