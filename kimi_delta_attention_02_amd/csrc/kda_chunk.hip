@@ -108,6 +108,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The chunks a second-pass block runs, from the checkpoint vote word v (+1 per
+// consumer whose state matched, +0x100 per one that did not): k once all
+// consumers matched, nch once any did not, -1 while votes are missing.
+// (A function of values: a lambda selecting between captured variables makes
+// the compiler keep its closure in scratch memory.)
+__device__ __forceinline__ int vote_chunks(int v, int k, int nch) {
+  if ((v & 0xFF) + (v >> 8) < NCW) return -1;
+  return v == NCW ? k : nch;
+}
+
 // flag reads are made wavefront-uniform so that every wait loop is a scalar loop
 __device__ __forceinline__ int wg_load(int* p) {
   return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
@@ -135,13 +145,6 @@ __device__ __forceinline__ void unpack4(u32x2 v, float* f) {
   f[1] = __uint_as_float(v.x & 0xFFFF0000u);
   f[2] = __uint_as_float(v.y << 16);
   f[3] = __uint_as_float(v.y & 0xFFFF0000u);
-}
-
-// x0 = h0 + l0, x1 = h1 + l1 with h = bf16(x) (round to nearest even) and
-// l = bf16(x - h): hi = (h0, h1), lo = (l0, l1) as packed bf16 pairs
-__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  hi = pack2(x0, x1);
-  lo = pack2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
 }
 
 // Where one chunk's producer inputs are: wavefront-uniform bases (chunk start,
@@ -187,11 +190,12 @@ __device__ __forceinline__ void load_prod(ProdIn& in, const InAddr& a) {
   load_vrows(in, a);
 }
 
-// V[4g+0..3][col] of a chunk from its slot, rows past the chunk end as zero
-__device__ __forceinline__ u32x2 slot_v(const Slot& sl, int m, int g, int col) {
+// V[4g+0..3][col] of a chunk from its slot (the producer stored rows past the
+// chunk end as zeros)
+__device__ __forceinline__ u32x2 slot_v(const Slot& sl, int g, int col) {
   uint32_t t[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t[i] = (4 * g + i < m) ? (uint32_t)sl.vo[4 * g + i][col] : 0u;
+  for (int i = 0; i < 4; ++i) t[i] = sl.vo[4 * g + i][col];
   return u32x2{t[0] | (t[1] << 16), t[2] | (t[3] << 16)};
 }
 
@@ -207,10 +211,17 @@ __device__ __forceinline__ float pick4(f32x4 v, int i) { return i == 0 ? v[0] : 
 __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, const InAddr& next,
                                         const Problem& p, int m, float a2, bool want_q, int L, int g, int c) {
   const bool ok = c < m;
-  {  // V rows into the slot, then the next chunk's V into the same registers
+  {  // V rows into the slot (rows past the chunk end as zeros), then the next
+     // chunk's V into the same registers
     const int L = threadIdx.x & 63;
+    if (m == C) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sl.vo[L >> 2][32 * (L & 3) + 8 * i]) = in.v[i];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sl.vo[L >> 2][32 * (L & 3) + 8 * i]) = in.v[i];
+    } else {
+      const uint32_t keep = (L >> 2) < m ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sl.vo[L >> 2][32 * (L & 3) + 8 * i]) = in.v[i] & keep;
+    }
     load_vrows(in, next);
   }
   // |q_c|^2, |k_c|^2: diagonals of the Gram matrices q q^T, k k^T from bf16 MFMAs
@@ -549,12 +560,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     };
     // chunks the block runs: nch, or K once the consumers agreed to stop
     // there; -1 while their vote is incomplete
-    auto n_run = [&sm, may_stop, K, nch]() -> int {
-      if (!may_stop) return nch;
-      const int v = wg_load(&sm.vote);
-      if ((v & 0xFF) + (v >> 8) < NCW) return -1;
-      return v == NCW ? K : nch;
-    };
+    auto n_run = [&]() -> int { return may_stop ? vote_chunks(wg_load(&sm.vote), K, nch) : nch; };
     // 1 once every consumer is done with chunk y, 0 if the block stopped
     // before y, -1 when the (bounded) wait gives up
     auto wait_done = [&](int y) -> int {
@@ -673,12 +679,11 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       if (WO) qb[s] = sl.qbf[s][L];
     }
     const u32x4 tf = sl.tf[L];
-    const int m = chunk_m(lc);
     u32x2 v[TPW];
     u32x2 Sb[TPW][8];
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) {
-      v[jj] = slot_v(sl, m, g, col0 + 16 * jj + c);
+      v[jj] = slot_v(sl, g, col0 + 16 * jj + c);
       pack_tile(S[jj], Sb[jj]);
     }
     // Y = Kbar S and O^T: independent MFMA chains
@@ -811,11 +816,10 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 #pragma unroll
       for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
       const u32x4 tf = sl.tf[L];
-      const int m = chunk_m(lc);
       UOps ur[TPW], um[TPW];
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj) {  // one R and one M tile at a time: bounded live range
-        const u32x2 v = slot_v(sl, m, g, col0 + 16 * jj + c);
+        const u32x2 v = slot_v(sl, g, col0 + 16 * jj + c);
         u32x2 Sb[2][8];
         pack_tile(Rs[jj], Sb[0]);
         pack_tile(Ms[jj], Sb[1]);

@@ -107,18 +107,21 @@ __device__ __forceinline__ u32x2 pack4(f32x4 x) {
   return r;
 }
 
-// x = hi + lo + O(2^-16 |x|): hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ float hi_part(float x) { return __uint_as_float(pack2(x, 0.f) << 16); }
+// x0 = h0 + l0, x1 = h1 + l1 with h = bf16(x) (round to nearest even) and
+// l = bf16(x - h), so x = h + l + O(2^-16 |x|): hi = (h0, h1), lo = (l0, l1) as
+// packed bf16 pairs.  One rounding per pair for h, whose fp32 values are read
+// back from the packed word.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack2(x0, x1);
+  lo = pack2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
+}
 
 __device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo) {
-  f32x4 h, l;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = hi_part(x[i]);
-    l[i] = x[i] - h[i];
-  }
-  hi = pack4(h);
-  lo = pack4(l);
+  uint32_t h0, l0, h1, l1;
+  split_pair(x[0], x[1], h0, l0);
+  split_pair(x[2], x[3], h1, l1);
+  hi = u32x2{h0, h1};
+  lo = u32x2{l0, l1};
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
