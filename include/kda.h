@@ -132,6 +132,12 @@ typedef enum {
                                entries are then not stored) (CP only) */
   KDA_WS_SEG_CHK,           /* fp32 [max_segs][H][128][128] zero-start state R^T of a segment >= 1 after
                                its first 4 chunks (segments longer than that; CP only) */
+  KDA_WS_SEQ_FULL_OFF,      /* int32[N+1]   prefix sums of the full-length segments per sequence
+                               (floor(chunks/seg); 1 per sequence when serial) */
+  KDA_WS_UNIT_TAB,          /* int32[max_segs][8] the segments in dispatch order: (segment, sequence,
+                               chunk begin, chunk end, segment in sequence, -1, -1, -1); every
+                               full-length segment first, then the shorter last segments, each group
+                               in segment order (-1 past the live count) */
   KDA_WS_MAX_CHUNKS,        /* (count, not an offset) chunk-table capacity */
   KDA_WS_MAX_SEGS,          /* (count, not an offset) segment-table capacity */
   KDA_WS_TOTAL,             /* total bytes (= kda_get_workspace_size) */

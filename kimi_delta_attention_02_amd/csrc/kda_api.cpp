@@ -152,6 +152,8 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
   take(KDA_WS_SEG_S, seg_bytes);
   take(KDA_WS_SEG_MNZ, seg > 0 ? ms * H * (kda::D / 16) * 4 : 0);
   take(KDA_WS_SEG_CHK, seg_bytes);
+  take(KDA_WS_SEQ_FULL_OFF, 4 * ((int64_t)N + 1));
+  take(KDA_WS_UNIT_TAB, 32 * ms);
   out->off[KDA_WS_MAX_CHUNKS] = mc;
   out->off[KDA_WS_MAX_SEGS] = ms;
   out->off[KDA_WS_TOTAL] = o;
@@ -240,6 +242,8 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   t.seq_seg_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_SEG_OFF]);
   t.chunk_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_CHUNK_TAB]);
   t.seg_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_TAB]);
+  t.seq_full_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_FULL_OFF]);
+  t.unit_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_UNIT_TAB]);
   const bool cp = lay.seg > 0;
   kda::Seg sg;
   sg.M = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;

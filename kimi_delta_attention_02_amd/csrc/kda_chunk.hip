@@ -499,11 +499,12 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[NT][8], float* dst3
 
 template <int ROLE>
 __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, const Seg& sg, int phase,
-                                           int sidx, int h) {
-  const int seq = t.seg_tab[4 * sidx + 0];
-  const int cb = t.seg_tab[4 * sidx + 1];
-  const int ce = t.seg_tab[4 * sidx + 2];
-  const int j = t.seg_tab[4 * sidx + 3];
+                                           const int32_t* urow, int h) {
+  const int sidx = urow[0];
+  const int seq = urow[1];
+  const int cb = urow[2];
+  const int ce = urow[3];
+  const int j = urow[4];
   const int ns = t.seq_seg_off[seq + 1] - t.seq_seg_off[seq];
   // RECUR, phase 0: segment 0 of every sequence from the initial state;
   // RECUR, phase 1: segments >= 1 from their merged start states;
@@ -862,23 +863,26 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   }
 }
 
-// One block per (segment, head) unit, numbered u = segment * H + head, so the
-// units that exist (the segment count is known only on the device) take the
-// first blocks and the rest exit at once: blocks are dealt to the XCDs in
-// turn, and this keeps their shares of the work equal.
+// One block per (segment, head) unit: block u runs head u % H of the
+// segment in row u / H of the dispatch table (full-length segments first,
+// so that the long units start first).  Units that exist (the segment count
+// is known only on the device) take the first blocks and the rest exit at
+// once: blocks are dealt to the XCDs in turn, and this keeps their shares of
+// the work equal.
 // MODE 0: the recurrence of the segments the phase selects.
 // MODE 1: first pass of a segmented call: segment 0 of each sequence from the
 // initial state, the others from a zero state.
 template <int MODE>
 __global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, Seg sg, int phase) {
   __shared__ Smem sm;
-  const int sidx = (int)blockIdx.x / p.H;
-  const int h = (int)blockIdx.x - sidx * p.H;
-  if (sidx >= t.counters[CNT_N_SEGS]) return;
-  if (MODE == 0 || t.seg_tab[4 * sidx + 3] == 0)
-    chunk_body<RECUR>(sm, p, t, sg, phase, sidx, h);
+  const int k = (int)blockIdx.x / p.H;
+  const int h = (int)blockIdx.x - k * p.H;
+  if (k >= t.counters[CNT_N_SEGS]) return;
+  const int32_t* urow = t.unit_tab + 8 * k;
+  if (MODE == 0 || urow[4] == 0)
+    chunk_body<RECUR>(sm, p, t, sg, phase, urow, h);
   else
-    chunk_body<PRE>(sm, p, t, sg, 0, sidx, h);
+    chunk_body<PRE>(sm, p, t, sg, 0, urow, h);
 }
 
 hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,

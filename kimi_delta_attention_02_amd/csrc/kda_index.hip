@@ -8,15 +8,22 @@
 // cuLA PR #106 commit list (CHUNK = 16, segment split) and review thread
 // (cu_seqlens and chunk_indices passed to the kernels).
 //
-// Two launches, both free of host synchronisation:
-//  1. kda_index_scan (one 1024-thread workgroup): clamps the offsets into a
-//     non-decreasing sequence within [0, total], then prefix-sums the chunk
-//     and segment counts.  Tables: seq_start[N+1], seq_len[N],
-//     seq_chunk_off[N+1], seq_seg_off[N+1], counters {n_chunks, n_segs, flags}.
-//  2. kda_index_fill: one thread per table row; binary search of the prefix
-//     sums gives chunk_tab[c] = (seq, chunk in seq) and
-//     seg_tab[s] = (seq, first chunk, end chunk, segment in seq).  Rows past
-//     the live counts are filled with -1.
+// Free of host synchronisation, in one of two forms:
+//  - up to FUSED_MAX_N sequences and FUSED_MAX_ROWS table rows: one launch of
+//    kda_index_fused (one 1024-thread workgroup) that does both steps below,
+//    the second from copies of the prefix sums in LDS;
+//  - otherwise two launches:
+//    1. kda_index_scan (one 1024-thread workgroup): clamps the offsets into a
+//       non-decreasing sequence within [0, total], then prefix-sums the chunk,
+//       segment and full-length segment counts.  Tables: seq_start[N+1],
+//       seq_len[N], seq_chunk_off[N+1], seq_seg_off[N+1], seq_full_off[N+1],
+//       counters {n_chunks, n_segs, flags, 0}.
+//    2. kda_index_fill: one thread per table row; binary search of the prefix
+//       sums gives chunk_tab[c] = (seq, chunk in seq) and
+//       seg_tab[s] = (seq, first chunk, end chunk, segment in seq), and puts
+//       segment s into the dispatch table unit_tab (full-length segments
+//       first, then the shorter last segments of their sequences, so that the
+//       long units start first).  Rows past the live counts are -1.
 #include "kda_internal.h"
 
 namespace kda {
@@ -25,6 +32,8 @@ namespace {
 
 constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_WAVES = SCAN_THREADS / 64;
+constexpr int FUSED_MAX_N = 4095;      // sequences the fused launch takes (LDS copies of the offsets)
+constexpr int FUSED_MAX_ROWS = 16384;  // table rows it fills (16 per thread at most)
 
 template <typename T, typename Op>
 __device__ T block_inclusive_scan(T x, Op op, T identity, T* smem, T* block_total) {
@@ -62,11 +71,14 @@ struct AddOp {
 
 }  // namespace
 
-__global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __restrict__ cu, int N, long long T_row,
-                                                               long long total, int seg_chunks, Tables t) {
-  __shared__ long long smem[SCAN_WAVES];
-  __shared__ int flags;
-  if (threadIdx.x == 0) flags = 0;
+// Clamped boundaries, lengths, chunk and segment prefix sums and the counters
+// (step 1 of the header).  When sst/coff/soff are given (LDS, N + 1 entries
+// each), the boundaries and the chunk and segment prefix sums are also kept
+// there, and the lengths are computed from the LDS copy.
+__device__ void index_scan_body(const int32_t* __restrict__ cu, int N, long long T_row, long long total,
+                                int seg_chunks, Tables t, long long* smem, int* flags, int* sst, int* coff,
+                                int* soff, int* foff) {
+  if (threadIdx.x == 0) *flags = 0;
   __syncthreads();
   // pass 1: boundaries b_i, i = 0..N (clamped running maximum of the offsets)
   long long carry = 0;
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __
         if (i > 0 && x < (long long)cu[i - 1]) f |= 2;
         if (i == N && x != total) f |= 4;
         if (x < 0 || x > total) f |= 8;
-        if (f) atomicOr(&flags, f);
+        if (f) atomicOr(flags, f);
       } else {
         x = (long long)i * T_row;
       }
@@ -90,42 +102,64 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __
     long long run = block_inclusive_scan(x, MaxOp(), (long long)INT64_MIN, smem, &tot);
     run = run > carry ? run : carry;
     long long b = run < 0 ? 0 : (run > total ? total : run);
-    if (i <= N) t.seq_start[i] = (int32_t)b;
+    if (i <= N) {
+      t.seq_start[i] = (int32_t)b;
+      if (sst) sst[i] = (int32_t)b;
+    }
     carry = tot > carry ? tot : carry;
   }
   __threadfence_block();
   __syncthreads();
   // pass 2: lengths, chunk and segment counts, exclusive prefix sums
-  long long c_carry = 0, s_carry = 0;
+  long long c_carry = 0, s_carry = 0, f_carry = 0;
   if (threadIdx.x == 0) {
     t.seq_chunk_off[0] = 0;
     t.seq_seg_off[0] = 0;
+    t.seq_full_off[0] = 0;
+    if (coff) coff[0] = 0;
+    if (soff) soff[0] = 0;
+    if (foff) foff[0] = 0;
   }
   for (int base = 0; base < N; base += SCAN_THREADS) {
     const int i = base + (int)threadIdx.x;
-    long long nc = 0, ns = 0;
+    long long nc = 0, ns = 0, nf = 0;
     if (i < N) {
-      const long long len = (long long)t.seq_start[i + 1] - (long long)t.seq_start[i];
+      const long long len = sst ? (long long)sst[i + 1] - (long long)sst[i]
+                                : (long long)t.seq_start[i + 1] - (long long)t.seq_start[i];
       t.seq_len[i] = (int32_t)len;
       nc = (len + C - 1) / C;
       ns = seg_chunks > 0 ? (nc > 0 ? (nc + seg_chunks - 1) / seg_chunks : 1) : 1;
+      nf = seg_chunks > 0 ? nc / seg_chunks : 1;  // serial: every sequence counts as full
     }
-    long long ctot, stot;
+    long long ctot, stot, ftot;
     const long long ci = block_inclusive_scan(nc, AddOp(), 0LL, smem, &ctot);
     const long long si = block_inclusive_scan(ns, AddOp(), 0LL, smem, &stot);
+    const long long fi = block_inclusive_scan(nf, AddOp(), 0LL, smem, &ftot);
     if (i < N) {
       t.seq_chunk_off[i + 1] = (int32_t)(c_carry + ci);
       t.seq_seg_off[i + 1] = (int32_t)(s_carry + si);
+      t.seq_full_off[i + 1] = (int32_t)(f_carry + fi);
+      if (coff) coff[i + 1] = (int32_t)(c_carry + ci);
+      if (soff) soff[i + 1] = (int32_t)(s_carry + si);
+      if (foff) foff[i + 1] = (int32_t)(f_carry + fi);
     }
     c_carry += ctot;
     s_carry += stot;
+    f_carry += ftot;
   }
   if (threadIdx.x == 0) {
     t.counters[CNT_N_CHUNKS] = (int32_t)c_carry;
     t.counters[CNT_N_SEGS] = (int32_t)s_carry;
-    t.counters[CNT_FLAGS] = flags;
-    t.counters[3] = 0;
+    t.counters[CNT_FLAGS] = *flags;
+    t.counters[CNT_EARLY_STOPS] = 0;
   }
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __restrict__ cu, int N, long long T_row,
+                                                               long long total, int seg_chunks, Tables t) {
+  __shared__ long long smem[SCAN_WAVES];
+  __shared__ int flags;
+  index_scan_body(cu, N, T_row, total, seg_chunks, t, smem, &flags, nullptr, nullptr, nullptr, nullptr);
 }
 
 // largest j in [0, n) with off[j] <= x, given off[0] = 0 <= x and off non-decreasing
@@ -139,6 +173,47 @@ __device__ __forceinline__ int owner_of(const int32_t* off, int n, int x) {
       hi = mid;
   }
   return lo;
+}
+
+// seg_tab row of segment idx of sequence sq, given its prefix sums
+__device__ __forceinline__ void seg_row(int32_t* row, int sq, int idx, const int* coff, const int* soff,
+                                        int seg_chunks) {
+  const int j = idx - soff[sq];
+  const int first = coff[sq];
+  const int nc = coff[sq + 1] - first;
+  int r1, r2;
+  if (seg_chunks > 0) {
+    const long long b0 = (long long)j * seg_chunks;
+    const long long e0 = b0 + seg_chunks;
+    r1 = first + (int)(b0 < nc ? b0 : nc);
+    r2 = first + (int)(e0 < nc ? e0 : nc);
+  } else {
+    r1 = first;
+    r2 = first + nc;
+  }
+  row[0] = sq;
+  row[1] = r1;
+  row[2] = r2;
+  row[3] = j;
+}
+
+// Puts segment idx (seg_tab row `row`) into the dispatch table at its rank:
+// the full-length segments in segment order, then the others (a sequence's
+// shorter last segment) in segment order.
+__device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32_t* row, const int* soff,
+                                         const int* foff, int n_full) {
+  const int sq = row[0], j = row[3];
+  const int full_here = foff[sq + 1] - foff[sq];
+  const int rank = j < full_here ? foff[sq] + j : n_full + (soff[sq] - foff[sq]);
+  int32_t* u = unit_tab + 8 * rank;
+  u[0] = idx;
+  u[1] = row[0];
+  u[2] = row[1];
+  u[3] = row[2];
+  u[4] = row[3];
+  u[5] = -1;
+  u[6] = -1;
+  u[7] = -1;
 }
 
 __global__ __launch_bounds__(256) void kda_index_fill(int N, int seg_chunks, long long max_chunks, long long max_segs,
@@ -159,34 +234,77 @@ __global__ __launch_bounds__(256) void kda_index_fill(int N, int seg_chunks, lon
     t.chunk_tab[2 * idx + 1] = b;
   }
   if (idx < max_segs) {
-    int r0 = -1, r1 = -1, r2 = -1, r3 = -1;
+    int32_t row[4] = {-1, -1, -1, -1};
     if (idx < n_segs) {
       int s = owner_of(t.seq_seg_off, N + 1, (int)idx);
       while (s + 1 <= N && t.seq_seg_off[s + 1] <= (int)idx) ++s;
-      const int j = (int)idx - t.seq_seg_off[s];
-      const int first = t.seq_chunk_off[s];
-      const int nc = t.seq_chunk_off[s + 1] - first;
-      r0 = s;
-      r3 = j;
-      if (seg_chunks > 0) {
-        const long long b0 = (long long)j * seg_chunks;
-        const long long e0 = b0 + seg_chunks;
-        r1 = first + (int)(b0 < nc ? b0 : nc);
-        r2 = first + (int)(e0 < nc ? e0 : nc);
-      } else {
-        r1 = first;
-        r2 = first + nc;
-      }
+      seg_row(row, s, (int)idx, t.seq_chunk_off, t.seq_seg_off, seg_chunks);
+      put_unit(t.unit_tab, (int)idx, row, t.seq_seg_off, t.seq_full_off, t.seq_full_off[N]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t.unit_tab[8 * idx + k] = -1;
     }
-    t.seg_tab[4 * idx + 0] = r0;
-    t.seg_tab[4 * idx + 1] = r1;
-    t.seg_tab[4 * idx + 2] = r2;
-    t.seg_tab[4 * idx + 3] = r3;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t.seg_tab[4 * idx + k] = row[k];
+  }
+}
+
+// Both steps in one workgroup.  Thread t fills a contiguous range of table
+// rows: one binary search in the LDS copy of the prefix sums for its first
+// row, then a forward walk (the owner of consecutive rows never decreases).
+__global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* __restrict__ cu, int N, long long T_row,
+                                                                long long total, int seg_chunks, int max_chunks,
+                                                                int max_segs, Tables t) {
+  __shared__ long long smem[SCAN_WAVES];
+  __shared__ int flags;
+  __shared__ int sst[FUSED_MAX_N + 1], coff[FUSED_MAX_N + 1], soff[FUSED_MAX_N + 1], foff[FUSED_MAX_N + 1];
+  index_scan_body(cu, N, T_row, total, seg_chunks, t, smem, &flags, sst, coff, soff, foff);
+  __syncthreads();
+  const int n_chunks = coff[N], n_segs = soff[N];
+  {
+    const int per = (max_chunks + SCAN_THREADS - 1) / SCAN_THREADS;
+    const int r0 = (int)threadIdx.x * per;
+    const int r1 = min(r0 + per, max_chunks);
+    int a = r0 < n_chunks ? owner_of(coff, N + 1, r0) : 0;
+    for (int r = r0; r < r1; ++r) {
+      int x = -1, y = -1;
+      if (r < n_chunks) {
+        while (a + 1 <= N && coff[a + 1] <= r) ++a;  // also skips empty sequences
+        x = a;
+        y = r - coff[a];
+      }
+      t.chunk_tab[2 * r] = x;
+      t.chunk_tab[2 * r + 1] = y;
+    }
+  }
+  {
+    const int per = (max_segs + SCAN_THREADS - 1) / SCAN_THREADS;
+    const int r0 = (int)threadIdx.x * per;
+    const int r1 = min(r0 + per, max_segs);
+    int a = r0 < n_segs ? owner_of(soff, N + 1, r0) : 0;
+    for (int r = r0; r < r1; ++r) {
+      int32_t row[4] = {-1, -1, -1, -1};
+      if (r < n_segs) {
+        while (a + 1 <= N && soff[a + 1] <= r) ++a;
+        seg_row(row, a, r, coff, soff, seg_chunks);
+        put_unit(t.unit_tab, r, row, soff, foff, foff[N]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t.unit_tab[8 * r + k] = -1;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t.seg_tab[4 * r + k] = row[k];
+    }
   }
 }
 
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st) {
+  if (N <= FUSED_MAX_N && max_chunks <= FUSED_MAX_ROWS && max_segs <= FUSED_MAX_ROWS) {
+    hipLaunchKernelGGL(kda_index_fused, dim3(1), dim3(SCAN_THREADS), 0, st, cu_seqlens, N, (long long)T_row,
+                       (long long)total_tokens, seg_chunks, (int)max_chunks, (int)max_segs, t);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(kda_index_scan, dim3(1), dim3(SCAN_THREADS), 0, st, cu_seqlens, N, (long long)T_row,
                      (long long)total_tokens, seg_chunks, t);
   hipError_t e = hipGetLastError();

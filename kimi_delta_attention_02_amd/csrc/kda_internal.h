@@ -35,6 +35,8 @@ struct Tables {
   int32_t* seq_seg_off;
   int32_t* chunk_tab;
   int32_t* seg_tab;
+  int32_t* seq_full_off;
+  int32_t* unit_tab;
 };
 
 struct Problem {

@@ -66,7 +66,7 @@ def test_workspace_layout_consistent():
         off = kda.workspace_offsets(*args)
         assert off["total"] == size
         prev = -1
-        for name in kda.WS_FIELDS[:12]:
+        for name in kda.WS_FIELDS[:14]:
             assert off[name] % kda.WS_ALIGN == 0
             assert off[name] >= prev
             prev = off[name]
@@ -77,12 +77,14 @@ def test_workspace_layout_consistent():
         assert off["seg_m"] - off["seg_tab"] >= 16 * off["max_segs"]
         mat = off["max_segs"] * H * 128 * 128 * 4
         if seg == 0:
-            assert off["seg_s"] == off["seg_r"] == off["seg_m"] == off["seg_mnz"] == off["seg_chk"] == off["total"]
+            assert off["seg_s"] == off["seg_r"] == off["seg_m"] == off["seg_mnz"] == off["seg_chk"] == off["seq_full_off"]
         else:
             assert off["seg_r"] - off["seg_m"] >= mat and off["seg_s"] - off["seg_r"] >= mat
             assert off["seg_mnz"] - off["seg_s"] >= mat
             assert off["seg_chk"] - off["seg_mnz"] >= off["max_segs"] * H * 8 * 4
-            assert off["total"] - off["seg_chk"] >= mat
+            assert off["seq_full_off"] - off["seg_chk"] >= mat
+        assert off["unit_tab"] - off["seq_full_off"] >= 4 * (N + 1)
+        assert off["total"] - off["unit_tab"] >= 32 * off["max_segs"]
 
 
 def _call(lib, **kw):

@@ -123,9 +123,12 @@ def test_every_chunk_tail(lb, init_std):
 
 # ------------------------------------------------------------------- index tables, bit-exact
 @pytest.mark.parametrize("lens,seg", [([1023, 1025, 1, 16, 4097, 8191, 65537], 64), ([0, 1, 15, 16, 17, 0], 1),
-                                      ([65536] + [1024] * 5, 0), ([65537], 37)])
+                                      ([65536] + [1024] * 5, 0), ([65537], 37),
+                                      # past the one-workgroup form's limits (4095 sequences, 16384 rows):
+                                      # the two-launch form
+                                      ([3] * 5000, 0), ([300000], 64)])
 def test_index_tables_bit_exact(lens, seg):
-    w = kda_inputs.custom(seqlens=lens, H=1, seed=28, name="tables")
+    w = kda_inputs.custom(seqlens=lens, H=1, seed=28, name="tables", init_std=None)
     x = kda_inputs.make_inputs(w)
     d = dev_inputs(x)
     mode = "force" if seg else "off"
@@ -143,6 +146,19 @@ def test_index_tables_bit_exact(lens, seg):
     np.testing.assert_array_equal(read_ws(ws, offs, "chunk_tab", 2 * nch, np.int32).reshape(-1, 2), ref["chunk_tab"])
     np.testing.assert_array_equal(read_ws(ws, offs, "seg_tab", 4 * nsg, np.int32).reshape(-1, 4), ref["seg_tab"])
     np.testing.assert_array_equal(read_ws(ws, offs, "seq_len", N, np.int32), lens)
+    # rows past the live counts are -1
+    mc, ms = offs["max_chunks"], offs["max_segs"]
+    assert (read_ws(ws, offs, "chunk_tab", 2 * mc, np.int32)[2 * nch:] == -1).all()
+    assert (read_ws(ws, offs, "seg_tab", 4 * ms, np.int32)[4 * nsg:] == -1).all()
+    # dispatch order: every full-length segment (seg chunks), then the others,
+    # each group in segment order (serial: every sequence counts as full)
+    st = ref["seg_tab"]
+    full = [i for i in range(nsg) if not seg or st[i][2] - st[i][1] == seg]
+    rest = [i for i in range(nsg) if seg and st[i][2] - st[i][1] != seg]
+    want = np.array([[i, *st[i], -1, -1, -1] for i in full + rest], dtype=np.int32).reshape(-1, 8)
+    unit = read_ws(ws, offs, "unit_tab", 8 * ms, np.int32).reshape(-1, 8)
+    np.testing.assert_array_equal(unit[:nsg], want)
+    assert (unit[nsg:] == -1).all()
 
 
 def test_malformed_offsets_are_clamped():
