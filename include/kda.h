@@ -138,6 +138,8 @@ typedef enum {
                                chunk begin, chunk end, segment in sequence, -1, -1, -1); every
                                full-length segment first, then the shorter last segments, each group
                                in segment order (-1 past the live count) */
+  KDA_WS_SEG_FIX,           /* fp32 [max_segs][H][128][128] state after a segment's first 4 chunks as the
+                               first pass's block of the previous segment reached it (CP only) */
   KDA_WS_MAX_CHUNKS,        /* (count, not an offset) chunk-table capacity */
   KDA_WS_MAX_SEGS,          /* (count, not an offset) segment-table capacity */
   KDA_WS_TOTAL,             /* total bytes (= kda_get_workspace_size) */

@@ -154,6 +154,7 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
   take(KDA_WS_SEG_CHK, seg_bytes);
   take(KDA_WS_SEQ_FULL_OFF, 4 * ((int64_t)N + 1));
   take(KDA_WS_UNIT_TAB, 32 * ms);
+  take(KDA_WS_SEG_FIX, seg_bytes);
   out->off[KDA_WS_MAX_CHUNKS] = mc;
   out->off[KDA_WS_MAX_SEGS] = ms;
   out->off[KDA_WS_TOTAL] = o;
@@ -250,6 +251,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   sg.R = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
   sg.S = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_S]) : nullptr;
   sg.chk = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_CHK]) : nullptr;
+  sg.fix = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_FIX]) : nullptr;
   sg.mnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
   sg.chk_chunks = cp ? kCheckChunks : 0;
   const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];

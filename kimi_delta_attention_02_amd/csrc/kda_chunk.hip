@@ -497,8 +497,8 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[NT][8], float* dst3
 
 }  // namespace
 
-template <int ROLE>
-__device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, const Seg& sg, int phase,
+template <int ROLE, int phase>
+__device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, const Seg& sg,
                                            const int32_t* urow, int h) {
   const int sidx = urow[0];
   const int seq = urow[1];
@@ -541,6 +541,58 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   // a last segment without a checkpoint: the first pass has nothing to hand on
   // (no merge after it, and the second pass runs it whole)
   if (ROLE == PRE && j == ns - 1 && !has_chk) return;
+  // The first pass goes on for K chunks into the next segment of the sequence
+  // (when that one has a checkpoint) from its own end state, which is the next
+  // segment's start state when this is segment 0 or its M is exactly zero.
+  // It writes those chunks' output and stores its state after them (fix): the
+  // second pass keeps them if that state equals the next segment's checkpoint
+  // bit for bit, and then has nothing left to compute.
+  int ext = 0;
+  if (phase == 0 && K > 0 && j < ns - 1) {
+    const int nn = t.seg_tab[4 * (sidx + 1) + 2] - t.seg_tab[4 * (sidx + 1) + 1];
+    if (nn > K) ext = K;
+  }
+  const int ntot = nch + ext;  // chunks this block runs
+  const long long seg_base = ((long long)sidx * H + h) * D * D;
+  const long long state_base = ((long long)seq * H + h) * D * D;
+
+  // Second pass: the first pass already ran this segment's first K chunks from
+  // its start state (the previous segment's R, kept when that segment's M is
+  // zero; or S_1).  If the state it reached equals the checkpoint bit for bit,
+  // every output of the segment is final and the block has nothing to do.
+  if (ROLE == RECUR && phase == 1 && has_chk) {
+    bool from_r = true;
+    if (j >= 2) {
+      const int32_t* nzf = sg.mnz + ((long long)(sidx - 1) * H + h) * (D / 16);
+      int nz = 0;
+#pragma unroll
+      for (int b = 0; b < D / 16; ++b) nz |= nzf[b];
+      from_r = nz == 0;
+    }
+    if (from_r) {
+      const u32x4* fa = reinterpret_cast<const u32x4*>(sg.fix + seg_base);
+      const u32x4* ch = reinterpret_cast<const u32x4*>(sg.chk + seg_base);
+      uint32_t diff = 0;
+      for (int i = threadIdx.x; i < D * D / 4; i += NTHREADS) {
+        const u32x4 x = fa[i] ^ ch[i];
+        diff |= x.x | x.y | x.z | x.w;
+      }
+      if (!__syncthreads_or(diff != 0u)) {
+        if (threadIdx.x == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
+        if (j == ns - 1 && p.final_state) {  // the end state is this segment's R
+          const f32x4* r = reinterpret_cast<const f32x4*>(sg.R + seg_base);
+          for (int i = threadIdx.x; i < D * D / 4; i += NTHREADS) {
+            const f32x4 v = r[i];
+            if (p.state_fp32)
+              reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + state_base)[i] = v;
+            else
+              reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + state_base)[i] = pack4(v);
+          }
+        }
+        return;
+      }
+    }
+  }
 
   const float a2 = LOG2E * expf(p.A_log[h]);
   if (threadIdx.x < D) sm.adt[threadIdx.x] = a2 * p.dt_bias[h * D + threadIdx.x];
@@ -556,12 +608,12 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     // past the last chunk the next-chunk address repeats the current one
     // (always in bounds, loaded and unused)
     auto addr = [&](int lc) {
-      const int lcc = lc < nch ? lc : lc - NPW;
+      const int lcc = lc < ntot ? lc : lc - NPW;
       return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, g, c);
     };
     // chunks the block runs: nch, or K once the consumers agreed to stop
     // there; -1 while their vote is incomplete
-    auto n_run = [&]() -> int { return may_stop ? vote_chunks(wg_load(&sm.vote), K, nch) : nch; };
+    auto n_run = [&]() -> int { return may_stop ? vote_chunks(wg_load(&sm.vote), K, nch) : ntot; };
     // 1 once every consumer is done with chunk y, 0 if the block stopped
     // before y, -1 when the (bounded) wait gives up
     auto wait_done = [&](int y) -> int {
@@ -599,14 +651,14 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     // lc it waits until the slot's previous chunk lc - NSLOT is consumed and
     // writes that chunk's output rows; past the last chunk it goes on only to
     // write out the outputs of the last NSLOT chunks.
-    if (pw < nch) load_prod(in, addr(pw));
-    for (int lc = pw; lc < nch + NSLOT; lc += NPW) {
+    if (pw < ntot) load_prod(in, addr(pw));
+    for (int lc = pw; lc < ntot + NSLOT; lc += NPW) {
       const int y = lc - NSLOT;
       if (y >= 0) {
         if (wait_done(y) <= 0) break;
         if (y >= o_from) flush(y);
       }
-      if (lc < nch) {
+      if (lc < ntot) {
         // chunks past the checkpoint wait for the vote (the block usually stops
         // there, and a chunk prepared meanwhile would slow the consumers)
         int n = n_run();
@@ -636,8 +688,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   // ======================= consumer =======================
   const int cw = wave - NPW;
   const int col0 = 16 * TPW * cw;
-  const long long state_base = ((long long)seq * H + h) * D * D;
-  const long long seg_base = ((long long)sidx * H + h) * D * D;
+  const long long fix_base = seg_base + (long long)H * D * D;  // the next segment's slot
 
   // The next chunk's ready flag is read early (relaxed) and looked at only
   // after this chunk is done; a chunk seen ready there needs no wait.  The
@@ -789,6 +840,10 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       base = seg_base + (long long)H * D * D;
     }
     store_state<TPW>(S, dst32, dst16, base, col0, g, c);
+    if (ext > 0 && ok) {  // into the next segment (see above)
+      for (int e = 0; ok && e < ext; ++e) ok = step_s(nch + e, S, WithOut{});
+      if (ok) store_state<TPW>(S, sg.fix, nullptr, fix_base, col0, g, c);
+    }
   } else {
     // first pass on the same columns: R (start 0, with Ut) and M (start I,
     // Ut = 0).  A column of M evolves on its own (U = -T' Kbar M needs only
@@ -860,6 +915,10 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         for (int jj = 0; jj < TPW; ++jj) sg.mnz[((long long)sidx * H + h) * (D / 16) + col0 / 16 + jj] = mzero ? 0 : 1;
       }
     }
+    if (ext > 0 && ok) {  // into the next segment (see above)
+      for (int e = 0; ok && e < ext; ++e) ok = step_s(nch + e, Rs, WithOut{});
+      if (ok) store_state<TPW>(Rs, sg.fix, nullptr, fix_base, col0, g, c);
+    }
   }
 }
 
@@ -869,30 +928,37 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 // is known only on the device) take the first blocks and the rest exit at
 // once: blocks are dealt to the XCDs in turn, and this keeps their shares of
 // the work equal.
-// MODE 0: the recurrence of the segments the phase selects.
+// MODE 0: whole sequences (serial plan).
 // MODE 1: first pass of a segmented call: segment 0 of each sequence from the
 // initial state, the others from a zero state.
+// MODE 2: second pass of a segmented call: segments >= 1 from their start states.
 template <int MODE>
-__global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, Seg sg, int phase) {
+__global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, Seg sg) {
   __shared__ Smem sm;
   const int k = (int)blockIdx.x / p.H;
   const int h = (int)blockIdx.x - k * p.H;
   if (k >= t.counters[CNT_N_SEGS]) return;
   const int32_t* urow = t.unit_tab + 8 * k;
-  if (MODE == 0 || urow[4] == 0)
-    chunk_body<RECUR>(sm, p, t, sg, phase, urow, h);
+  if (MODE == 0)
+    chunk_body<RECUR, 0>(sm, p, t, sg, urow, h);
+  else if (MODE == 2)
+    chunk_body<RECUR, 1>(sm, p, t, sg, urow, h);
+  else if (urow[4] == 0)
+    chunk_body<RECUR, 0>(sm, p, t, sg, urow, h);
   else
-    chunk_body<PRE>(sm, p, t, sg, 0, urow, h);
+    chunk_body<PRE, 0>(sm, p, t, sg, urow, h);
 }
 
 hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
                          hipStream_t st) {
   if (max_segs <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)(max_segs * p.H);
-  if (phase == 0 && segmented)
-    hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg, 0);
+  if (!segmented)
+    hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg);
+  else if (phase == 0)
+    hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg);
   else
-    hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg, phase);
+    hipLaunchKernelGGL(kda_chunk_kernel<2>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg);
   return hipGetLastError();
 }
 

@@ -62,12 +62,15 @@ struct Problem {
 //   M, R : transition and zero-start state of segments >= 1 (first pass);
 //   S    : merged state entering a segment;
 //   chk  : R after the first chk_chunks chunks of segments >= 1 (first pass);
+//   fix  : the state after a segment's first chk_chunks chunks as the first
+//          pass's block of the previous segment reached it (first pass);
 //   mnz  : per (segment, head, 16-column block of M) 1 if nonzero, 0 if exactly zero.
 struct Seg {
   float* M;
   float* R;
   float* S;
   float* chk;
+  float* fix;
   int32_t* mnz;
   int chk_chunks;
 };

@@ -66,7 +66,7 @@ def test_workspace_layout_consistent():
         off = kda.workspace_offsets(*args)
         assert off["total"] == size
         prev = -1
-        for name in kda.WS_FIELDS[:14]:
+        for name in kda.WS_FIELDS[:15]:
             assert off[name] % kda.WS_ALIGN == 0
             assert off[name] >= prev
             prev = off[name]
@@ -84,7 +84,8 @@ def test_workspace_layout_consistent():
             assert off["seg_chk"] - off["seg_mnz"] >= off["max_segs"] * H * 8 * 4
             assert off["seq_full_off"] - off["seg_chk"] >= mat
         assert off["unit_tab"] - off["seq_full_off"] >= 4 * (N + 1)
-        assert off["total"] - off["unit_tab"] >= 32 * off["max_segs"]
+        assert off["seg_fix"] - off["unit_tab"] >= 32 * off["max_segs"]
+        assert off["total"] - off["seg_fix"] >= (mat if seg else 0)
 
 
 def _call(lib, **kw):
