@@ -242,7 +242,7 @@ def main() -> int:
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfl / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    kernels = ["kda_chunk_kernel<1>", "kda_chunk_kernel<0>"] if seg > 0 else ["kda_chunk_kernel<0>"]
+    kernels = ["kda_chunk_kernel<1>", "kda_chunk_kernel<2>"] if seg > 0 else ["kda_chunk_kernel<0>"]
     per_launch = [measured_traffic(w.name, k) for k in kernels]
     roof["traffic"] = None if any(t is None for t in per_launch) else sum(per_launch)
     roof["kernel"] = "kda_chunk_kernel"
