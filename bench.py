@@ -198,9 +198,11 @@ def main() -> int:
     # and lengthen it, so region 2 does not feed ms_per_step.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     evs[0].record(stream)
+    h0 = time.perf_counter()
     for i in range(a.steps):
         step()
         evs[i + 1].record(stream)
+    host_us = (time.perf_counter() - h0) / a.steps * 1e6  # submission only: the loop never waits
     torch.cuda.synchronize()
     kda.profile_enable(True)
     for i in range(a.steps):
@@ -280,6 +282,8 @@ def main() -> int:
             "hbm_frac": round(path_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_frac": round(path_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "iqr_mean_ms": round(iqr_mean, 4),
+            # host time to submit one call (Python binding + C ABI validation + launches)
+            "host_us_per_call": round(host_us, 1),
         },
         "stages_ms_per_step": {n: round(t / a.steps, 4) for n, (t, c) in stages.items() if c},
     }

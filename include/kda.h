@@ -51,6 +51,10 @@ typedef enum {
 } kda_status;
 
 typedef enum { KDA_STATE_BF16 = 0, KDA_STATE_FP32 = 1 } kda_state_dtype;
+/* Layout of the caller's state tensors: [N, H, V, K] (the transposed layout
+ * the kernel API requires, "State Handling and Variable-Length Batches") or
+ * [N, H, K, V] (the chunk_kda call with transpose_state_layout=False). */
+typedef enum { KDA_STATE_VK = 0, KDA_STATE_KV = 1 } kda_state_layout;
 
 /* Segment split of long sequences (the intracard context-parallel switch of
  * the cuLA PR #106 page, with its automatic, off and on settings). */
@@ -85,6 +89,8 @@ size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t n
  *                  may alias initial_state.  Any of the four presence
  *                  combinations is valid.
  *   state_dtype  : kda_state_dtype, applies to whichever state is present
+ *   state_layout : kda_state_layout of both states (KDA_STATE_KV: [N, H,
+ *                  128(K), 128(V)] instead)
  *   cu_seqlens   : NULL (fixed length, N = B) or int32 [num_seqs + 1] device
  *                  offsets into the packed token axis (then B must be 1).
  *                  Offsets are clamped into a non-decreasing sequence within
@@ -101,7 +107,7 @@ size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t n
  * B*T == 0 with no final_state returns KDA_OK without a launch. */
 int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                 float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
-                const void* initial_state, void* final_state, int32_t state_dtype,
+                const void* initial_state, void* final_state, int32_t state_dtype, int32_t state_layout,
                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t D,
                 void* workspace, size_t workspace_bytes, int32_t cp_mode, int32_t seg_chunks,
                 void* stream);

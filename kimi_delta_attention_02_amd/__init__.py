@@ -26,6 +26,7 @@ from typing import Optional
 
 __all__ = [
     "fwd",
+    "chunk_kda",
     "get_workspace_size",
     "plan_seg_chunks",
     "workspace_offsets",
@@ -82,7 +83,7 @@ def load_library():
     lib.kda_get_workspace_size.restype = sz
     lib.kda_workspace_offsets.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
     lib.kda_workspace_offsets.restype = i32
-    lib.kda_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, vp, i32, vp, i32, i32, i64, i32, i32,
+    lib.kda_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, vp, i32, i32, vp, i32, i32, i64, i32, i32,
                             vp, sz, i32, i32, vp]
     lib.kda_fwd.restype = i32
     lib.kda_profile_enable.argtypes = [i32]
@@ -182,13 +183,15 @@ def _check(t, name, dtype, shape=None):
 
 
 def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound: float, workspace=None,
-        initial_state=None, final_state=None, cu_seqlens=None, cp_mode="auto", seg_chunks: int = 0):
+        initial_state=None, final_state=None, cu_seqlens=None, cp_mode="auto", seg_chunks: int = 0,
+        state_layout: str = "vk"):
     """KDA forward.  Returns out (allocated if None).
 
     q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; A_log: fp32 [H];
     dt_bias: fp32 [H, 128]; lower_bound in [-5, 0];
-    initial_state / final_state: None or [N, H, 128, 128] ([v][k]) in bf16 or
-    fp32 (both the same dtype when both are given); cu_seqlens: None or int32
+    initial_state / final_state: None or [N, H, 128, 128] in bf16 or fp32
+    (both the same dtype when both are given), [v][k] per head when
+    state_layout is "vk", [k][v] when it is "kv"; cu_seqlens: None or int32
     [N + 1] (then B == 1); workspace: uint8 device buffer of at least
     get_workspace_size(B*T, H, N, cp_mode, seg_chunks) bytes, 256-byte
     aligned (allocated here when None); cp_mode: "auto" | "off" | "force".
@@ -235,6 +238,8 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
     for t in tensors:
         if t is not None and t.device != dev:
             raise ValueError("all tensors must be on the same device")
+    if state_layout not in ("vk", "kv"):
+        raise ValueError(f"state_layout must be 'vk' or 'kv' (got {state_layout!r})")
     cpm = _cp(cp_mode)
     need = get_workspace_size(B * T, H, N, cpm, seg_chunks)
     with torch.cuda.device_of(q):
@@ -247,7 +252,7 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
             A_log.data_ptr(), dt_bias.data_ptr(), float(lower_bound),
             initial_state.data_ptr() if initial_state is not None else None,
             final_state.data_ptr() if final_state is not None else None,
-            1 if sdt in (None, torch.float32) else 0,
+            1 if sdt in (None, torch.float32) else 0, 1 if state_layout == "kv" else 0,
             cu_seqlens.data_ptr() if cu_seqlens is not None else None, N if cu_seqlens is not None else 0,
             B, T, H, D, workspace.data_ptr(), workspace.numel(), cpm, int(seg_chunks), stream)
     if st != 0:
@@ -259,3 +264,46 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
         print(f"[kda] fwd B={B} T={T} H={H} N={N} plan={'serial' if seg == 0 else f'segments of {seg} chunks'}",
               file=sys.stderr)
     return out
+
+
+def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state: bool = False, *, A_log,
+              dt_bias, lower_bound: float, use_gate_in_kernel: bool = True, use_qk_l2norm_in_kernel: bool = True,
+              use_beta_sigmoid_in_kernel: bool = True, safe_gate: bool = True, transpose_state_layout: bool = True,
+              cu_seqlens=None, cp_mode="auto"):
+    """The chunk_kda call of the flash-linear-attention integration ("How to Use
+    FlashKDA as a Backend for flash-linear-attention", "Running Inference with
+    chunk_kda"), served by this library.  Returns (out, final_state), with
+    final_state None unless output_final_state.
+
+    Same tensors as fwd.  scale None means 1/sqrt(128).  With
+    transpose_state_layout the states are [N, H, V, K] per head, otherwise
+    [N, H, K, V]; the kernels read and write either layout directly.  The final
+    state is allocated in the initial state's dtype (float32 without one);
+    out and the workspace are allocated here too.
+
+    The kernels always apply the L2 norm of q and k, the beta sigmoid and the
+    lower-bounded gate; the integration page routes other settings of those
+    flags to a different implementation, which this library does not have, so
+    they raise ValueError.
+    """
+    import torch
+
+    for name, val in (("use_gate_in_kernel", use_gate_in_kernel),
+                      ("use_qk_l2norm_in_kernel", use_qk_l2norm_in_kernel),
+                      ("use_beta_sigmoid_in_kernel", use_beta_sigmoid_in_kernel), ("safe_gate", safe_gate)):
+        if val is not True:
+            raise ValueError(f"{name}={val!r} is not supported: the kernels compute only the {name}=True form")
+    if scale is None:
+        scale = HEAD_DIM ** -0.5
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B, T, H, D] tensor")
+    B, T, H, D = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    final = None
+    if output_final_state:
+        sdt = initial_state.dtype if initial_state is not None else torch.float32
+        final = torch.empty((N, H, D, D), dtype=sdt, device=q.device)
+    out = fwd(q, k, v, g, beta, scale, None, A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
+              initial_state=initial_state, final_state=final, cu_seqlens=cu_seqlens, cp_mode=cp_mode,
+              state_layout="vk" if transpose_state_layout else "kv")
+    return out, final

@@ -190,7 +190,8 @@ int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t n
 
 int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale, void* out,
                 const float* A_log, const float* dt_bias, float lower_bound, const void* initial_state,
-                void* final_state, int32_t state_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                void* final_state, int32_t state_dtype, int32_t state_layout, const int32_t* cu_seqlens,
+                int32_t num_seqs, int32_t B,
                 int64_t T, int32_t H, int32_t D, void* workspace, size_t workspace_bytes, int32_t cp_mode,
                 int32_t seg_chunks, void* stream) {
   g_last_error.clear();
@@ -205,6 +206,8 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite");
   if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32)
     return fail(KDA_ERR_INVALID_ARG, "state_dtype %d invalid", state_dtype);
+  if (state_layout != KDA_STATE_VK && state_layout != KDA_STATE_KV)
+    return fail(KDA_ERR_INVALID_ARG, "state_layout %d invalid", state_layout);
   int32_t N;
   if (cu_seqlens) {
     if (B != 1) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens requires B == 1 (got B=%d)", B);
@@ -269,6 +272,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   p.init_state = initial_state;
   p.final_state = final_state;
   p.state_fp32 = state_dtype == KDA_STATE_FP32;
+  p.state_kv = state_layout == KDA_STATE_KV;
   p.scale = scale;
   p.lower_bound = lower_bound;
   p.H = H;

@@ -495,6 +495,38 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[NT][8], float* dst3
   }
 }
 
+// The caller's state in the [K][V] layout: element (k, v) at k D + v.  Lane
+// (g, c) holds rows k = 16tt + 4g + i of column v = col0 + 16jj + c, so each
+// scalar access is coalesced over the 16 lanes of a row group.
+template <int NT>
+__device__ __forceinline__ void load_state_kv(f32x4 (&S)[NT][8], const void* src, bool f32, long long base,
+                                              int col0, int g, int c) {
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long off = base + (long long)(16 * tt + 4 * g + i) * D + col0 + 16 * jj + c;
+        S[jj][tt][i] = f32 ? static_cast<const float*>(src)[off] : bf16_to_f32(static_cast<const uint16_t*>(src)[off]);
+      }
+}
+
+template <int NT>
+__device__ __forceinline__ void store_state_kv(const f32x4 (&S)[NT][8], float* dst32, uint16_t* dst16,
+                                               long long base, int col0, int g, int c) {
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long off = base + (long long)(16 * tt + 4 * g + i) * D + col0 + 16 * jj + c;
+        if (dst32) dst32[off] = S[jj][tt][i];
+        if (dst16) dst16[off] = (uint16_t)(pack2(S[jj][tt][i], 0.f) & 0xFFFFu);
+      }
+}
+
 }  // namespace
 
 template <int ROLE, int phase>
@@ -582,11 +614,21 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         if (j == ns - 1 && p.final_state) {  // the end state is this segment's R
           const f32x4* r = reinterpret_cast<const f32x4*>(sg.R + seg_base);
           for (int i = threadIdx.x; i < D * D / 4; i += NTHREADS) {
-            const f32x4 v = r[i];
-            if (p.state_fp32)
+            const f32x4 v = r[i];  // (v, k) = (4i / D, 4i % D + 0..3)
+            if (p.state_kv) {
+              const long long o = state_base + (long long)(4 * i % D) * D + 4 * i / D;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (p.state_fp32)
+                  static_cast<float*>(p.final_state)[o + e * D] = v[e];
+                else
+                  static_cast<uint16_t*>(p.final_state)[o + e * D] = (uint16_t)(pack2(v[e], 0.f) & 0xFFFFu);
+              }
+            } else if (p.state_fp32) {
               reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + state_base)[i] = v;
-            else
+            } else {
               reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + state_base)[i] = pack4(v);
+            }
           }
         }
         return;
@@ -783,8 +825,11 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         for (int b = 0; b < D / 16; ++b) nz |= nzf[b];
         if (nz == 0) seg_start = sg.R + seg_base - (long long)H * D * D;
       }
-      load_state<TPW>(S, from_seg ? (const void*)seg_start : p.init_state, from_seg || p.state_fp32,
-                      from_seg ? 0 : state_base, col0, g, c);
+      if (!from_seg && p.state_kv && p.init_state)
+        load_state_kv<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
+      else
+        load_state<TPW>(S, from_seg ? (const void*)seg_start : p.init_state, from_seg || p.state_fp32,
+                        from_seg ? 0 : state_base, col0, g, c);
     }
     int lc = 0;
     bool ok = true;
@@ -819,27 +864,23 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       if (stopped && cw == 0 && L == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
       for (; ok && !stopped && lc < nch; ++lc) ok = step_s(lc, S, WithOut{});
     }
-    float* dst32 = nullptr;
-    uint16_t* dst16 = nullptr;
-    long long base = 0;
     if (j == ns - 1) {
-      if (p.final_state) {
-        base = state_base;
-        if (p.state_fp32)
-          dst32 = static_cast<float*>(p.final_state);
-        else
-          dst16 = static_cast<uint16_t*>(p.final_state);
+      if (p.final_state) {  // the caller's final state, in its dtype and layout
         // stopped: the end state is the first pass's R of this segment
         if (stopped) load_state<TPW>(S, sg.R, true, seg_base, col0, g, c);
+        float* dst32 = p.state_fp32 ? static_cast<float*>(p.final_state) : nullptr;
+        uint16_t* dst16 = p.state_fp32 ? nullptr : static_cast<uint16_t*>(p.final_state);
+        if (p.state_kv)
+          store_state_kv<TPW>(S, dst32, dst16, state_base, col0, g, c);
+        else
+          store_state<TPW>(S, dst32, dst16, state_base, col0, g, c);
       }
     } else if (phase == 0) {
       // segment 0's end state is S_1, the merge's starting point (slot sidx + 1).
       // The second pass stores nothing here: the next segment's start state
       // was already merged, and that block may be reading it in this launch.
-      dst32 = sg.S;
-      base = seg_base + (long long)H * D * D;
+      store_state<TPW>(S, sg.S, nullptr, seg_base + (long long)H * D * D, col0, g, c);
     }
-    store_state<TPW>(S, dst32, dst16, base, col0, g, c);
     if (ext > 0 && ok) {  // into the next segment (see above)
       for (int e = 0; ok && e < ext; ++e) ok = step_s(nch + e, S, WithOut{});
       if (ok) store_state<TPW>(S, sg.fix, nullptr, fix_base, col0, g, c);

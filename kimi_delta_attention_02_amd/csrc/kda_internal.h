@@ -51,6 +51,7 @@ struct Problem {
   const void* init_state;
   void* final_state;
   int state_fp32;
+  int state_kv;  // caller's states are [N][H][K][V] (else [N][H][V][K])
   float scale;
   float lower_bound;
   int H;
