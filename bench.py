@@ -14,7 +14,9 @@ Per-stage kernel time comes from the library's own event hook
 stream) over a second run of K steps: its events sit between the kernels of
 a step and lengthen it, so the step time comes from the first, uninstrumented
 run.  The roofline object is computed for the chunk kernel (chunk prep +
-recurrence), summed over its launches in a step.
+recurrence), summed over its launches in a step.  The same call is also
+captured once in a HIP graph and replayed K times; that time and the host
+time per call are reported under "path", beside the plain calls.
 
 The CPU baseline times the fp64 oracle (unchanged) on a bounded sample of the
 same workload: whole sequences taken in order, all heads, one head per worker
@@ -204,6 +206,23 @@ def main() -> int:
         evs[i + 1].record(stream)
     host_us = (time.perf_counter() - h0) / a.steps * 1e6  # submission only: the loop never waits
     torch.cuda.synchronize()
+    # Timed region 3: the same call captured once in a HIP graph and replayed K
+    # times (the call allocates nothing and never synchronises, so it can be
+    # captured); reported beside the plain calls, not as the value.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    gev[0].record(stream)
+    h0 = time.perf_counter()
+    for i in range(a.steps):
+        graph.replay()
+    graph_host_us = (time.perf_counter() - h0) / a.steps * 1e6
+    gev[1].record(stream)
+    torch.cuda.synchronize()
+    graph_ms = gev[0].elapsed_time(gev[1]) / a.steps
+    del graph
     kda.profile_enable(True)
     for i in range(a.steps):
         step()
@@ -284,6 +303,9 @@ def main() -> int:
             "iqr_mean_ms": round(iqr_mean, 4),
             # host time to submit one call (Python binding + C ABI validation + launches)
             "host_us_per_call": round(host_us, 1),
+            # the call captured in a HIP graph, replayed K times
+            "graph_ms_per_step": round(graph_ms, 4),
+            "graph_host_us_per_call": round(graph_host_us, 1),
         },
         "stages_ms_per_step": {n: round(t / a.steps, 4) for n, (t, c) in stages.items() if c},
     }
