@@ -97,7 +97,12 @@ size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t n
  *                  [0, B*T] on the device, so malformed offsets cannot cause
  *                  out-of-bounds access; they are not otherwise diagnosed.
  *   num_seqs     : N; with cu_seqlens == NULL it must equal B (or be 0)
- *   B, T, H, D   : D must be 128
+ *   B, T, H, D   : D must be 128; H heads for v, g, beta, out, A_log, dt_bias
+ *                  and the states (one recurrence per sequence and head)
+ *   H_qk         : heads of q and k (0 means H).  When H_qk < H it must divide
+ *                  H, and head h uses q and k of head h / (H / H_qk) (grouped
+ *                  value heads: q and k are [B, T, H_qk, 128]; the reading of
+ *                  "HV > H" on the cuLA PR #106 page that this library takes)
  *   workspace    : device buffer, KDA_WORKSPACE_ALIGN-aligned, of at least
  *                  kda_get_workspace_size(B*T, H, N, cp_mode, seg_chunks) bytes;
  *                  owned by the caller, clobbered by the call, and must not be
@@ -108,8 +113,8 @@ size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t n
 int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                 float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
                 const void* initial_state, void* final_state, int32_t state_dtype, int32_t state_layout,
-                const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t D,
-                void* workspace, size_t workspace_bytes, int32_t cp_mode, int32_t seg_chunks,
+                const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t H_qk,
+                int32_t D, void* workspace, size_t workspace_bytes, int32_t cp_mode, int32_t seg_chunks,
                 void* stream);
 
 /* Byte offsets of the workspace regions for these sizes and plan, so a caller

@@ -84,7 +84,7 @@ def load_library():
     lib.kda_workspace_offsets.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
     lib.kda_workspace_offsets.restype = i32
     lib.kda_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, vp, i32, i32, vp, i32, i32, i64, i32, i32,
-                            vp, sz, i32, i32, vp]
+                            i32, vp, sz, i32, i32, vp]
     lib.kda_fwd.restype = i32
     lib.kda_profile_enable.argtypes = [i32]
     lib.kda_profile_enable.restype = i32
@@ -188,6 +188,8 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
     """KDA forward.  Returns out (allocated if None).
 
     q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; A_log: fp32 [H];
+    q and k may have fewer heads H_qk (dividing H): head h then uses q/k head
+    h // (H // H_qk) (grouped value heads);
     dt_bias: fp32 [H, 128]; lower_bound in [-5, 0];
     initial_state / final_state: None or [N, H, 128, 128] in bf16 or fp32
     (both the same dtype when both are given), [v][k] per head when
@@ -200,14 +202,18 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
 
     lib = load_library()
     _check(q, "q", torch.bfloat16)
-    if q.dim() != 4:
-        raise ValueError("q must be [B, T, H, D]")
-    B, T, H, D = q.shape
+    _check(v, "v", torch.bfloat16)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, T, heads, D]")
+    B, T, Hqk, D = q.shape
+    H = v.shape[2]
     if D != HEAD_DIM:
         raise ValueError(f"head dimension must be {HEAD_DIM} (got {D})")
+    if tuple(v.shape) != (B, T, H, D) or H % Hqk != 0:
+        raise ValueError(f"v has shape {tuple(v.shape)}: expected [B, T, H, D] with H a multiple of q's {Hqk} heads")
     dev = q.device
-    for name, t in (("k", k), ("v", v), ("g", g)):
-        _check(t, name, torch.bfloat16, q.shape)
+    _check(k, "k", torch.bfloat16, q.shape)
+    _check(g, "g", torch.bfloat16, v.shape)
     _check(beta, "beta", torch.bfloat16, (B, T, H))
     _check(A_log, "A_log", torch.float32, (H,))
     _check(dt_bias, "dt_bias", torch.float32, (H, D))
@@ -231,9 +237,9 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
             raise TypeError("initial_state and final_state must have the same dtype")
         sdt = st.dtype
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(v)
     else:
-        _check(out, "out", torch.bfloat16, q.shape)
+        _check(out, "out", torch.bfloat16, v.shape)
     tensors = [q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, workspace]
     for t in tensors:
         if t is not None and t.device != dev:
@@ -254,7 +260,7 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
             final_state.data_ptr() if final_state is not None else None,
             1 if sdt in (None, torch.float32) else 0, 1 if state_layout == "kv" else 0,
             cu_seqlens.data_ptr() if cu_seqlens is not None else None, N if cu_seqlens is not None else 0,
-            B, T, H, D, workspace.data_ptr(), workspace.numel(), cpm, int(seg_chunks), stream)
+            B, T, H, Hqk, D, workspace.data_ptr(), workspace.numel(), cpm, int(seg_chunks), stream)
     if st != 0:
         _raise(st)
     if os.environ.get("KDA_LOG") == "1":
@@ -295,9 +301,9 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
             raise ValueError(f"{name}={val!r} is not supported: the kernels compute only the {name}=True form")
     if scale is None:
         scale = HEAD_DIM ** -0.5
-    if not isinstance(q, torch.Tensor) or q.dim() != 4:
-        raise ValueError("q must be a [B, T, H, D] tensor")
-    B, T, H, D = q.shape
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a [B, T, H, D] tensor")
+    B, T, H, D = v.shape
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     final = None
     if output_final_state:

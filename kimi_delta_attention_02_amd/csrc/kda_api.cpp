@@ -192,13 +192,16 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
                 const float* A_log, const float* dt_bias, float lower_bound, const void* initial_state,
                 void* final_state, int32_t state_dtype, int32_t state_layout, const int32_t* cu_seqlens,
                 int32_t num_seqs, int32_t B,
-                int64_t T, int32_t H, int32_t D, void* workspace, size_t workspace_bytes, int32_t cp_mode,
+                int64_t T, int32_t H, int32_t H_qk, int32_t D, void* workspace, size_t workspace_bytes, int32_t cp_mode,
                 int32_t seg_chunks, void* stream) {
   g_last_error.clear();
   // ---- pure argument checks (no HIP calls before these pass) ----
   if (D != kda::D) return fail(KDA_ERR_UNSUPPORTED, "head dimension %d unsupported (only 128)", D);
   if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARG, "B=%d and T=%lld must be >= 0", B, (long long)T);
   if (H < 1) return fail(KDA_ERR_INVALID_ARG, "H=%d must be >= 1", H);
+  if (H_qk == 0) H_qk = H;
+  if (H_qk < 1 || H_qk > H || H % H_qk != 0)
+    return fail(KDA_ERR_INVALID_ARG, "H_qk=%d must divide H=%d", H_qk, H);
   if (T > 0 && B > kMaxTokens / T) return fail(KDA_ERR_INVALID_ARG, "B*T too large");
   const int64_t total = (int64_t)B * T;
   if (!(lower_bound >= -5.0f && lower_bound <= 0.0f))
@@ -276,6 +279,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   p.scale = scale;
   p.lower_bound = lower_bound;
   p.H = H;
+  p.Hqk = H_qk;
   p.N = N;
   p.total_tokens = total;
 

@@ -149,19 +149,23 @@ __device__ __forceinline__ void unpack4(u32x2 v, float* f) {
 
 // Where one chunk's producer inputs are: wavefront-uniform bases (chunk start,
 // head) plus 32-bit lane offsets; rows past the chunk end repeat its last row.
+// q and k are read at head hq of their Hqk heads (hq = h with one q/k head
+// per head), g, v and beta at head h.
 struct InAddr {
   const uint16_t *q, *k, *g, *b, *v;
-  uint32_t row, brow, vrow;
+  uint32_t row, qrow, brow, vrow;
 };
 
-__device__ __forceinline__ InAddr in_addr(const Problem& p, long long tok0, int m, int h, int g, int c) {
+__device__ __forceinline__ InAddr in_addr(const Problem& p, long long tok0, int m, int h, int hq, int g, int c) {
   const long long base = (tok0 * p.H + h) * D;
+  const long long qbase = (tok0 * p.Hqk + hq) * D;
   InAddr a;
-  a.q = p.q + base;
-  a.k = p.k + base;
+  a.q = p.q + qbase;
+  a.k = p.k + qbase;
   a.g = p.g + base;
   a.b = p.beta + tok0 * p.H + h;
   a.row = __umul24((uint32_t)min(c, m - 1), (uint32_t)(p.H * D)) + 4 * g;
+  a.qrow = __umul24((uint32_t)min(c, m - 1), (uint32_t)(p.Hqk * D)) + 4 * g;
   a.brow = __umul24((uint32_t)min(c, m - 1), (uint32_t)p.H);
   const int L = threadIdx.x & 63;
   a.v = p.v + base;
@@ -177,9 +181,9 @@ __device__ __forceinline__ void load_vrows(ProdIn& in, const InAddr& a) {
 
 // k-step s of q, k and g: channels 32s+4g+0..3, then 32s+16+4g+0..3
 __device__ __forceinline__ void load_part(ProdIn& in, const InAddr& a, int s) {
-  const uint32_t o = a.row + 32 * s;
-  in.q[s] = cat(*reinterpret_cast<const u32x2*>(a.q + o), *reinterpret_cast<const u32x2*>(a.q + o + 16));
-  in.k[s] = cat(*reinterpret_cast<const u32x2*>(a.k + o), *reinterpret_cast<const u32x2*>(a.k + o + 16));
+  const uint32_t o = a.row + 32 * s, oq = a.qrow + 32 * s;
+  in.q[s] = cat(*reinterpret_cast<const u32x2*>(a.q + oq), *reinterpret_cast<const u32x2*>(a.q + oq + 16));
+  in.k[s] = cat(*reinterpret_cast<const u32x2*>(a.k + oq), *reinterpret_cast<const u32x2*>(a.k + oq + 16));
   in.g[s] = cat(*reinterpret_cast<const u32x2*>(a.g + o), *reinterpret_cast<const u32x2*>(a.g + o + 16));
 }
 
@@ -548,6 +552,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   }
 
   const int H = p.H;
+  const int hq = h / (H / p.Hqk);  // q/k head of this head
   const int wave = threadIdx.x >> 6;
   const int L = threadIdx.x & 63;
   const int g = L >> 4;
@@ -651,7 +656,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     // (always in bounds, loaded and unused)
     auto addr = [&](int lc) {
       const int lcc = lc < ntot ? lc : lc - NPW;
-      return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, g, c);
+      return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, hq, g, c);
     };
     // chunks the block runs: nch, or K once the consumers agreed to stop
     // there; -1 while their vote is incomplete
@@ -717,10 +722,10 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
           if (n < 0) break;
         }
         if (n >= 0 && lc >= n) continue;  // stopped before this chunk
-        if (ROLE == RECUR || lc >= o_from)
-          produce(sm, sm.slot[lc % NSLOT], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, true, L, g, c);
-        else
-          produce(sm, sm.slot[lc % NSLOT], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, false, L, g, c);
+        // Qbar and Aqk are prepared for every chunk, also the first pass's
+        // first chunks, whose output it does not write: one inlined copy of the
+        // preparation keeps the loop's scalar registers from spilling.
+        produce(sm, sm.slot[lc % NSLOT], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, true, L, g, c);
         wg_store(&sm.ready[lc % NSLOT], lc);
       }
     }

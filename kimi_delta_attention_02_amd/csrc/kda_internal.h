@@ -54,7 +54,8 @@ struct Problem {
   int state_kv;  // caller's states are [N][H][K][V] (else [N][H][V][K])
   float scale;
   float lower_bound;
-  int H;
+  int H;    // heads of v, g, beta, out and the states
+  int Hqk;  // heads of q and k (divides H; head h reads q/k head h / (H / Hqk))
   int N;
   int64_t total_tokens;
 };

@@ -94,7 +94,7 @@ def _call(lib, **kw):
     P = ctypes.c_void_p(0x10000)
     a = dict(q=P, k=P, v=P, g=P, beta=P, scale=0.1, out=P, A_log=P, dt_bias=P, lower_bound=-1.0,
              initial_state=None, final_state=None, state_dtype=1, state_layout=0, cu_seqlens=None, num_seqs=0, B=1, T=64, H=2,
-             D=128, workspace=ctypes.c_void_p(0x100000), workspace_bytes=1 << 40, cp_mode=0, seg_chunks=0,
+             H_qk=0, D=128, workspace=ctypes.c_void_p(0x100000), workspace_bytes=1 << 40, cp_mode=0, seg_chunks=0,
              stream=None)
     a.update(kw)
     return lib.kda_fwd(*a.values())
@@ -108,6 +108,8 @@ def _call(lib, **kw):
     (dict(scale=float("inf")), -1, "scale"),
     (dict(state_dtype=7), -1, "state_dtype"),
     (dict(state_layout=2), -1, "state_layout"),
+    (dict(H=4, H_qk=3), -1, "H_qk"),
+    (dict(H=2, H_qk=4), -1, "H_qk"),
     (dict(B=2, cu_seqlens=ctypes.c_void_p(0x2000), num_seqs=2), -1, "B == 1"),
     (dict(cu_seqlens=ctypes.c_void_p(0x2000), num_seqs=0), -1, "num_seqs"),
     (dict(B=2, num_seqs=3), -1, "num_seqs"),
