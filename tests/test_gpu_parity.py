@@ -122,13 +122,18 @@ def test_every_chunk_tail(lb, init_std):
 
 
 # ------------------------------------------------------------------- index tables, bit-exact
-@pytest.mark.parametrize("lens,seg", [([1023, 1025, 1, 16, 4097, 8191, 65537], 64), ([0, 1, 15, 16, 17, 0], 1),
-                                      ([65536] + [1024] * 5, 0), ([65537], 37),
-                                      # past the one-workgroup form's limits (4095 sequences, 16384 rows):
-                                      # the two-launch form
-                                      ([3] * 5000, 0), ([300000], 64)])
-def test_index_tables_bit_exact(lens, seg):
-    w = kda_inputs.custom(seqlens=lens, H=1, seed=28, name="tables", init_std=None)
+@pytest.mark.parametrize("lens,seg,fixed", [
+    ([1023, 1025, 1, 16, 4097, 8191, 65537], 64, False), ([0, 1, 15, 16, 17, 0], 1, False),
+    ([65536] + [1024] * 5, 0, False), ([65537], 37, False),
+    # past the one-workgroup form's limits (4095 sequences, 16384 rows): the two-launch form
+    ([3] * 5000, 0, False), ([300000], 64, False),
+    # fixed length (no cu_seqlens): the closed-form tables
+    ([100] * 3, 2, True), ([4096] * 2, 32, True), ([33] * 7, 0, True), ([512], 16, True)])
+def test_index_tables_bit_exact(lens, seg, fixed):
+    if fixed:
+        w = kda_inputs.custom(B=len(lens), T=lens[0], H=1, seed=28, name="tables fixed", init_std=None)
+    else:
+        w = kda_inputs.custom(seqlens=lens, H=1, seed=28, name="tables", init_std=None)
     x = kda_inputs.make_inputs(w)
     d = dev_inputs(x)
     mode = "force" if seg else "off"
