@@ -206,14 +206,16 @@ __device__ __forceinline__ u32x2 slot_v(const Slot& sl, int g, int col) {
 // ---------------------------------------------------------------- producer
 __device__ __forceinline__ float pick4(f32x4 v, int i) { return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3]; }
 
-// Prepares one chunk into a ring slot.  want_q: also Qbar and Aqk (RECUR).
+// Prepares one chunk into a ring slot: V rows, Kbar, Ktil, Qbar, gamma_C, beta,
+// Aqk and T' (the first pass of a segmented call needs Qbar and Aqk too, since
+// it writes the outputs of every chunk after the checkpoint).
 // a2 = log2(e) exp(A_log); the log decays are kept in base 2 (G2 = G log2 e),
 // so every exponential is one v_exp_f32.
 // Each part of `in` is reloaded from `next` (the producer's next chunk) as soon
 // as it has been used, so the inputs of one chunk are in flight while the
 // previous one is prepared, in the same registers.
 __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, const InAddr& next,
-                                        const Problem& p, int m, float a2, bool want_q, int L, int g, int c) {
+                                        const Problem& p, int m, float a2, int L, int g, int c) {
   const bool ok = c < m;
   {  // V rows into the slot (rows past the chunk end as zeros), then the next
      // chunk's V into the same registers
@@ -288,7 +290,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
       }
       kbh[i] = pack2(Kb[0], Kb[1]);
       split_pair(Kt[0], Kt[1], kth[i], ktl[i]);
-      if (want_q) split_pair(Qb[0], Qb[1], qbh[i], qbl[i]);
+      split_pair(Qb[0], Qb[1], qbh[i], qbl[i]);
       // Ktil, channel-major: ktp[ch][(c/4 + ch/2) % 4] holds tokens 4(c/4)..+3,
       // high parts then low parts
       const int ch = 32 * s + 16 * (i >> 1) + 4 * g + 2 * (i & 1);
@@ -302,7 +304,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
     const u32x4 kth4 = {kth[0], kth[1], kth[2], kth[3]}, ktl4 = {ktl[0], ktl[1], ktl[2], ktl[3]};
     Araw = mfma_k32(kbh4, kth4, Araw);  // D[4g+i][c] += Kbar_{4g+i} . Ktil_c over this k-step
     sl.kbf[s][L] = kbh4;
-    if (want_q) {
+    {
       const u32x4 qbh4 = {qbh[0], qbh[1], qbh[2], qbh[3]}, qbl4 = {qbl[0], qbl[1], qbl[2], qbl[3]};
       AqkT = mfma_k32(kth4, qbh4, AqkT);  // D[4g+i][c] += Ktil_{4g+i} . Qbar_c = Aqk[c][4g+i]
       AqkT = mfma_k32(kth4, qbl4, AqkT);
@@ -323,7 +325,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
     const int row = 4 * g + i;
     sm.Aq[pw][row][4 * (c & 3) + (c >> 2)] = (c < row) ? sm.bt[pw][row] * Araw[i] : 0.f;
   }
-  if (want_q) {
+  {
     f32x4 aq;
 #pragma unroll
     for (int i = 0; i < 4; ++i) aq[i] = (4 * g + i <= c) ? AqkT[i] : 0.f;
@@ -725,7 +727,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
         // Qbar and Aqk are prepared for every chunk, also the first pass's
         // first chunks, whose output it does not write: one inlined copy of the
         // preparation keeps the loop's scalar registers from spilling.
-        produce(sm, sm.slot[lc % NSLOT], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, true, L, g, c);
+        produce(sm, sm.slot[lc % NSLOT], pw, in, addr(lc + NPW), p, chunk_m(lc), a2, L, g, c);
         wg_store(&sm.ready[lc % NSLOT], lc);
       }
     }
