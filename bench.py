@@ -12,10 +12,10 @@ timed at the clock the chip holds under load.  Then W untimed steps, then
 exactly K steps timed with HIP events on the stream the library launches on,
 bracketed by device synchronisation.  Prints ONE JSON line.
 
-Per-stage kernel time comes from the library's own event hook
-(kda_profile_enable / kda_profile_collect, HIP events on the library's
-stream) over a second run of K steps: its events sit between the kernels of
-a step and lengthen it, so the step time comes from the first, uninstrumented
+Per-kernel time comes from the library's own timing hook
+(kda_profile_enable / kda_profile_collect: every kernel launched with a pair
+of HIP events that take its own start and end, on the library's stream) over
+a second run of K steps; the step time comes from the first, uninstrumented
 run.  The roofline object is computed for the chunk kernel (chunk prep +
 recurrence), summed over its launches in a step.  The same call is also
 captured once in a HIP graph and replayed K times; that time and the host
@@ -212,9 +212,8 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     # Timed region 1: the K steps as a caller runs them (events only around
     # whole steps).  Timed region 2: the same K steps again with the library's
-    # per-stage events on, for the stage split and the chunk kernel's own
-    # duration (the roofline); those events sit between the kernels of a step
-    # and lengthen it, so region 2 does not feed ms_per_step.
+    # per-kernel events on, for the stage split and the chunk kernel's own
+    # duration (the roofline); region 2 does not feed ms_per_step.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     evs[0].record(stream)
     h0 = time.perf_counter()

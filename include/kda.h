@@ -160,12 +160,15 @@ typedef enum {
 int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
                               int32_t seg_chunks, int64_t* offs);
 
-/* Per-stage kernel timing for benchmarks.  While enabled on a host thread,
- * every kda_fwd on that thread records a pair of HIP events around each stage
- * on its stream (the events are created by the library on first use and kept
- * for reuse).  kda_profile_collect waits for the recorded events, adds the
- * elapsed milliseconds of each stage into stage_ms[0..n_stages-1] and the
- * number of timed launches of the stage into stage_calls, and forgets them.
+/* Per-kernel timing for benchmarks.  While enabled on a host thread, every
+ * kernel that kda_fwd launches on that thread is launched with a pair of HIP
+ * events (hipExtLaunchKernelGGL) that take the kernel's own start and end
+ * times, with no gap between kernels added (the events are created by the
+ * library on first use and kept for reuse).  Leave it disabled while a call is
+ * captured into a HIP graph.  kda_profile_collect waits for the recorded
+ * events, adds the elapsed milliseconds of each kernel into its stage's
+ * stage_ms[0..n_stages-1] entry and the number of timed launches of the stage
+ * into stage_calls, and forgets them.
  * Stages: KDA_STAGE_INDEX (index scan + table fill), KDA_STAGE_RECUR0 (chunk
  * prep + recurrence of whole sequences / first segments, and the pre-scan of
  * middle segments), KDA_STAGE_MERGE, KDA_STAGE_RECUR1 (chunk prep + recurrence

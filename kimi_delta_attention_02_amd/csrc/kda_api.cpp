@@ -49,7 +49,7 @@ constexpr int kMinSegChunks = 16;   // shortest automatic segment (256 tokens)
 constexpr int kCheckChunks = 4;     // chunks the second pass redoes before comparing with the checkpoint
 constexpr int kSerialChains = 256;  // chains that already fill the chip without splitting
 
-// ---- optional per-stage event timing (benchmarks) ----
+// ---- optional per-kernel event timing (benchmarks) ----
 struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> pool;
@@ -70,27 +70,6 @@ struct Profiler {
   }
 };
 thread_local Profiler g_prof;
-
-struct StageTimer {
-  int stage;
-  hipStream_t s;
-  hipEvent_t a = nullptr;
-  StageTimer(int st, hipStream_t stream) : stage(st), s(stream) {
-    if (!g_prof.on) return;
-    a = g_prof.get();
-    if (a) hipEventRecord(a, s);
-  }
-  ~StageTimer() {
-    if (!a) return;
-    hipEvent_t b = g_prof.get();
-    if (!b) {
-      g_prof.pool.push_back(a);
-      return;
-    }
-    hipEventRecord(b, s);
-    g_prof.recs.push_back({stage, a, b});
-  }
-};
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -163,6 +142,25 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
 }
 
 }  // namespace
+
+namespace kda {
+
+void stage_events(int stage, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (!g_prof.on) return;
+  hipEvent_t a = g_prof.get();
+  if (!a) return;
+  hipEvent_t b = g_prof.get();
+  if (!b) {
+    g_prof.pool.push_back(a);
+    return;
+  }
+  g_prof.recs.push_back({stage, a, b});
+  *start = a;
+  *stop = b;
+}
+
+}  // namespace kda
 
 extern "C" {
 
@@ -285,23 +283,11 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  {
-    StageTimer tm(KDA_STAGE_INDEX, s);
-    e = kda::launch_index(cu_seqlens, N, T, total, lay.seg, mc, ms, t, s);
-  }
-  if (e == hipSuccess) {
-    StageTimer tm(KDA_STAGE_RECUR0, s);
-    e = kda::launch_chunks(p, t, sg, ms, 0, cp, s);
-  }
+  e = kda::launch_index(cu_seqlens, N, T, total, lay.seg, mc, ms, t, s);
+  if (e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 0, cp, s);
   if (cp) {
-    if (e == hipSuccess) {
-      StageTimer tm(KDA_STAGE_MERGE, s);
-      e = kda::launch_merge(p, t, sg, s);
-    }
-    if (e == hipSuccess) {
-      StageTimer tm(KDA_STAGE_RECUR1, s);
-      e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
-    }
+    if (e == hipSuccess) e = kda::launch_merge(p, t, sg, s);
+    if (e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
   }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   return KDA_OK;

@@ -1001,12 +1001,14 @@ hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_
                          hipStream_t st) {
   if (max_segs <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)(max_segs * p.H);
+  hipEvent_t e0, e1;
+  stage_events(phase == 0 ? KDA_STAGE_RECUR0 : KDA_STAGE_RECUR1, &e0, &e1);
   if (!segmented)
-    hipLaunchKernelGGL(kda_chunk_kernel<0>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg);
+    hipExtLaunchKernelGGL(kda_chunk_kernel<0>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
   else if (phase == 0)
-    hipLaunchKernelGGL(kda_chunk_kernel<1>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg);
+    hipExtLaunchKernelGGL(kda_chunk_kernel<1>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
   else
-    hipLaunchKernelGGL(kda_chunk_kernel<2>, dim3(blocks), dim3(NTHREADS), 0, st, p, t, sg);
+    hipExtLaunchKernelGGL(kda_chunk_kernel<2>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
   return hipGetLastError();
 }
 

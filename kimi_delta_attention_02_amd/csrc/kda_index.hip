@@ -367,24 +367,31 @@ hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t
     if (rows < N + 1) rows = N + 1;
     long long blocks = (rows + 255) / 256;
     if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(kda_index_fixed, dim3((unsigned)blocks), dim3(256), 0, st, N, (long long)T_row, seg_chunks,
-                       (long long)max_chunks, (long long)max_segs, t);
+    hipEvent_t e0, e1;
+    stage_events(KDA_STAGE_INDEX, &e0, &e1);
+    hipExtLaunchKernelGGL(kda_index_fixed, dim3((unsigned)blocks), dim3(256), 0, st, e0, e1, 0, N, (long long)T_row,
+                          seg_chunks, (long long)max_chunks, (long long)max_segs, t);
     return hipGetLastError();
   }
   if (N <= FUSED_MAX_N && max_chunks <= FUSED_MAX_ROWS && max_segs <= FUSED_MAX_ROWS) {
-    hipLaunchKernelGGL(kda_index_fused, dim3(1), dim3(SCAN_THREADS), 0, st, cu_seqlens, N, (long long)T_row,
-                       (long long)total_tokens, seg_chunks, (int)max_chunks, (int)max_segs, t);
+    hipEvent_t e0, e1;
+    stage_events(KDA_STAGE_INDEX, &e0, &e1);
+    hipExtLaunchKernelGGL(kda_index_fused, dim3(1), dim3(SCAN_THREADS), 0, st, e0, e1, 0, cu_seqlens, N,
+                          (long long)T_row, (long long)total_tokens, seg_chunks, (int)max_chunks, (int)max_segs, t);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(kda_index_scan, dim3(1), dim3(SCAN_THREADS), 0, st, cu_seqlens, N, (long long)T_row,
-                     (long long)total_tokens, seg_chunks, t);
+  hipEvent_t e0, e1;
+  stage_events(KDA_STAGE_INDEX, &e0, &e1);
+  hipExtLaunchKernelGGL(kda_index_scan, dim3(1), dim3(SCAN_THREADS), 0, st, e0, e1, 0, cu_seqlens, N,
+                        (long long)T_row, (long long)total_tokens, seg_chunks, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = max_chunks > max_segs ? max_chunks : max_segs;
   if (rows > 0) {
     const unsigned blocks = (unsigned)((rows + 255) / 256);
-    hipLaunchKernelGGL(kda_index_fill, dim3(blocks), dim3(256), 0, st, N, seg_chunks, (long long)max_chunks,
-                       (long long)max_segs, t);
+    stage_events(KDA_STAGE_INDEX, &e0, &e1);
+    hipExtLaunchKernelGGL(kda_index_fill, dim3(blocks), dim3(256), 0, st, e0, e1, 0, N, seg_chunks,
+                          (long long)max_chunks, (long long)max_segs, t);
     e = hipGetLastError();
   }
   return e;

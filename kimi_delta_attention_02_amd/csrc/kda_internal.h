@@ -10,6 +10,7 @@
 // permutation.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,6 +79,11 @@ struct Seg {
 };
 
 // ---- launchers (host functions defined next to their kernels) ----
+// Kernel timing for the profiling hook (kda_profile_enable): a launch site asks
+// for an event pair for its stage before each launch.  While profiling is on it
+// gets two events, which hipExtLaunchKernelGGL stamps with the kernel's own
+// start and end; otherwise both stay null and the launch is a plain one.
+void stage_events(int stage, hipEvent_t* start, hipEvent_t* stop);
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
 // producer/consumer chunk kernel: one launch per pass (phase 0: every segment,

@@ -113,8 +113,10 @@ __global__ __launch_bounds__(256) void kda_merge_kernel(Problem p, Tables t, con
 
 hipError_t launch_merge(const Problem& p, Tables t, const Seg& sg, hipStream_t st) {
   if (p.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kda_merge_kernel, dim3((unsigned)p.N, (unsigned)p.H, D / 16), dim3(256), 0, st, p, t,
-                     (const float*)sg.M, (const float*)sg.R, sg.S, (const int32_t*)sg.mnz);
+  hipEvent_t e0, e1;
+  stage_events(KDA_STAGE_MERGE, &e0, &e1);
+  hipExtLaunchKernelGGL(kda_merge_kernel, dim3((unsigned)p.N, (unsigned)p.H, D / 16), dim3(256), 0, st, e0, e1, 0,
+                        p, t, (const float*)sg.M, (const float*)sg.R, sg.S, (const int32_t*)sg.mnz);
   return hipGetLastError();
 }
 
