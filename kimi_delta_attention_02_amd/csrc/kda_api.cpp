@@ -8,16 +8,19 @@
 //      sequences / first segments from the initial state, and of segments >= 1
 //      from a zero state (their transitions M while nonzero, their output
 //      after the first kCheckChunks chunks, a checkpoint of the state there)
-//   [-> merge -> chunk kernel, second pass: the first kCheckChunks chunks of
-//      segments >= 1 from their merged start states, continued to the
-//      segment's end only where the state differs from the checkpoint]
+//   [-> chunk kernel, second pass: each block merges its segment's start state
+//      (S_j = M_{j-1} S_{j-1} + R_{j-1}, walking back only over nonzero M), then
+//      redoes the first kCheckChunks chunks of segments >= 1 from it, continued
+//      to the segment's end only where the state differs from the checkpoint]
 // The bracketed part runs only when the plan splits sequences into segments.
 // It follows the segment scheme on the cuLA PR #106 page (pre-scan, merge,
-// segment recurrence), with two changes: chunk prep is recomputed in each pass
-// from the inputs rather than stored once (a stored prep record is larger than
-// the inputs it is computed from), and the zero-start pass also produces the
+// segment recurrence), with three changes: chunk prep is recomputed in each
+// pass from the inputs rather than stored once (a stored prep record is larger
+// than the inputs it is computed from); the zero-start pass also produces the
 // output, so that the second pass only redoes a segment's first chunks where
-// the start state's influence has decayed to nothing in fp32 by then.
+// the start state's influence has decayed to nothing in fp32 by then; and the
+// merge runs inside the second pass, so a call whose maps M are all zero
+// launches no merge at all.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -285,10 +288,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   hipError_t e;
   e = kda::launch_index(cu_seqlens, N, T, total, lay.seg, mc, ms, t, s);
   if (e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 0, cp, s);
-  if (cp) {
-    if (e == hipSuccess) e = kda::launch_merge(p, t, sg, s);
-    if (e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
-  }
+  if (cp && e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   return KDA_OK;
 }

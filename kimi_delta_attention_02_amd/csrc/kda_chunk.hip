@@ -533,6 +533,35 @@ __device__ __forceinline__ void store_state_kv(const f32x4 (&S)[NT][8], float* d
       }
 }
 
+// Segment merge for this wavefront's column tiles: S <- M S + R, the affine map
+// of one segment (M from a start state, R from zero).  M and R are stored
+// [v][k] like the states (Mt[p][k] = M[k][p]); bit b of nz is set when columns
+// 16b..16b+15 of M (the reduction index) are nonzero, and zero blocks, which
+// the first pass leaves unstored, are skipped.  fp32 products on
+// v_mfma_f32_16x16x4_f32: for output row tile `to`, K slot g of the MFMA for
+// (tt, i) is reduction index p = 16tt + 4g + i, whose S value this lane holds.
+template <int NT>
+__device__ __forceinline__ void apply_map(f32x4 (&S)[NT][8], const float* Mt, const float* Rt, uint32_t nz, int col0,
+                                          int g, int c) {
+  f32x4 acc[NT][8];
+  load_state<NT>(acc, Rt, true, 0, col0, g, c);
+  for (int tt = 0; tt < 8; ++tt) {
+    if (!((nz >> tt) & 1u)) continue;
+#pragma unroll
+    for (int to = 0; to < 8; ++to)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = Mt[(long long)(16 * tt + 4 * g + i) * D + 16 * to + c];
+#pragma unroll
+        for (int jj = 0; jj < NT; ++jj) acc[jj][to] = mfma_f32_k4(a, S[jj][tt][i], acc[jj][to]);
+      }
+  }
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) S[jj][tt] = acc[jj][tt];
+}
+
 }  // namespace
 
 template <int ROLE, int phase>
@@ -578,7 +607,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   const int o_from = ROLE == PRE ? (has_chk ? K : nch) : 0;  // first chunk whose output this pass writes
   const bool may_stop = ROLE == RECUR && phase == 1 && has_chk;
   // a last segment without a checkpoint: the first pass has nothing to hand on
-  // (no merge after it, and the second pass runs it whole)
+  // (no segment after it needs its map, and the second pass runs it whole)
   if (ROLE == PRE && j == ns - 1 && !has_chk) return;
   // The first pass goes on for K chunks into the next segment of the sequence
   // (when that one has a checkpoint) from its own end state, which is the next
@@ -820,23 +849,28 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 
   if (ROLE == RECUR) {
     f32x4 S[TPW][8];
-    {
-      const bool from_seg = (phase == 1);
-      // start state of segment j >= 1: the merged S_j, or R_{j-1} itself when the
-      // previous middle segment's M is all zero (the merge then writes nothing)
-      const float* seg_start = sg.S + seg_base;
-      if (from_seg && j >= 2) {
-        const int32_t* nzf = sg.mnz + ((long long)(sidx - 1) * H + h) * (D / 16);
-        int nz = 0;
+    if (phase == 1) {
+      // Start state of segment j >= 1 (merge): S_j = M_{j-1} S_{j-1} + R_{j-1}.
+      // Walk back to the nearest segment i0 whose start state is stored as is:
+      // segment 1 (S_1, from segment 0's block) or a segment after one whose M
+      // is exactly zero (then S_i0 = R_{i0-1}); then apply the maps of
+      // segments i0 .. j-1 in order.  With every M zero this is one load.
+      auto seg_at = [&](int m) { return ((long long)(sidx - (j - m)) * H + h) * D * D; };
+      auto nz_bits = [&](int m) {
+        const int32_t* f = sg.mnz + ((long long)(sidx - (j - m)) * H + h) * (D / 16);
+        uint32_t b = 0;
 #pragma unroll
-        for (int b = 0; b < D / 16; ++b) nz |= nzf[b];
-        if (nz == 0) seg_start = sg.R + seg_base - (long long)H * D * D;
-      }
-      if (!from_seg && p.state_kv && p.init_state)
-        load_state_kv<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
-      else
-        load_state<TPW>(S, from_seg ? (const void*)seg_start : p.init_state, from_seg || p.state_fp32,
-                        from_seg ? 0 : state_base, col0, g, c);
+        for (int q = 0; q < D / 16; ++q) b |= (f[q] != 0 ? 1u : 0u) << q;
+        return b;
+      };
+      int i0 = j;
+      while (i0 >= 2 && nz_bits(i0 - 1) != 0) --i0;
+      load_state<TPW>(S, i0 == 1 ? sg.S + seg_at(1) : sg.R + seg_at(i0 - 1), true, 0, col0, g, c);
+      for (int m = i0; m < j; ++m) apply_map<TPW>(S, sg.M + seg_at(m), sg.R + seg_at(m), nz_bits(m), col0, g, c);
+    } else if (p.state_kv && p.init_state) {
+      load_state_kv<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
+    } else {
+      load_state<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
     }
     int lc = 0;
     bool ok = true;
@@ -883,9 +917,9 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
           store_state<TPW>(S, dst32, dst16, state_base, col0, g, c);
       }
     } else if (phase == 0) {
-      // segment 0's end state is S_1, the merge's starting point (slot sidx + 1).
-      // The second pass stores nothing here: the next segment's start state
-      // was already merged, and that block may be reading it in this launch.
+      // segment 0's end state is S_1, where the second pass's merge starts
+      // (slot sidx + 1).  The second pass stores nothing here: the next
+      // segment's block may be reading its start state in that launch.
       store_state<TPW>(S, sg.S, nullptr, seg_base + (long long)H * D * D, col0, g, c);
     }
     if (ext > 0 && ok) {  // into the next segment (see above)
@@ -956,7 +990,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     for (; ok && lc < nch && !mzero; ++lc) ok = step_rm(lc, WithOut{});
     for (; ok && lc < nch; ++lc) ok = step_s(lc, Rs, WithOut{});
     store_state<TPW>(Rs, sg.R, nullptr, seg_base, col0, g, c);
-    if (j < ns - 1) {  // the merge reads the transitions of middle segments
+    if (j < ns - 1) {  // the second pass's merge reads the maps of middle segments
       if (!mzero) store_state<TPW>(Ms, sg.M, nullptr, seg_base, col0, g, c);
       if (L == 0) {
 #pragma unroll

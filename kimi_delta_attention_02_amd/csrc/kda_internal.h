@@ -90,7 +90,6 @@ hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t
 // phase 1: the start of segments >= 1 from their merged states)
 hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
                          hipStream_t st);
-hipError_t launch_merge(const Problem& p, Tables t, const Seg& sg, hipStream_t st);
 
 }  // namespace kda
 
