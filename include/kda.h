@@ -135,9 +135,9 @@ typedef enum {
   KDA_WS_SEG_TAB,           /* int32[max_segs][4] (sequence, chunk begin, chunk end, segment in sequence) */
   KDA_WS_SEG_M,             /* fp32 [max_segs][H][128][128] segment transitions M^T (CP only) */
   KDA_WS_SEG_R,             /* fp32 [max_segs][H][128][128] zero-start segment states R^T (CP only) */
-  KDA_WS_SEG_S,             /* fp32 [max_segs][H][128][128] state entering each segment, [v][k] (CP only);
-                               not written for a segment whose predecessor's M is all zero (that
-                               segment starts from the predecessor's R) */
+  KDA_WS_SEG_S,             /* fp32 [max_segs][H][128][128] state entering segment 1 of each sequence
+                               (segment 0's end state), [v][k], in that segment's slot; the second
+                               pass merges the later segments' start states itself (CP only) */
   KDA_WS_SEG_MNZ,           /* int32 [max_segs][H][8]: per 16-column block of a middle segment's M, 1 if
                                any entry is nonzero, 0 if the block underflowed to exactly zero (its M
                                entries are then not stored) (CP only) */
