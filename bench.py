@@ -9,8 +9,10 @@ Untimed calls first run for --preheat-ms of wall time (default 300 ms): the
 GPU's clock rises over the first tens of milliseconds of sustained load (the
 per-step time falls by 13-17 % over them), and the steps are meant to be
 timed at the clock the chip holds under load.  Then W untimed steps, then
-exactly K steps timed with HIP events on the stream the library launches on,
-bracketed by device synchronisation.  Prints ONE JSON line.
+exactly K steps timed with HIP events on the stream the library launches on
+(events made for timing only, without the system-scope fence that would flush
+the L2 after every step), bracketed by device synchronisation.  Prints ONE
+JSON line.
 
 Per-kernel time comes from the library's own timing hook
 (kda_profile_enable / kda_profile_collect: every kernel launched with a pair
@@ -76,6 +78,52 @@ def measured_traffic(workload: str, kernel: str):
         if len(f) == 5 and not line.startswith("#") and f[0] == workload and f[1] == kernel and f[2] == sha:
             return int(f[3]) + int(f[4])
     return None
+
+
+class HipTimingEvents:
+    """HIP events for timing only (hipEventDisableSystemFence), on a given
+    stream.  Reaching one of torch's events runs a system-scope fence, which
+    writes back and invalidates the L2; recorded after every step, that adds a
+    cache flush the calls do not otherwise have.  These come from the HIP
+    runtime already loaded in the process (torch's, found by soname)."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+
+        self.c = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: hipError {rc}")
+
+    def create(self):
+        e = self.c.c_void_p()
+        self._ok(self.lib.hipEventCreateWithFlags(self.c.byref(e), self.FLAGS), "hipEventCreateWithFlags")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        self._ok(self.lib.hipEventRecord(e, self.c.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def elapsed_ms(self, a, b):
+        self._ok(self.lib.hipEventSynchronize(b), "hipEventSynchronize")
+        ms = self.c.c_float()
+        self._ok(self.lib.hipEventElapsedTime(self.c.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.lib.hipEventDestroy(e)
+        self.events = []
 
 
 _CPU_X = None  # inputs shared with the forked baseline workers
@@ -211,17 +259,29 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     # Timed region 1: the K steps as a caller runs them (events only around
-    # whole steps).  Timed region 2: the same K steps again with the library's
-    # per-kernel events on, for the stage split and the chunk kernel's own
-    # duration (the roofline); region 2 does not feed ms_per_step.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    evs[0].record(stream)
+    # whole steps).  Timed region 2, right after it: the same K steps again
+    # with the library's per-kernel events on, for the stage split and the
+    # chunk kernel's own duration (the roofline); region 2 does not feed
+    # ms_per_step.  The graph replays come last: kernels that follow them on
+    # this stack ran measurably slower (72 against 65 us for the first pass
+    # of B=2 T=4096 H=16), so nothing timed for the line comes after them.
+    tev = HipTimingEvents()
+    evs = [tev.create() for _ in range(a.steps + 1)]
+    tev.record(evs[0], stream)
     h0 = time.perf_counter()
     for i in range(a.steps):
         step()
-        evs[i + 1].record(stream)
+        tev.record(evs[i + 1], stream)
     host_us = (time.perf_counter() - h0) / a.steps * 1e6  # submission only: the loop never waits
     torch.cuda.synchronize()
+    total_ms = tev.elapsed_ms(evs[0], evs[-1])
+    per = sorted(tev.elapsed_ms(evs[i], evs[i + 1]) for i in range(a.steps))
+    kda.profile_enable(True)
+    for i in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    kda.profile_enable(False)
+    stages = kda.profile_collect()
     # Timed region 3: the same call captured once in a HIP graph and replayed K
     # times (the call allocates nothing and never synchronises, so it can be
     # captured); reported beside the plain calls, not as the value.
@@ -229,24 +289,17 @@ def main() -> int:
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
-    gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    gev[0].record(stream)
+    gev = [tev.create() for _ in range(2)]
+    tev.record(gev[0], stream)
     h0 = time.perf_counter()
     for i in range(a.steps):
         graph.replay()
     graph_host_us = (time.perf_counter() - h0) / a.steps * 1e6
-    gev[1].record(stream)
+    tev.record(gev[1], stream)
     torch.cuda.synchronize()
-    graph_ms = gev[0].elapsed_time(gev[1]) / a.steps
+    graph_ms = tev.elapsed_ms(gev[0], gev[1]) / a.steps
+    tev.close()
     del graph
-    kda.profile_enable(True)
-    for i in range(a.steps):
-        step()
-    torch.cuda.synchronize()
-    kda.profile_enable(False)
-    stages = kda.profile_collect()
-    total_ms = evs[0].elapsed_time(evs[-1])
-    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
     q1, q3 = len(per) // 4, len(per) - len(per) // 4
     iqr_mean = float(np.mean(per[q1:q3])) if q3 > q1 else float(np.mean(per))
     ms = total_ms / a.steps

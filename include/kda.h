@@ -163,16 +163,19 @@ int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t n
 /* Per-kernel timing for benchmarks.  While enabled on a host thread, every
  * kernel that kda_fwd launches on that thread is launched with a pair of HIP
  * events (hipExtLaunchKernelGGL) that take the kernel's own start and end
- * times, with no gap between kernels added (the events are created by the
- * library on first use and kept for reuse).  Leave it disabled while a call is
- * captured into a HIP graph.  kda_profile_collect waits for the recorded
- * events, adds the elapsed milliseconds of each kernel into its stage's
- * stage_ms[0..n_stages-1] entry and the number of timed launches of the stage
- * into stage_calls, and forgets them.
- * Stages: KDA_STAGE_INDEX (index scan + table fill), KDA_STAGE_RECUR0 (chunk
- * prep + recurrence of whole sequences / first segments, and the pre-scan of
- * middle segments), KDA_STAGE_MERGE, KDA_STAGE_RECUR1 (chunk prep + recurrence
- * of segments >= 1).  Returns KDA_OK or KDA_ERR_HIP. */
+ * times, with no gap between kernels added.  The events are created by the
+ * library on first use, without the system-scope fence (which would write
+ * back and invalidate the L2 at the event and lengthen the kernel it times),
+ * and kept for reuse.  Leave it disabled while a call is captured into a HIP
+ * graph.  kda_profile_collect waits for the recorded events, adds the elapsed
+ * milliseconds of each kernel into its stage's stage_ms[0..n_stages-1] entry
+ * and the number of timed launches of the stage into stage_calls, and forgets
+ * them.
+ * Stages: KDA_STAGE_INDEX (index tables), KDA_STAGE_RECUR0 (chunk prep +
+ * recurrence of whole sequences / first segments, and the pre-scan of
+ * segments >= 1), KDA_STAGE_MERGE (no kernel reports it: the merge runs at
+ * the start of the second pass), KDA_STAGE_RECUR1 (merge + chunk prep +
+ * recurrence of segments >= 1).  Returns KDA_OK or KDA_ERR_HIP. */
 typedef enum {
   KDA_STAGE_INDEX = 0,
   KDA_STAGE_RECUR0,

@@ -67,8 +67,10 @@ struct Profiler {
       pool.pop_back();
       return e;
     }
+    // timing only: no system-scope fence (an L2 write-back and invalidate)
+    // when the event is reached, which would lengthen the kernel it times
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
   }
 };
