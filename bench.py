@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg2] [--cp auto]
 
 One step = one kda_fwd call (index tables, chunk prep fused with the
-recurrence and, when the plan splits sequences, pre-scan + merge + segment
-recurrence) over one batch of seeded synthetic inputs already resident in HBM.
+recurrence and, when the plan splits sequences, a second pass that merges each
+segment's start state and redoes its first chunks where needed) over one batch of seeded synthetic inputs already resident in HBM.
 Untimed calls first run for --preheat-ms of wall time (default 300 ms): the
 GPU's clock rises over the first tens of milliseconds of sustained load (the
 per-step time falls by 13-17 % over them), and the steps are meant to be
@@ -316,8 +316,8 @@ def main() -> int:
     # token-head's output is written by exactly one of those launches, so the
     # algorithmic work of a step (1282 B and 6 D^2 + 10 C D flops per
     # token-head, plus the state read and write) is set against the summed
-    # duration of the chunk-kernel launches of a step.  Pre-scan, merge and
-    # workspace traffic are overhead and earn nothing.
+    # duration of the chunk-kernel launches of a step.  The index tables and
+    # the segment hand-off traffic are overhead and earn nothing.
     chunk_stages = [n for n in ("recur0", "recur1") if stages.get(n, (0.0, 0))[1]]
     chunk_ms = sum(stages[n][0] for n in chunk_stages) / a.steps
     launches = sum(stages[n][1] for n in chunk_stages) / a.steps

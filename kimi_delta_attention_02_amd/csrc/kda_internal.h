@@ -63,7 +63,8 @@ struct Problem {
 
 // Segment buffers of a segmented call (all null when serial), [segment][head][v][k] fp32:
 //   M, R : transition and zero-start state of segments >= 1 (first pass);
-//   S    : merged state entering a segment;
+//   S    : state entering segment 1 of each sequence (segment 0's end state);
+//          the second pass merges the later start states itself;
 //   chk  : R after the first chk_chunks chunks of segments >= 1 (first pass);
 //   fix  : the state after a segment's first chk_chunks chunks as the first
 //          pass's block of the previous segment reached it (first pass);
@@ -87,7 +88,7 @@ void stage_events(int stage, hipEvent_t* start, hipEvent_t* stop);
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
 // producer/consumer chunk kernel: one launch per pass (phase 0: every segment,
-// phase 1: the start of segments >= 1 from their merged states)
+// phase 1: segments >= 1 from their start states, merged in the same launch)
 hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
                          hipStream_t st);
 
