@@ -51,9 +51,27 @@ BYTES_OUT = 2 * D  # out bf16
 FLOPS_PATH = 6 * D * D + 10 * C * D  # 3 chunk GEMMs of 2*16*128*128 per 16 tokens + five 16x16x128 products
 
 
+def _code_only(text: str) -> str:
+    """C/C++/HIP source without its comments and blank space, so that editing
+    a comment does not change what counts as the kernel's source.  String and
+    character literals are kept as they are."""
+    import re
+
+    tok = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
+
+    def keep(m):
+        t = m.group(0)
+        if t.startswith("//") or t.startswith("/*") or t.isspace():
+            return " "
+        return t
+
+    return " ".join(tok.sub(keep, text).split())
+
+
 def kernel_source_sha() -> str:
-    """Short hash of the HIP sources, to tell whether committed counter data
-    still describes the kernels being run."""
+    """Short hash of the HIP sources' code (comments and blank space
+    removed), to tell whether committed counter data still describes the
+    kernels being run."""
     import glob
     import hashlib
 
@@ -61,7 +79,7 @@ def kernel_source_sha() -> str:
     csrc = os.path.join(ROOT, "kimi_delta_attention_02_amd", "csrc")
     for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
         h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+        h.update(_code_only(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
