@@ -562,6 +562,64 @@ __device__ __forceinline__ void apply_map(f32x4 (&S)[NT][8], const float* Mt, co
     for (int tt = 0; tt < 8; ++tt) S[jj][tt] = acc[jj][tt];
 }
 
+// Whole-block work on one 128x128 fp32 state: thread x takes 16-byte pieces
+// x + NTHREADS r, r < PIECES, and issues all its loads before using any, so
+// the block waits for one memory round trip rather than one per piece.
+constexpr int PIECES = (D * D / 4 + NTHREADS - 1) / NTHREADS;
+
+// Bitwise equality of two states (every thread of the block calls it).
+__device__ __forceinline__ bool states_equal(const float* a, const float* b) {
+  const u32x4* x = reinterpret_cast<const u32x4*>(a);
+  const u32x4* y = reinterpret_cast<const u32x4*>(b);
+  u32x4 va[PIECES], vb[PIECES];
+#pragma unroll
+  for (int r = 0; r < PIECES; ++r) {
+    const int i = threadIdx.x + NTHREADS * r;
+    const bool in = i < D * D / 4;
+    va[r] = in ? x[i] : u32x4{0u, 0u, 0u, 0u};
+    vb[r] = in ? y[i] : u32x4{0u, 0u, 0u, 0u};
+  }
+  uint32_t diff = 0;
+#pragma unroll
+  for (int r = 0; r < PIECES; ++r) {
+    const u32x4 d = va[r] ^ vb[r];
+    diff |= d.x | d.y | d.z | d.w;
+  }
+  return !__syncthreads_or(diff != 0u);
+}
+
+// A segment's R as the caller's final state (its dtype and layout), by the
+// whole block: used when the last segment is decided at its checkpoint, so
+// that its end state is the zero-start state R bit for bit.
+__device__ __forceinline__ void copy_final(const Problem& p, const float* R, long long state_base) {
+  const f32x4* r = reinterpret_cast<const f32x4*>(R);
+  f32x4 v[PIECES];
+#pragma unroll
+  for (int q = 0; q < PIECES; ++q) {
+    const int i = threadIdx.x + NTHREADS * q;
+    v[q] = i < D * D / 4 ? r[i] : zero4();
+  }
+#pragma unroll
+  for (int q = 0; q < PIECES; ++q) {
+    const int i = threadIdx.x + NTHREADS * q;  // (v, k) = (4i / D, 4i % D + 0..3)
+    if (i >= D * D / 4) continue;
+    if (p.state_kv) {
+      const long long o = state_base + (long long)(4 * i % D) * D + 4 * i / D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (p.state_fp32)
+          static_cast<float*>(p.final_state)[o + e * D] = v[q][e];
+        else
+          static_cast<uint16_t*>(p.final_state)[o + e * D] = (uint16_t)(pack2(v[q][e], 0.f) & 0xFFFFu);
+      }
+    } else if (p.state_fp32) {
+      reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + state_base)[i] = v[q];
+    } else {
+      reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + state_base)[i] = pack4(v[q]);
+    }
+  }
+}
+
 }  // namespace
 
 template <int ROLE, int phase>
@@ -638,35 +696,9 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       from_r = nz == 0;
     }
     if (from_r) {
-      const u32x4* fa = reinterpret_cast<const u32x4*>(sg.fix + seg_base);
-      const u32x4* ch = reinterpret_cast<const u32x4*>(sg.chk + seg_base);
-      uint32_t diff = 0;
-      for (int i = threadIdx.x; i < D * D / 4; i += NTHREADS) {
-        const u32x4 x = fa[i] ^ ch[i];
-        diff |= x.x | x.y | x.z | x.w;
-      }
-      if (!__syncthreads_or(diff != 0u)) {
+      if (states_equal(sg.fix + seg_base, sg.chk + seg_base)) {
         if (threadIdx.x == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
-        if (j == ns - 1 && p.final_state) {  // the end state is this segment's R
-          const f32x4* r = reinterpret_cast<const f32x4*>(sg.R + seg_base);
-          for (int i = threadIdx.x; i < D * D / 4; i += NTHREADS) {
-            const f32x4 v = r[i];  // (v, k) = (4i / D, 4i % D + 0..3)
-            if (p.state_kv) {
-              const long long o = state_base + (long long)(4 * i % D) * D + 4 * i / D;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (p.state_fp32)
-                  static_cast<float*>(p.final_state)[o + e * D] = v[e];
-                else
-                  static_cast<uint16_t*>(p.final_state)[o + e * D] = (uint16_t)(pack2(v[e], 0.f) & 0xFFFFu);
-              }
-            } else if (p.state_fp32) {
-              reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + state_base)[i] = v;
-            } else {
-              reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + state_base)[i] = pack4(v);
-            }
-          }
-        }
+        if (j == ns - 1 && p.final_state) copy_final(p, sg.R + seg_base, state_base);  // the end state is R
         return;
       }
     }
