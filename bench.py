@@ -83,19 +83,23 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per dispatch of one kernel from the committed rocprofv3 counter
-    runs (profiles/pmc_traffic.txt), or None when they were taken on other
-    kernel sources or another workload."""
+def measured_traffic(workload: str, kernel_prefix: str = "kda_chunk_kernel"):
+    """HBM bytes (read + write) of one call's launches of the chunk kernel,
+    whichever variant ran, from the committed rocprofv3 counter runs
+    (profiles/pmc_traffic.txt, one row per kernel and dispatch), or None when
+    they were taken on other kernel sources or another workload."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
     if not os.path.exists(path):
         return None
     sha = kernel_source_sha()
+    total, found = 0, False
     for line in open(path):
         f = line.split()
-        if len(f) == 5 and not line.startswith("#") and f[0] == workload and f[1] == kernel and f[2] == sha:
-            return int(f[3]) + int(f[4])
-    return None
+        if len(f) == 5 and not line.startswith("#") and f[0] == workload and f[1].startswith(kernel_prefix) \
+                and f[2] == sha:
+            total += int(f[3]) + int(f[4])
+            found = True
+    return total if found else None
 
 
 class HipTimingEvents:
@@ -350,9 +354,7 @@ def main() -> int:
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfl / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    kernels = ["kda_chunk_kernel<1>", "kda_chunk_kernel<2>"] if seg > 0 else ["kda_chunk_kernel<0>"]
-    per_launch = [measured_traffic(w.name, k) for k in kernels]
-    roof["traffic"] = None if any(t is None for t in per_launch) else sum(per_launch)
+    roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "kda_chunk_kernel"
     roof["launches_per_step"] = launches
     roof["kernel_ms_per_step"] = round(chunk_ms, 4)

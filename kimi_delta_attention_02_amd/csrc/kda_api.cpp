@@ -51,6 +51,7 @@ constexpr int kTargetUnits = 256;   // (segment, head) units the automatic plan 
 constexpr int kMinSegChunks = 16;   // shortest automatic segment (256 tokens)
 constexpr int kCheckChunks = 4;     // chunks the second pass redoes before comparing with the checkpoint
 constexpr int kSerialChains = 256;  // chains that already fill the chip without splitting
+constexpr int kWideMinChunks = 128; // units at least this long (on average) run the 4-consumer kernel
 
 // ---- optional per-kernel event timing (benchmarks) ----
 struct Profiler {
@@ -289,7 +290,15 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   e = kda::launch_index(cu_seqlens, N, T, total, lay.seg, mc, ms, t, s);
-  if (e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 0, cp, s);
+  // Long units run their first (or only) pass with 4 consumer wavefronts of two
+  // state tiles each, short ones with 8 of one tile (measured: 2-3 % faster
+  // at 256-512 chunks per unit, 4 % slower at 36).  The second pass keeps 8:
+  // it usually only compares, and where it redoes chunks the 4-consumer
+  // kernel would spill.  Both give the same bits.
+  const int64_t unit_chunks = lay.seg > 0 ? lay.seg : (N > 0 ? mc / N : 0);
+  if (e == hipSuccess)
+    e = unit_chunks >= kWideMinChunks ? kda::launch_chunks_c4(p, t, sg, ms, 0, cp, s)
+                                      : kda::launch_chunks(p, t, sg, ms, 0, cp, s);
   if (cp && e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   return KDA_OK;

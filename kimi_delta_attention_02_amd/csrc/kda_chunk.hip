@@ -53,8 +53,17 @@ namespace {
 
 enum Role { RECUR = 0, PRE = 1 };
 
+// Consumer wavefronts: 8, one 16-column state tile each (kda_chunk_kernel).
+// The file is also built with KDA_CONSUMERS=4, two tiles each, into
+// kda_chunk_kernel_c4: a consumer then shares its per-chunk operand loads,
+// waits and loop overhead between two tiles, which is faster on long units
+// and slower on short ones.  Each state column goes through the same
+// instructions in both, so they give the same bits.
+#ifndef KDA_CONSUMERS
+#define KDA_CONSUMERS 8
+#endif
 constexpr int NPW = 4;                  // producer wavefronts
-constexpr int NCW = 8;                  // consumer wavefronts
+constexpr int NCW = KDA_CONSUMERS;      // consumer wavefronts
 constexpr int TPW = (D / 16) / NCW;     // 16-column state tiles per consumer wavefront
 constexpr int NTHREADS = 64 * (NPW + NCW);
 constexpr int NSLOT = 6;
@@ -1046,8 +1055,18 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 // MODE 1: first pass of a segmented call: segment 0 of each sequence from the
 // initial state, the others from a zero state.
 // MODE 2: second pass of a segmented call: segments >= 1 from their start states.
+#if KDA_CONSUMERS == 8
+#define KDA_CHUNK_KERNEL kda_chunk_kernel
+#define KDA_LAUNCH_CHUNKS launch_chunks
+#elif KDA_CONSUMERS == 4
+#define KDA_CHUNK_KERNEL kda_chunk_kernel_c4
+#define KDA_LAUNCH_CHUNKS launch_chunks_c4
+#else
+#error "KDA_CONSUMERS must be 8 or 4"
+#endif
+
 template <int MODE>
-__global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t, Seg sg) {
+__global__ __launch_bounds__(NTHREADS) void KDA_CHUNK_KERNEL(Problem p, Tables t, Seg sg) {
   __shared__ Smem sm;
   const int k = (int)blockIdx.x / p.H;
   const int h = (int)blockIdx.x - k * p.H;
@@ -1063,18 +1082,20 @@ __global__ __launch_bounds__(NTHREADS) void kda_chunk_kernel(Problem p, Tables t
     chunk_body<PRE, 0>(sm, p, t, sg, urow, h);
 }
 
-hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
-                         hipStream_t st) {
+hipError_t KDA_LAUNCH_CHUNKS(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
+                             hipStream_t st) {
   if (max_segs <= 0) return hipSuccess;
+  if (segmented && phase != 0 && KDA_CONSUMERS != 8) return hipErrorInvalidValue;  // second pass: 8 consumers only
   const unsigned blocks = (unsigned)(max_segs * p.H);
   hipEvent_t e0, e1;
   stage_events(phase == 0 ? KDA_STAGE_RECUR0 : KDA_STAGE_RECUR1, &e0, &e1);
   if (!segmented)
-    hipExtLaunchKernelGGL(kda_chunk_kernel<0>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
+    hipExtLaunchKernelGGL(KDA_CHUNK_KERNEL<0>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
   else if (phase == 0)
-    hipExtLaunchKernelGGL(kda_chunk_kernel<1>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
+    hipExtLaunchKernelGGL(KDA_CHUNK_KERNEL<1>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
   else
-    hipExtLaunchKernelGGL(kda_chunk_kernel<2>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p, t, sg);
+    hipExtLaunchKernelGGL(KDA_CHUNK_KERNEL<KDA_CONSUMERS == 8 ? 2 : 1>, dim3(blocks), dim3(NTHREADS), 0, st, e0, e1, 0, p,
+                          t, sg);
   return hipGetLastError();
 }
 

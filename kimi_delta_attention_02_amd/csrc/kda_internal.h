@@ -91,6 +91,9 @@ hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t
 // phase 1: segments >= 1 from their start states, merged in the same launch)
 hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
                          hipStream_t st);
+// the same kernel with 4 consumer wavefronts of two state tiles each
+hipError_t launch_chunks_c4(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
+                            hipStream_t st);
 
 }  // namespace kda
 
