@@ -83,23 +83,25 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel_prefix: str = "kda_chunk_kernel"):
-    """HBM bytes (read + write) of one call's launches of the chunk kernel,
-    whichever variant ran, from the committed rocprofv3 counter runs
+def measured_traffic(workload: str, modes):
+    """HBM bytes (read + write) of one call's chunk-kernel launches, one per
+    mode in `modes` (0 serial; 1 and 2 the two passes of a segmented plan),
+    whichever consumer variant ran, from the committed rocprofv3 counter runs
     (profiles/pmc_traffic.txt, one row per kernel and dispatch), or None when
-    they were taken on other kernel sources or another workload."""
+    they were taken on other kernel sources, another workload or another plan."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
     if not os.path.exists(path):
         return None
     sha = kernel_source_sha()
-    total, found = 0, False
+    rows = {}
     for line in open(path):
         f = line.split()
-        if len(f) == 5 and not line.startswith("#") and f[0] == workload and f[1].startswith(kernel_prefix) \
-                and f[2] == sha:
-            total += int(f[3]) + int(f[4])
-            found = True
-    return total if found else None
+        if len(f) == 5 and not line.startswith("#") and f[0] == workload and f[2] == sha \
+                and f[1].startswith("kda_chunk_kernel") and f[1].endswith(">"):
+            rows[f[1][f[1].index("<") + 1:-1]] = int(f[3]) + int(f[4])
+    if any(str(m) not in rows for m in modes):
+        return None
+    return sum(rows[str(m)] for m in modes)
 
 
 class HipTimingEvents:
@@ -354,7 +356,7 @@ def main() -> int:
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfl / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof["traffic"] = measured_traffic(w.name)
+    roof["traffic"] = measured_traffic(w.name, (1, 2) if seg > 0 else (0,))
     roof["kernel"] = "kda_chunk_kernel"
     roof["launches_per_step"] = launches
     roof["kernel_ms_per_step"] = round(chunk_ms, 4)
