@@ -3,18 +3,19 @@
 // workgroup, with the prepared operands handed from producer to consumer
 // wavefronts through an LDS ring (no HBM hand-off).
 //
-// Workgroup = 12 wavefronts (3 per SIMD) for one (segment, head):
+// Workgroup = 12 wavefronts (3 per SIMD) for one (segment, head), or 8 in the
+// build with 4 consumers:
 //   producers 0..3  : wavefront p prepares chunks p, p+4, p+8, ... of the
 //                     segment, each one alone (lane (g, c) = token c with key
 //                     channels {32s+4g+0..3, 32s+16+4g+0..3}, s = 0..3, the
 //                     consumers' own operand order), into ring slot chunk % 6
-//   consumers 4..11 : wavefront 4+w walks the chunks in order and applies them
-//                     to value columns 16w..16w+15 of the state, held in MFMA
-//                     accumulators (first pass of a segment >= 1: the
-//                     zero-start state R, plus the transition M while it is
-//                     nonzero).
+//   consumers       : wavefront 4+w walks the chunks in order and applies them
+//                     to value columns 16w..16w+15 (two such tiles with 4
+//                     consumers) of the state, held in MFMA accumulators
+//                     (first pass of a segment >= 1: the zero-start state R,
+//                     plus the transition M while it is nonzero).
 // V goes through the slot as whole rows (the producer loads 256-byte token rows
-// with the chunk's other inputs); each consumer reads its 16-column slice and
+// with the chunk's other inputs); each consumer reads its column slice and
 // overwrites it with its slice of the output, and the producer that next reuses
 // the slot writes the output rows out whole, so HBM sees full rows both ways.
 // Producers and consumers meet at per-slot flags in LDS (ready: the chunk a
