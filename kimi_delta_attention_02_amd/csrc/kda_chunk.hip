@@ -98,6 +98,7 @@ struct Smem {
   float adt[D];         // log2(e) exp(A_log) dt_bias of the head
   int ready[NSLOT];
   int done[NSLOT][NCW];
+  int go;    // producers allowed to issue their first loads (staggered start)
   int vote;  // second pass at the checkpoint: +1 per consumer whose columns match, +0x100 per mismatch
 };
 
@@ -577,57 +578,70 @@ __device__ __forceinline__ void apply_map(f32x4 (&S)[NT][8], const float* Mt, co
 // the block waits for one memory round trip rather than one per piece.
 constexpr int PIECES = (D * D / 4 + NTHREADS - 1) / NTHREADS;
 
-// Bitwise equality of two states (every thread of the block calls it).
-__device__ __forceinline__ bool states_equal(const float* a, const float* b) {
-  const u32x4* x = reinterpret_cast<const u32x4*>(a);
-  const u32x4* y = reinterpret_cast<const u32x4*>(b);
-  u32x4 va[PIECES], vb[PIECES];
+// A segment's R as the caller's final state (its dtype and layout): piece i
+// of the state, (v, k) = (4i / D, 4i % D + 0..3).
+__device__ __forceinline__ void store_final_piece(const Problem& p, long long state_base, int i, f32x4 v) {
+  if (p.state_kv) {
+    const long long o = state_base + (long long)(4 * i % D) * D + 4 * i / D;
 #pragma unroll
-  for (int r = 0; r < PIECES; ++r) {
-    const int i = threadIdx.x + NTHREADS * r;
-    const bool in = i < D * D / 4;
-    va[r] = in ? x[i] : u32x4{0u, 0u, 0u, 0u};
-    vb[r] = in ? y[i] : u32x4{0u, 0u, 0u, 0u};
+    for (int e = 0; e < 4; ++e) {
+      if (p.state_fp32)
+        static_cast<float*>(p.final_state)[o + e * D] = v[e];
+      else
+        static_cast<uint16_t*>(p.final_state)[o + e * D] = (uint16_t)(pack2(v[e], 0.f) & 0xFFFFu);
+    }
+  } else if (p.state_fp32) {
+    reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + state_base)[i] = v;
+  } else {
+    reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + state_base)[i] = pack4(v);
   }
-  uint32_t diff = 0;
-#pragma unroll
-  for (int r = 0; r < PIECES; ++r) {
-    const u32x4 d = va[r] ^ vb[r];
-    diff |= d.x | d.y | d.z | d.w;
-  }
-  return !__syncthreads_or(diff != 0u);
 }
 
-// A segment's R as the caller's final state (its dtype and layout), by the
-// whole block: used when the last segment is decided at its checkpoint, so
-// that its end state is the zero-start state R bit for bit.
-__device__ __forceinline__ void copy_final(const Problem& p, const float* R, long long state_base) {
-  const f32x4* r = reinterpret_cast<const f32x4*>(R);
-  f32x4 v[PIECES];
+// Second pass, before any chunk (every thread of the block calls it): true if
+// the state the first pass reached after this segment's first K chunks (fix,
+// run from the previous segment's R) equals the segment's checkpoint bit for
+// bit, and that R was the segment's start state: the previous segment is
+// segment 0 (nzf null) or its M is exactly zero (the flags nzf[0..D/16) all
+// zero).  The segment's outputs are then all final; for the sequence's last
+// segment (LAST) the end state is R, written to the caller's final state here.
+// Every load (flags, fix, checkpoint, and R for LAST) is issued before any is
+// used, so the block waits for one memory round trip.
+template <bool LAST>
+__device__ __forceinline__ bool decided_at_checkpoint(const Problem& p, const Seg& sg, const int32_t* nzf,
+                                                      long long seg_base, long long state_base) {
+  const u32x4* x = reinterpret_cast<const u32x4*>(sg.fix + seg_base);
+  const u32x4* y = reinterpret_cast<const u32x4*>(sg.chk + seg_base);
+  const f32x4* r = reinterpret_cast<const f32x4*>(sg.R + seg_base);
+  // Threads past the last piece load (and compare) the last piece again: no
+  // load sits in a branch, whose end would wait for all loads issued before it.
+  u32x4 va[PIECES], vb[PIECES];
+  f32x4 vr[PIECES];
 #pragma unroll
   for (int q = 0; q < PIECES; ++q) {
-    const int i = threadIdx.x + NTHREADS * q;
-    v[q] = i < D * D / 4 ? r[i] : zero4();
+    const int i = min((int)threadIdx.x + NTHREADS * q, D * D / 4 - 1);
+    va[q] = x[i];
+    vb[q] = y[i];
+    if (LAST) vr[q] = r[i];
+  }
+  uint32_t diff = 0;
+  if (nzf) {
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b) diff |= (uint32_t)nzf[b];
   }
 #pragma unroll
   for (int q = 0; q < PIECES; ++q) {
-    const int i = threadIdx.x + NTHREADS * q;  // (v, k) = (4i / D, 4i % D + 0..3)
-    if (i >= D * D / 4) continue;
-    if (p.state_kv) {
-      const long long o = state_base + (long long)(4 * i % D) * D + 4 * i / D;
+    const u32x4 d = va[q] ^ vb[q];
+    diff |= d.x | d.y | d.z | d.w;
+  }
+  if (__syncthreads_or(diff != 0u)) return false;
+  if (LAST) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (p.state_fp32)
-          static_cast<float*>(p.final_state)[o + e * D] = v[q][e];
-        else
-          static_cast<uint16_t*>(p.final_state)[o + e * D] = (uint16_t)(pack2(v[q][e], 0.f) & 0xFFFFu);
-      }
-    } else if (p.state_fp32) {
-      reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + state_base)[i] = v[q];
-    } else {
-      reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + state_base)[i] = pack4(v[q]);
+    for (int q = 0; q < PIECES; ++q) {
+      const int i = threadIdx.x + NTHREADS * q;
+      if (i < D * D / 4) store_final_piece(p, state_base, i, vr[q]);
     }
   }
+  return true;
 }
 
 }  // namespace
@@ -697,20 +711,13 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   // zero; or S_1).  If the state it reached equals the checkpoint bit for bit,
   // every output of the segment is final and the block has nothing to do.
   if (ROLE == RECUR && phase == 1 && has_chk) {
-    bool from_r = true;
-    if (j >= 2) {
-      const int32_t* nzf = sg.mnz + ((long long)(sidx - 1) * H + h) * (D / 16);
-      int nz = 0;
-#pragma unroll
-      for (int b = 0; b < D / 16; ++b) nz |= nzf[b];
-      from_r = nz == 0;
-    }
-    if (from_r) {
-      if (states_equal(sg.fix + seg_base, sg.chk + seg_base)) {
-        if (threadIdx.x == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
-        if (j == ns - 1 && p.final_state) copy_final(p, sg.R + seg_base, state_base);  // the end state is R
-        return;
-      }
+    const int32_t* nzf = j >= 2 ? sg.mnz + ((long long)(sidx - 1) * H + h) * (D / 16) : nullptr;
+    const bool decided = (j == ns - 1 && p.final_state)
+                             ? decided_at_checkpoint<true>(p, sg, nzf, seg_base, state_base)
+                             : decided_at_checkpoint<false>(p, sg, nzf, seg_base, state_base);
+    if (decided) {
+      if (threadIdx.x == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
+      return;
     }
   }
 
@@ -719,6 +726,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   if (threadIdx.x < NSLOT) sm.ready[threadIdx.x] = -1;
   if (threadIdx.x < NSLOT * NCW) sm.done[threadIdx.x / NCW][threadIdx.x % NCW] = -1;
   if (threadIdx.x == 0) sm.vote = 0;
+  if (threadIdx.x == 0) sm.go = 0;
   __syncthreads();
 
   if (wave < NPW) {
@@ -771,7 +779,20 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     // lc it waits until the slot's previous chunk lc - NSLOT is consumed and
     // writes that chunk's output rows; past the last chunk it goes on only to
     // write out the outputs of the last NSLOT chunks.
-    if (pw < ntot) load_prod(in, addr(pw));
+    // Staggered start: producer pw issues its first chunk's loads once those of
+    // producer pw - 1 have returned.  Every block starts at once, and this keeps
+    // the inputs of chunk 0, which the consumers wait for, from queueing behind
+    // those of chunks 1..3.  The wait only orders loads: it is bounded, and
+    // going on after it gives up changes no result.
+    if (pw > 0) {
+      int it = 0;
+      while (wg_load(&sm.go) < pw && ++it < 4096) __builtin_amdgcn_s_sleep(1);
+    }
+    if (pw < ntot) {
+      load_prod(in, addr(pw));
+      asm volatile("" ::"v"(in.v[3]));  // a use of the last load issued: waits for all of them
+    }
+    if (pw + 1 < NPW) wg_store(&sm.go, pw + 1);
     for (int lc = pw; lc < ntot + NSLOT; lc += NPW) {
       const int y = lc - NSLOT;
       if (y >= 0) {

@@ -65,3 +65,47 @@ def test_chunk_kda_matches_fwd_and_final_only():
     o2, f2 = kda.chunk_kda(d["q"], d["k"], d["v"], d["g"], d["beta"], A_log=d["A_log"], dt_bias=d["dt_bias"],
                            lower_bound=x["lower_bound"])
     assert f2 is None and o2.shape == o.shape
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("sdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["vk", "kv"])
+def test_final_state_decided_at_checkpoint(sdt, layout):
+    """Segments of 6 chunks, past the 4-chunk checkpoint, with fast decay
+    (lb = -5): the second pass decides every such segment at its checkpoint, and
+    for the last segment of a sequence (the 480-token one) the final state is
+    then the first pass's zero-start state R, written straight into the caller's
+    dtype and layout.  The 200-token sequence ends in a 1-chunk segment with no
+    checkpoint, which the second pass runs whole.  Output and final state equal
+    the serial call's bits and the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests.gpu_util import check_against_oracle, dev_inputs, read_ws
+
+    w = kda_inputs.custom(seqlens=[480, 96, 200], H=2, lower_bound=-5.0, state_dtype=sdt, seed=43,
+                          name=f"checkpoint final {sdt} {layout}")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    init = d["initial_state"] if layout == "vk" else d["initial_state"].transpose(-1, -2).contiguous()
+    st = torch.float32 if sdt == "fp32" else torch.bfloat16
+
+    def call(cp, seg):
+        final = torch.full((w.N, w.H, 128, 128), float("nan"), dtype=st, device="cuda")
+        ws = torch.empty(kda.get_workspace_size(w.B * w.T, w.H, w.N, cp, seg), dtype=torch.uint8, device="cuda")
+        out = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], A_log=d["A_log"], dt_bias=d["dt_bias"],
+                      lower_bound=x["lower_bound"], workspace=ws, initial_state=init, final_state=final,
+                      cu_seqlens=d["cu_seqlens"], cp_mode=cp, seg_chunks=seg, state_layout=layout)
+        torch.cuda.synchronize()
+        return out, final, ws
+
+    o_ser, f_ser, _ = call("off", 0)
+    o_seg, f_seg, ws = call("force", 6)
+    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, "force", 6)
+    stops = int(read_ws(ws, offs, "counters", 4, np.int32)[3])
+    # checkpointed segments: 4 of the 480-token sequence, 1 of the 200-token one; per head
+    assert stops == 5 * w.H, stops
+    assert torch.equal(o_seg.view(torch.int16), o_ser.view(torch.int16))
+    assert torch.equal(f_seg.view(torch.int16) if sdt == "bf16" else f_seg,
+                       f_ser.view(torch.int16) if sdt == "bf16" else f_ser)
+    f_vk = f_seg if layout == "vk" else f_seg.transpose(-1, -2).contiguous()
+    check_against_oracle(w, x, o_seg, f_vk, final_dtype=sdt)
