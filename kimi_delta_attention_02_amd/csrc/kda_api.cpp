@@ -264,6 +264,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   sg.fix = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_FIX]) : nullptr;
   sg.mnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
   sg.chk_chunks = cp ? kCheckChunks : 0;
+  sg.seg_chunks = cp ? (int)lay.seg : 0;
   const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
   const int64_t ms = lay.off[KDA_WS_MAX_SEGS];
 

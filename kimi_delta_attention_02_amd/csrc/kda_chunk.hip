@@ -646,15 +646,29 @@ __device__ __forceinline__ bool decided_at_checkpoint(const Problem& p, const Se
 
 }  // namespace
 
+// One row of the dispatch table: segment (row of the segment tables), its
+// sequence, its chunk range [cb, ce) in global chunk numbers, its index in the
+// sequence, and the sequence's first token and length.
+struct Unit {
+  int sidx, seq, cb, ce, j, start, len;
+};
+
 template <int ROLE, int phase>
 __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, const Seg& sg,
-                                           const int32_t* urow, int h) {
-  const int sidx = urow[0];
-  const int seq = urow[1];
-  const int cb = urow[2];
-  const int ce = urow[3];
-  const int j = urow[4];
-  const int ns = t.seq_seg_off[seq + 1] - t.seq_seg_off[seq];
+                                           const Unit& u, int h) {
+  const int sidx = u.sidx;
+  const int seq = u.seq;
+  const int cb = u.cb;
+  const int ce = u.ce;
+  const int j = u.j;
+  // the sequence's chunk and segment counts, its first chunk and the next
+  // segment's length follow from its length and the segment length (serial:
+  // one segment per sequence)
+  const int seq_len = u.len;
+  const int seq_nc = (seq_len + C - 1) / C;
+  const int seg_c = sg.seg_chunks;
+  const int ns = seg_c > 0 ? (seq_nc > 0 ? (seq_nc + seg_c - 1) / seg_c : 1) : 1;
+  const int first_chunk = cb - j * seg_c;
   // RECUR, phase 0: segment 0 of every sequence from the initial state;
   // RECUR, phase 1: segments >= 1 from their merged start states;
   // PRE (first pass of a segmented call): segments >= 1 from a zero state.
@@ -671,9 +685,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   const int g = L >> 4;
   const int c = L & 15;
   const int nch = ce - cb;
-  const int first_chunk = t.seq_chunk_off[seq];
-  const long long seq_tok0 = t.seq_start[seq];
-  const int seq_len = t.seq_len[seq];
+  const long long seq_tok0 = u.start;
   auto chunk_m = [&](int lc) { return min(C, seq_len - C * (cb + lc - first_chunk)); };
   auto chunk_tok0 = [&](int lc) { return seq_tok0 + (long long)C * (cb + lc - first_chunk); };
 
@@ -699,7 +711,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   // bit for bit, and then has nothing left to compute.
   int ext = 0;
   if (phase == 0 && K > 0 && j < ns - 1) {
-    const int nn = t.seg_tab[4 * (sidx + 1) + 2] - t.seg_tab[4 * (sidx + 1) + 1];
+    const int nn = min(seg_c, seq_nc - (j + 1) * seg_c);  // the next segment's chunks
     if (nn > K) ext = K;
   }
   const int ntot = nch + ext;  // chunks this block runs
@@ -1092,16 +1104,20 @@ __global__ __launch_bounds__(NTHREADS) void KDA_CHUNK_KERNEL(Problem p, Tables t
   __shared__ Smem sm;
   const int k = (int)blockIdx.x / p.H;
   const int h = (int)blockIdx.x - k * p.H;
-  if (k >= t.counters[CNT_N_SEGS]) return;
-  const int32_t* urow = t.unit_tab + 8 * k;
+  // the whole row in one read (rows past the live units hold -1); the grid
+  // has one row of blocks per table row
+  const int4 r0 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k];
+  const int4 r1 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k + 1];
+  if (r0.x < 0) return;
+  const Unit u{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z};
   if (MODE == 0)
-    chunk_body<RECUR, 0>(sm, p, t, sg, urow, h);
+    chunk_body<RECUR, 0>(sm, p, t, sg, u, h);
   else if (MODE == 2)
-    chunk_body<RECUR, 1>(sm, p, t, sg, urow, h);
-  else if (urow[4] == 0)
-    chunk_body<RECUR, 0>(sm, p, t, sg, urow, h);
+    chunk_body<RECUR, 1>(sm, p, t, sg, u, h);
+  else if (u.j == 0)
+    chunk_body<RECUR, 0>(sm, p, t, sg, u, h);
   else
-    chunk_body<PRE, 0>(sm, p, t, sg, urow, h);
+    chunk_body<PRE, 0>(sm, p, t, sg, u, h);
 }
 
 hipError_t KDA_LAUNCH_CHUNKS(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,

@@ -27,6 +27,10 @@
 //       segment s into the dispatch table unit_tab (full-length segments
 //       first, then the shorter last segments of their sequences, so that the
 //       long units start first).  Rows past the live counts are -1.
+// A unit_tab row is (segment, seq, first chunk, end chunk, segment in seq,
+// sequence start token, sequence length, -1): everything the chunk kernel needs
+// to place its unit, in one 32-byte row, so that its first input loads wait
+// for a single table read.
 #include "kda_internal.h"
 
 namespace kda {
@@ -204,7 +208,7 @@ __device__ __forceinline__ void seg_row(int32_t* row, int sq, int idx, const int
 // the full-length segments in segment order, then the others (a sequence's
 // shorter last segment) in segment order.
 __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32_t* row, const int* soff,
-                                         const int* foff, int n_full) {
+                                         const int* foff, int n_full, int seq_start, int seq_len) {
   const int sq = row[0], j = row[3];
   const int full_here = foff[sq + 1] - foff[sq];
   const int rank = j < full_here ? foff[sq] + j : n_full + (soff[sq] - foff[sq]);
@@ -214,8 +218,8 @@ __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32
   u[2] = row[1];
   u[3] = row[2];
   u[4] = row[3];
-  u[5] = -1;
-  u[6] = -1;
+  u[5] = seq_start;
+  u[6] = seq_len;
   u[7] = -1;
 }
 
@@ -242,7 +246,8 @@ __global__ __launch_bounds__(256) void kda_index_fill(int N, int seg_chunks, lon
       int s = owner_of(t.seq_seg_off, N + 1, (int)idx);
       while (s + 1 <= N && t.seq_seg_off[s + 1] <= (int)idx) ++s;
       seg_row(row, s, (int)idx, t.seq_chunk_off, t.seq_seg_off, seg_chunks);
-      put_unit(t.unit_tab, (int)idx, row, t.seq_seg_off, t.seq_full_off, t.seq_full_off[N]);
+      put_unit(t.unit_tab, (int)idx, row, t.seq_seg_off, t.seq_full_off, t.seq_full_off[N], t.seq_start[s],
+               t.seq_len[s]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) t.unit_tab[8 * idx + k] = -1;
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* _
       if (r < n_segs) {
         while (a + 1 <= N && soff[a + 1] <= r) ++a;
         seg_row(row, a, r, coff, soff, seg_chunks);
-        put_unit(t.unit_tab, r, row, soff, foff, foff[N]);
+        put_unit(t.unit_tab, r, row, soff, foff, foff[N], sst[a], sst[a + 1] - sst[a]);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) t.unit_tab[8 * r + k] = -1;
@@ -348,8 +353,8 @@ __global__ __launch_bounds__(256) void kda_index_fixed(int N, long long T_row, i
       u[2] = row[1];
       u[3] = row[2];
       u[4] = row[3];
-      u[5] = -1;
-      u[6] = -1;
+      u[5] = sq * L;
+      u[6] = L;
       u[7] = -1;
     } else {
 #pragma unroll

@@ -77,6 +77,7 @@ struct Seg {
   float* fix;
   int32_t* mnz;
   int chk_chunks;
+  int seg_chunks;  // segment length in chunks (0: serial, one segment per sequence)
 };
 
 // ---- launchers (host functions defined next to their kernels) ----

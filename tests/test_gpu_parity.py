@@ -156,11 +156,14 @@ def test_index_tables_bit_exact(lens, seg, fixed):
     assert (read_ws(ws, offs, "chunk_tab", 2 * mc, np.int32)[2 * nch:] == -1).all()
     assert (read_ws(ws, offs, "seg_tab", 4 * ms, np.int32)[4 * nsg:] == -1).all()
     # dispatch order: every full-length segment (seg chunks), then the others,
-    # each group in segment order (serial: every sequence counts as full)
+    # each group in segment order (serial: every sequence counts as full); a
+    # row also carries its sequence's first token and length
     st = ref["seg_tab"]
+    starts = np.concatenate([[0], np.cumsum(lens)])
     full = [i for i in range(nsg) if not seg or st[i][2] - st[i][1] == seg]
     rest = [i for i in range(nsg) if seg and st[i][2] - st[i][1] != seg]
-    want = np.array([[i, *st[i], -1, -1, -1] for i in full + rest], dtype=np.int32).reshape(-1, 8)
+    want = np.array([[i, *st[i], starts[st[i][0]], lens[st[i][0]], -1] for i in full + rest],
+                    dtype=np.int32).reshape(-1, 8)
     unit = read_ws(ws, offs, "unit_tab", 8 * ms, np.int32).reshape(-1, 8)
     np.testing.assert_array_equal(unit[:nsg], want)
     assert (unit[nsg:] == -1).all()
