@@ -733,6 +733,19 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     }
   }
 
+  // Producer p prepares chunks p, p + NPW, ...; its inputs are loaded a chunk
+  // ahead into `in`.  Past the last chunk the next-chunk address repeats the
+  // current one (always in bounds, loaded and unused).
+  ProdIn in;
+  auto addr = [&](int lc) {
+    const int lcc = lc < ntot ? lc : lc - NPW;
+    return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, hq, g, c);
+  };
+  // The inputs of chunk 0, which every consumer waits for, are requested
+  // first, so that their latency overlaps that of the gate constants below
+  // and of the workgroup barrier.
+  if (wave == 0 && ntot > 0) load_prod(in, addr(0));
+
   const float a2 = LOG2E * expf(p.A_log[h]);
   if (threadIdx.x < D) sm.adt[threadIdx.x] = a2 * p.dt_bias[h * D + threadIdx.x];
   if (threadIdx.x < NSLOT) sm.ready[threadIdx.x] = -1;
@@ -744,13 +757,6 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   if (wave < NPW) {
     // ======================= producer =======================
     const int pw = wave;
-    ProdIn in;
-    // past the last chunk the next-chunk address repeats the current one
-    // (always in bounds, loaded and unused)
-    auto addr = [&](int lc) {
-      const int lcc = lc < ntot ? lc : lc - NPW;
-      return in_addr(p, chunk_tok0(lcc), chunk_m(lcc), h, hq, g, c);
-    };
     // chunks the block runs: nch, or K once the consumers agreed to stop
     // there; -1 while their vote is incomplete
     auto n_run = [&]() -> int { return may_stop ? vote_chunks(wg_load(&sm.vote), K, nch) : ntot; };
@@ -801,7 +807,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       while (wg_load(&sm.go) < pw && ++it < 4096) __builtin_amdgcn_s_sleep(1);
     }
     if (pw < ntot) {
-      load_prod(in, addr(pw));
+      if (pw > 0) load_prod(in, addr(pw));  // producer 0's are in flight since the start
       asm volatile("" ::"v"(in.v[3]));  // a use of the last load issued: waits for all of them
     }
     if (pw + 1 < NPW) wg_store(&sm.go, pw + 1);
