@@ -123,6 +123,9 @@ def _call(lib, **kw):
     (dict(workspace_bytes=1024), -3, "need"),
     (dict(cp_mode=5), -1, "cp_mode"),
     (dict(seg_chunks=-2), -1, "seg_chunks"),
+    # token offsets and table rows are int32
+    (dict(B=2, T=2 ** 30), -1, "B*T too large"),
+    (dict(T=2 ** 30, H=64, cp_mode=2, seg_chunks=1), -1, "too large for the index tables"),
 ])
 def test_fwd_rejects_before_launch(lib, kw, status, msg):
     st = _call(lib, **kw)
