@@ -146,9 +146,10 @@ typedef enum {
   KDA_WS_SEQ_FULL_OFF,      /* int32[N+1]   prefix sums of the full-length segments per sequence
                                (floor(chunks/seg); 1 per sequence when serial) */
   KDA_WS_UNIT_TAB,          /* int32[max_segs][8] the segments in dispatch order: (segment, sequence,
-                               chunk begin, chunk end, segment in sequence, -1, -1, -1); every
-                               full-length segment first, then the shorter last segments, each group
-                               in segment order (-1 past the live count) */
+                               chunk begin, chunk end, segment in sequence, sequence start token,
+                               sequence length, -1); every full-length segment first, then the
+                               shorter last segments, each group in segment order (all -1 past the
+                               live count) */
   KDA_WS_SEG_FIX,           /* fp32 [max_segs][H][128][128] state after a segment's first 4 chunks as the
                                first pass's block of the previous segment reached it (CP only) */
   KDA_WS_MAX_CHUNKS,        /* (count, not an offset) chunk-table capacity */
