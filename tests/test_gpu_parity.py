@@ -121,6 +121,41 @@ def test_every_chunk_tail(lb, init_std):
     check_against_oracle(w, x, out, final)
 
 
+# The shape of the pages' own benchmark (64 heads, no initial state) on a varlen
+# mix of irregular lengths, serial (64 heads x 4 sequences already fill the
+# chip) and split into 16-chunk segments.
+@pytest.mark.parametrize("cp,seg", [("auto", 0), ("force", 16)])
+def test_sixty_four_heads_no_initial_state(cp, seg):
+    w = kda_inputs.custom(seqlens=[1000, 3000, 37, 2048], H=64, lower_bound=-5.0, init_std=None, seed=71,
+                          name=f"H64 no-init {cp}")
+    _case(w, cp_mode=cp, seg_chunks=seg, heads=[0, 31, 63])
+
+
+# Degenerate inputs: all-zero query or key rows (the norm gives a zero vector, no
+# NaN), beta logits of +-30 (sigmoid 1 and ~1e-13) and gate inputs of +-30 (the
+# log decay saturates at lower_bound or at 0).
+@pytest.mark.parametrize("cp,seg", [("off", 0), ("force", 5)])
+def test_degenerate_rows_and_saturated_gates(cp, seg):
+    w = kda_inputs.custom(seqlens=[300, 77], H=4, lower_bound=-5.0, seed=73, name=f"degenerate {cp}")
+    say(f"case {w.name} seed={w.seed} cp={cp} seg={seg}")
+    x = kda_inputs.make_inputs(w)
+    x = dict(x)
+    for n in ("q", "k", "beta", "g"):
+        x[n] = x[n].copy()
+    pos, neg = np.uint16(0x41F0), np.uint16(0xC1F0)  # bf16 30.0 and -30.0
+    x["q"][0, 5::23] = 0
+    x["k"][0, 11::29] = 0
+    x["q"][0, 150:160, 1] = 0
+    x["k"][0, 150:160, 1] = 0
+    x["beta"][0, 3::17] = pos
+    x["beta"][0, 7::19] = neg
+    x["g"][0, 2::13, :, :40] = pos
+    x["g"][0, 9::31, :, 60:] = neg
+    d = dev_inputs(x)
+    out, final, _ = run_gpu(w, x, d, cp, seg)
+    check_against_oracle(w, x, out, final, final_dtype=w.state_dtype)
+
+
 # ------------------------------------------------------------------- index tables, bit-exact
 @pytest.mark.parametrize("lens,seg,fixed", [
     ([1023, 1025, 1, 16, 4097, 8191, 65537], 64, False), ([0, 1, 15, 16, 17, 0], 1, False),
