@@ -161,6 +161,22 @@ typedef enum {
 int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
                               int32_t seg_chunks, int64_t* offs);
 
+/* Index tables of a fixed-length call, for inspection and tests.  A kda_fwd
+ * call without cu_seqlens launches no index kernel: its chunk-kernel blocks
+ * compute their rows of these tables in closed form (B sequences of T tokens:
+ * sequence i starts at token i*T and has ceil(T/16) chunks) and store only the
+ * counters.  This call writes every table region and the counters of the
+ * layout kda_workspace_offsets gives for (B*T, H, B, cp_mode, seg_chunks), with
+ * the contents the varlen construction gives for B equal lengths ("How
+ * FlashKDA Integrates with CUTLASS", "Variable-Length Sequence Support": a
+ * fixed-length batch read as a varlen one).  It launches one kernel on stream,
+ * asynchronously, and allocates nothing.  The workspace (caller-owned, device)
+ * must hold at least kda_get_workspace_size bytes and be KDA_WORKSPACE_ALIGN
+ * aligned; the segment buffers are untouched.  Errors: KDA_ERR_INVALID_ARG,
+ * KDA_ERR_WORKSPACE_TOO_SMALL (nothing launched), KDA_ERR_HIP. */
+int32_t kda_write_fixed_tables(int32_t B, int64_t T, int32_t H, int32_t cp_mode, int32_t seg_chunks,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Per-kernel timing for benchmarks.  While enabled on a host thread, every
  * kernel that kda_fwd launches on that thread is launched with a pair of HIP
  * events (hipExtLaunchKernelGGL) that take the kernel's own start and end

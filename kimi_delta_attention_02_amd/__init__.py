@@ -83,6 +83,8 @@ def load_library():
     lib.kda_get_workspace_size.restype = sz
     lib.kda_workspace_offsets.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
     lib.kda_workspace_offsets.restype = i32
+    lib.kda_write_fixed_tables.argtypes = [i32, i64, i32, i32, i32, vp, sz, vp]
+    lib.kda_write_fixed_tables.restype = i32
     lib.kda_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, vp, i32, i32, vp, i32, i32, i64, i32, i32,
                             i32, vp, sz, i32, i32, vp]
     lib.kda_fwd.restype = i32
@@ -146,6 +148,21 @@ def workspace_offsets(total_tokens: int, num_heads: int, num_seqs: int = 1, cp_m
     if st != 0:
         _raise(st)
     return dict(zip(WS_FIELDS, [int(x) for x in arr]))
+
+
+def write_fixed_tables(B: int, T: int, H: int, cp_mode, seg_chunks: int, workspace) -> None:
+    """Write the index tables of a fixed-length call (B sequences of T tokens)
+    into workspace, on the current stream; kda_fwd computes them in closed
+    form without storing them (for inspection and tests)."""
+    import torch
+
+    _check(workspace, "workspace", torch.uint8)
+    with torch.cuda.device_of(workspace):
+        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+        st = load_library().kda_write_fixed_tables(int(B), int(T), int(H), _cp(cp_mode), int(seg_chunks),
+                                                   workspace.data_ptr(), workspace.numel(), stream)
+    if st != 0:
+        _raise(st)
 
 
 STAGES = ["index", "recur0", "merge", "recur1"]

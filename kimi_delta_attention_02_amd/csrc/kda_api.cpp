@@ -3,7 +3,8 @@
 //
 // Launch sequence of one kda_fwd call, all on the caller's stream, with no
 // host synchronisation, allocation or device-to-host copy:
-//   index scan + table fill
+//   index scan + table fill (varlen; a fixed-length call has none: the first
+//   chunk-kernel launch writes its tables, whose closed form every block uses)
 //   -> chunk kernel, first pass: chunk prep fused with the recurrence of whole
 //      sequences / first segments from the initial state, and of segments >= 1
 //      from a zero state (their transitions M while nonzero, their output
@@ -168,6 +169,26 @@ void stage_events(int stage, hipEvent_t* start, hipEvent_t* stop) {
 
 }  // namespace kda
 
+// Tables carved from a workspace of layout lay; fixed_T >= 0 marks a
+// fixed-length call of that many tokens per sequence, -1 a varlen one.
+kda::Tables carve_tables(uint8_t* ws, const Layout& lay, int64_t fixed_T) {
+  kda::Tables t;
+  t.counters = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_COUNTERS]);
+  t.seq_start = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_START]);
+  t.seq_len = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_LEN]);
+  t.seq_chunk_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_CHUNK_OFF]);
+  t.seq_seg_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_SEG_OFF]);
+  t.chunk_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_CHUNK_TAB]);
+  t.seg_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_TAB]);
+  t.seq_full_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_FULL_OFF]);
+  t.unit_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_UNIT_TAB]);
+  t.fixed = fixed_T >= 0;
+  t.fixed_T = fixed_T >= 0 ? (int)fixed_T : 0;
+  t.max_chunks = lay.off[KDA_WS_MAX_CHUNKS];
+  t.max_segs = lay.off[KDA_WS_MAX_SEGS];
+  return t;
+}
+
 extern "C" {
 
 int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
@@ -189,6 +210,26 @@ int32_t kda_workspace_offsets(int64_t total_tokens, int32_t num_heads, int32_t n
   const int32_t st = layout(total_tokens, num_heads, num_seqs, cp_mode, seg_chunks, &lay);
   if (st != KDA_OK) return st;
   std::memcpy(offs, lay.off, sizeof(lay.off));
+  return KDA_OK;
+}
+
+int32_t kda_write_fixed_tables(int32_t B, int64_t T, int32_t H, int32_t cp_mode, int32_t seg_chunks, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B < 1 || T < 0) return fail(KDA_ERR_INVALID_ARG, "B=%d must be >= 1 and T=%lld >= 0", B, (long long)T);
+  if (T > 0 && B > kMaxTokens / T) return fail(KDA_ERR_INVALID_ARG, "B*T too large");
+  Layout lay;
+  const int32_t st = layout((int64_t)B * T, H, B, cp_mode, seg_chunks, &lay);
+  if (st != KDA_OK) return st;
+  if (!workspace) return fail(KDA_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % KDA_WORKSPACE_ALIGN != 0)
+    return fail(KDA_ERR_INVALID_ARG, "workspace must be %d-byte aligned", KDA_WORKSPACE_ALIGN);
+  if ((int64_t)workspace_bytes < lay.off[KDA_WS_TOTAL])
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %lld", workspace_bytes,
+                (long long)lay.off[KDA_WS_TOTAL]);
+  const kda::Tables t = carve_tables(static_cast<uint8_t*>(workspace), lay, T);
+  const hipError_t e = kda::launch_index_fixed(B, (int)T, lay.seg, t, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   return KDA_OK;
 }
 
@@ -245,16 +286,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
 
   // ---- carve ----
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  kda::Tables t;
-  t.counters = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_COUNTERS]);
-  t.seq_start = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_START]);
-  t.seq_len = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_LEN]);
-  t.seq_chunk_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_CHUNK_OFF]);
-  t.seq_seg_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_SEG_OFF]);
-  t.chunk_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_CHUNK_TAB]);
-  t.seg_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_TAB]);
-  t.seq_full_off = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEQ_FULL_OFF]);
-  t.unit_tab = reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_UNIT_TAB]);
+  const kda::Tables t = carve_tables(ws, lay, cu_seqlens ? -1 : T);
   const bool cp = lay.seg > 0;
   kda::Seg sg;
   sg.M = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;

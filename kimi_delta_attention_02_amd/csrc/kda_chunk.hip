@@ -1110,12 +1110,24 @@ __global__ __launch_bounds__(NTHREADS) void KDA_CHUNK_KERNEL(Problem p, Tables t
   __shared__ Smem sm;
   const int k = (int)blockIdx.x / p.H;
   const int h = (int)blockIdx.x - k * p.H;
-  // the whole row in one read (rows past the live units hold -1); the grid
-  // has one row of blocks per table row
-  const int4 r0 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k];
-  const int4 r1 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k + 1];
-  if (r0.x < 0) return;
-  const Unit u{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z};
+  Unit u;
+  if (t.fixed) {
+    // fixed length: every block takes its unit from the tables' closed form
+    // The first launch sets the counters before any block can add to one.  No
+    // kernel reads the table rows of a fixed-length call, and none stores them
+    // (kda_write_fixed_tables does, for inspection).
+    if (MODE != 2 && blockIdx.x == 0 && threadIdx.x == 0) fixed_counters(p.N, t.fixed_T, sg.seg_chunks, t);
+    int32_t row[8];
+    if (!fixed_unit_row(p.N, t.fixed_T, sg.seg_chunks, k, row)) return;
+    u = Unit{row[0], row[1], row[2], row[3], row[4], row[5], row[6]};
+  } else {
+    // the whole row in one read (rows past the live units hold -1); the grid
+    // has one row of blocks per table row
+    const int4 r0 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k];
+    const int4 r1 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k + 1];
+    if (r0.x < 0) return;
+    u = Unit{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z};
+  }
   if (MODE == 0)
     chunk_body<RECUR, 0>(sm, p, t, sg, u, h);
   else if (MODE == 2)

@@ -10,8 +10,10 @@
 //
 // Free of host synchronisation, in one of three forms:
 //  - fixed length (no cu_seqlens): every row has a closed form (sequence i
-//    starts at i T, has ceil(T/16) chunks, ...); kda_index_fixed writes them
-//    all in one pass, one thread per row;
+//    starts at i T, has ceil(T/16) chunks, ...; fixed_tables in
+//    kda_internal.h): kda_fwd launches no index kernel and the chunk kernel's
+//    blocks find their units from that closed form; kda_index_fixed writes
+//    the rows out only for kda_write_fixed_tables (inspection and tests);
 //  - up to FUSED_MAX_N sequences and FUSED_MAX_ROWS table rows: one launch of
 //    kda_index_fused (one 1024-thread workgroup) that does both steps below,
 //    the second from copies of the prefix sums in LDS;
@@ -307,77 +309,26 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* _
 }
 
 // Every table of a fixed-length call (N sequences of T tokens) from its
-// closed form, one thread per row; same contents as the scan and fill give.
-__global__ __launch_bounds__(256) void kda_index_fixed(int N, long long T_row, int seg_chunks, long long max_chunks,
-                                                       long long max_segs, Tables t) {
-  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long nthr = (long long)gridDim.x * blockDim.x;
-  const int L = (int)T_row;
-  const int nc = (L + C - 1) / C;
-  const int ns = seg_chunks > 0 ? (nc > 0 ? (nc + seg_chunks - 1) / seg_chunks : 1) : 1;
-  const int nf = seg_chunks > 0 ? nc / seg_chunks : 1;  // full-length segments per sequence
-  const int n_chunks = N * nc, n_segs = N * ns, n_full = N * nf;
-  if (tid == 0) {
-    t.counters[CNT_N_CHUNKS] = n_chunks;
-    t.counters[CNT_N_SEGS] = n_segs;
-    t.counters[CNT_FLAGS] = 0;
-    t.counters[CNT_EARLY_STOPS] = 0;
-  }
-  for (long long i = tid; i <= N; i += nthr) {
-    t.seq_start[i] = (int32_t)(i * L);
-    t.seq_chunk_off[i] = (int32_t)(i * nc);
-    t.seq_seg_off[i] = (int32_t)(i * ns);
-    t.seq_full_off[i] = (int32_t)(i * nf);
-    if (i < N) t.seq_len[i] = L;
-  }
-  for (long long r = tid; r < max_chunks; r += nthr) {
-    const bool live = r < n_chunks;
-    t.chunk_tab[2 * r] = live ? (int32_t)(r / nc) : -1;
-    t.chunk_tab[2 * r + 1] = live ? (int32_t)(r % nc) : -1;
-  }
-  for (long long r = tid; r < max_segs; r += nthr) {
-    if (r < n_segs) {
-      const int sq = (int)(r / ns), j = (int)(r % ns);
-      const int first = sq * nc;
-      int32_t row[4] = {sq, first, first + nc, j};
-      if (seg_chunks > 0) {
-        const long long b0 = (long long)j * seg_chunks, e0 = b0 + seg_chunks;
-        row[1] = first + (int)(b0 < nc ? b0 : nc);
-        row[2] = first + (int)(e0 < nc ? e0 : nc);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t.seg_tab[4 * r + k] = row[k];
-      int32_t* u = t.unit_tab + 8 * (j < nf ? sq * nf + j : n_full + sq);
-      u[0] = (int32_t)r;
-      u[1] = row[0];
-      u[2] = row[1];
-      u[3] = row[2];
-      u[4] = row[3];
-      u[5] = sq * L;
-      u[6] = L;
-      u[7] = -1;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t.seg_tab[4 * r + k] = -1;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) t.unit_tab[8 * r + k] = -1;
-    }
-  }
+// closed form, one thread per row; the rows kda_fwd's kernels compute
+// without storing them.
+__global__ __launch_bounds__(256) void kda_index_fixed(int N, int L, int seg, Tables t) {
+  const int tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (tid == 0) fixed_counters(N, L, seg, t);
+  fixed_tables(tid, (int)(gridDim.x * blockDim.x), N, L, seg, t);
+}
+
+hipError_t launch_index_fixed(int N, int L, int seg, Tables t, hipStream_t st) {
+  long long rows = t.max_chunks > t.max_segs ? t.max_chunks : t.max_segs;
+  if (rows < N + 1) rows = N + 1;
+  long long blocks = (rows + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(kda_index_fixed, dim3((unsigned)blocks), dim3(256), 0, st, N, L, seg, t);
+  return hipGetLastError();
 }
 
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st) {
-  if (!cu_seqlens) {
-    long long rows = max_chunks > max_segs ? max_chunks : max_segs;
-    if (rows < N + 1) rows = N + 1;
-    long long blocks = (rows + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipEvent_t e0, e1;
-    stage_events(KDA_STAGE_INDEX, &e0, &e1);
-    hipExtLaunchKernelGGL(kda_index_fixed, dim3((unsigned)blocks), dim3(256), 0, st, e0, e1, 0, N, (long long)T_row,
-                          seg_chunks, (long long)max_chunks, (long long)max_segs, t);
-    return hipGetLastError();
-  }
+  if (!cu_seqlens) return hipSuccess;  // fixed length: written by the first chunk-kernel launch
   if (N <= FUSED_MAX_N && max_chunks <= FUSED_MAX_ROWS && max_segs <= FUSED_MAX_ROWS) {
     hipEvent_t e0, e1;
     stage_events(KDA_STAGE_INDEX, &e0, &e1);

@@ -38,6 +38,12 @@ struct Tables {
   int32_t* seg_tab;
   int32_t* seq_full_off;
   int32_t* unit_tab;
+  // A fixed-length call (no cu_seqlens) launches no index kernel: its first
+  // chunk-kernel launch writes these tables from their closed form, and every
+  // block finds its unit from that closed form.
+  int fixed;       // 1: fixed length, fixed_T tokens per sequence; 0: varlen
+  int fixed_T;
+  int64_t max_chunks, max_segs;  // table capacities
 };
 
 struct Problem {
@@ -86,6 +92,7 @@ struct Seg {
 // gets two events, which hipExtLaunchKernelGGL stamps with the kernel's own
 // start and end; otherwise both stay null and the launch is a plain one.
 void stage_events(int stage, hipEvent_t* start, hipEvent_t* stop);
+hipError_t launch_index_fixed(int N, int L, int seg, Tables t, hipStream_t st);
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
                         int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
 // producer/consumer chunk kernel: one launch per pass (phase 0: every segment,
@@ -163,6 +170,100 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
 __device__ __forceinline__ f32x4 zero4() {
   f32x4 z = {0.f, 0.f, 0.f, 0.f};
   return z;
+}
+
+// ---- tables of a fixed-length call (N sequences of L tokens), closed form ----
+// A sequence has nc = ceil(L/16) chunks and, split into segments of seg
+// chunks (seg = 0: one segment, serial), ns = ceil(nc/seg) segments (1 when
+// nc = 0) of which nf = floor(nc/seg) are full length.  Dispatch rank r
+// (a row of unit_tab) holds, for r < N nf, full segment r % nf of sequence
+// r / nf, and past that the shorter last segment of sequence r - N nf.
+struct FixedShape {
+  int nc, ns, nf;
+};
+
+__device__ __forceinline__ FixedShape fixed_shape(int L, int seg) {
+  FixedShape s;
+  s.nc = (L + 15) / 16;
+  s.ns = seg > 0 ? (s.nc > 0 ? (s.nc + seg - 1) / seg : 1) : 1;
+  s.nf = seg > 0 ? s.nc / seg : 1;
+  return s;
+}
+
+// The unit_tab row of dispatch rank r; false past the live units.  (Table
+// sizes are validated to fit int32 with room to spare, so 32-bit arithmetic
+// suffices here.)
+__device__ __forceinline__ bool fixed_unit_row(int N, int L, int seg, int r, int32_t row[8]) {
+  const FixedShape s = fixed_shape(L, seg);
+  const int n_full = N * s.nf;
+  if (r >= N * s.ns) return false;
+  const int sq = r < n_full ? r / s.nf : r - n_full;
+  const int j = r < n_full ? r - sq * s.nf : s.ns - 1;
+  const int first = sq * s.nc;
+  int b = first, e = first + s.nc;
+  if (seg > 0) {
+    const int b0 = j * seg;
+    b = first + min(b0, s.nc);
+    e = first + min(b0 + min(seg, s.nc), s.nc);
+  }
+  row[0] = sq * s.ns + j;  // segment row
+  row[1] = sq;
+  row[2] = b;
+  row[3] = e;
+  row[4] = j;
+  row[5] = sq * L;
+  row[6] = L;
+  row[7] = -1;
+  return true;
+}
+
+// The counters of a fixed-length call (one thread).
+__device__ __forceinline__ void fixed_counters(int N, int L, int seg, const Tables& t) {
+  const FixedShape s = fixed_shape(L, seg);
+  t.counters[CNT_N_CHUNKS] = N * s.nc;
+  t.counters[CNT_N_SEGS] = N * s.ns;
+  t.counters[CNT_FLAGS] = 0;
+  t.counters[CNT_EARLY_STOPS] = 0;
+}
+
+// Every table row of a fixed-length call, rows tid, tid + nthr, ... (the same
+// contents the varlen index kernels give for equal lengths).  Rows number
+// less than 2^30; tid and nthr come clamped to that.
+__device__ __forceinline__ void fixed_tables(int tid, int nthr, int N, int L, int seg, const Tables& t) {
+  const FixedShape s = fixed_shape(L, seg);
+  for (int i = tid; i <= N; i += nthr) {
+    t.seq_start[i] = i * L;
+    t.seq_chunk_off[i] = i * s.nc;
+    t.seq_seg_off[i] = i * s.ns;
+    t.seq_full_off[i] = i * s.nf;
+    if (i < N) t.seq_len[i] = L;
+  }
+  const int n_chunks = N * s.nc;
+  const int max_chunks = (int)t.max_chunks, max_segs = (int)t.max_segs;
+  for (int r = tid; r < max_chunks; r += nthr) {
+    const bool live = r < n_chunks;
+    const int sq = live ? r / s.nc : -1;
+    t.chunk_tab[2 * (long long)r] = sq;
+    t.chunk_tab[2 * (long long)r + 1] = live ? r - sq * s.nc : -1;
+  }
+  for (int r = tid; r < max_segs; r += nthr) {
+    int32_t row[8];
+    const bool live = fixed_unit_row(N, L, seg, r, row);
+    int32_t* u = t.unit_tab + 8 * (long long)r;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = live ? row[q] : -1;
+    if (live) {
+      // the segment of this rank into its row of seg_tab
+      int32_t* sr = t.seg_tab + 4 * (long long)row[0];
+      sr[0] = row[1];
+      sr[1] = row[2];
+      sr[2] = row[3];
+      sr[3] = row[4];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t.seg_tab[4 * (long long)r + q] = -1;
+    }
+  }
 }
 
 }  // namespace kda

@@ -175,6 +175,10 @@ def test_index_tables_bit_exact(lens, seg, fixed):
     _, _, ws = run_gpu(w, x, d, cp_mode=mode, seg_chunks=seg, want_final=False)
     import kimi_delta_attention_02_amd as kda
 
+    if fixed:  # kda_fwd computes these rows in closed form without storing them
+        kda.write_fixed_tables(w.B, w.T, w.H, mode, seg, ws)
+        torch.cuda.synchronize()
+
     offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, mode, seg)
     ref = O.index_tables(lens, 16, seg if seg else None)
     N = len(lens)
