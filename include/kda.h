@@ -119,7 +119,8 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
 
 /* Byte offsets of the workspace regions for these sizes and plan, so a caller
  * can inspect the index tables and segment maps a kda_fwd call left in its
- * workspace.  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
+ * workspace (a varlen call stores its tables; a fixed-length call stores only
+ * the counters, see kda_write_fixed_tables).  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
  * order of kda_ws_offset.  Returns KDA_OK or a negative kda_status. */
 typedef enum {
   KDA_WS_COUNTERS = 0,      /* int32[4]: n_chunks, n_segs, flags, early_stops; flags bits 0x1..0x8 name
@@ -188,7 +189,7 @@ int32_t kda_write_fixed_tables(int32_t B, int64_t T, int32_t H, int32_t cp_mode,
  * milliseconds of each kernel into its stage's stage_ms[0..n_stages-1] entry
  * and the number of timed launches of the stage into stage_calls, and forgets
  * them.
- * Stages: KDA_STAGE_INDEX (index tables), KDA_STAGE_RECUR0 (chunk prep +
+ * Stages: KDA_STAGE_INDEX (index tables; varlen calls only), KDA_STAGE_RECUR0 (chunk prep +
  * recurrence of whole sequences / first segments, and the pre-scan of
  * segments >= 1), KDA_STAGE_MERGE (no kernel reports it: the merge runs at
  * the start of the second pass), KDA_STAGE_RECUR1 (merge + chunk prep +
