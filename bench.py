@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg2] [--cp auto]
 
-One step = one kda_fwd call (index tables in closed form, chunk prep fused with the
+One step = one kda_fwd call (index tables: a launch for varlen calls, closed form
+inside the chunk kernel for fixed-length ones; chunk prep fused with the
 recurrence and, when the plan splits sequences, a second pass that merges each
 segment's start state and redoes its first chunks where needed) over one batch of seeded synthetic inputs already resident in HBM.
 Untimed calls first run for --preheat-ms of wall time (default 300 ms): the
