@@ -1,11 +1,13 @@
 """KDA forward prefill benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg2] [--cp auto]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg4a] [--cp auto]
 
 One step = one kda_fwd call (index tables: a launch for varlen calls, closed form
 inside the chunk kernel for fixed-length ones; chunk prep fused with the
 recurrence and, when the plan splits sequences, a second pass that merges each
-segment's start state and redoes its first chunks where needed) over one batch of seeded synthetic inputs already resident in HBM.
+segment's start state and redoes its first chunks where needed) over one batch
+of seeded synthetic inputs already resident in HBM.  The default workload is
+the long single sequence, B=1 T=65536 H=16 (the 64K end of the metric's range).
 Untimed calls first run for --preheat-ms of wall time (default 300 ms): the
 GPU's clock rises over the first tens of milliseconds of sustained load (the
 per-step time falls by 13-17 % over them), and the steps are meant to be
@@ -20,13 +22,17 @@ Per-kernel time comes from the library's own timing hook
 of HIP events that take its own start and end, on the library's stream) over
 a second run of K steps; the step time comes from the first, uninstrumented
 run.  The roofline object is computed for the chunk kernel (chunk prep +
-recurrence), summed over its launches in a step.  The same call is also
-captured once in a HIP graph and replayed K times; that time and the host
-time per call are reported under "path", beside the plain calls.
+recurrence), summed over its launches in a step, against the vendor HBM peak
+and, beside it, the bandwidth of a plain device copy measured in the same run.
+Host time per call is reported under "path" three ways: fwd() from Python,
+the prepared call (kda.prepare: checked and marshalled once), and the C ABI's
+own share (the library's host timer).  The same call is also captured once in
+a HIP graph and replayed K times, last.
 
 The CPU baseline times the fp64 oracle (unchanged) on a bounded sample of the
-same workload: whole sequences taken in order, all heads, one head per worker
-process, repeated to about --cpu-seconds, before any GPU work starts.
+same workload, before any GPU work starts: its first tokens (whole sequences
+in order, the last cut to a prefix), all heads, one head per worker process,
+sized to about --cpu-seconds; and one head on one core, scaled to all heads.
 """
 from __future__ import annotations
 
@@ -152,61 +158,124 @@ class HipTimingEvents:
 
 
 _CPU_X = None  # inputs shared with the forked baseline workers
+CPU_SHARE = 16  # host cores a one-GPU machine grants a job (worker pools are sized to it)
+
+
+def _sample_spans(w, x, tokens: int):
+    """The first `tokens` tokens of the workload, sequence by sequence in
+    order (the last one cut to a prefix): [(row, first token, length, seq)]."""
+    from oracle import kda_oracle as O
+
+    out, left = [], tokens
+    for i, (b, t0, L) in enumerate(O.sequence_spans(w.B, w.T, x["cu_seqlens"])):
+        if left <= 0:
+            break
+        n = min(L, left)
+        if n > 0:
+            out.append((b, t0, n, i))
+            left -= n
+    return out
+
+
+def _oracle_on(x, spans, head):
+    """The oracle, unchanged, over the given sequence prefixes of one head."""
+    from oracle import kda_oracle as O
+
+    for b, t0, n, i in spans:
+        sl = (slice(b, b + 1), slice(t0, t0 + n))
+        init = None if x["initial_state"] is None else x["initial_state"][i:i + 1]
+        O.kda_forward(x["q"][sl], x["k"][sl], x["v"][sl], x["g"][sl], x["beta"][sl], x["A_log"], x["dt_bias"],
+                      x["scale"], x["lower_bound"], init, None, heads=[head])
 
 
 def _cpu_worker(args):
-    head, seqs, reps = args
+    head, spans, reps = args
     from threadpoolctl import threadpool_limits
 
-    from oracle import kda_oracle as O
-
     with threadpool_limits(1):
-        x = _CPU_X
         t = time.perf_counter()
         for _ in range(reps):
-            O.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["A_log"], x["dt_bias"], x["scale"],
-                          x["lower_bound"], x["initial_state"], x["cu_seqlens"], seqs=seqs, heads=[head])
+            _oracle_on(_CPU_X, spans, head)
         return time.perf_counter() - t
 
 
 def cpu_baseline(name: str, target_s: float) -> dict:
-    """The oracle, unchanged, over a bounded sample of the workload: whole
-    sequences (all heads, one head per worker process), repeated so that the
-    timed work lasts about target_s seconds."""
+    """The oracle, unchanged, over a bounded sample of the workload: its first
+    tokens (whole sequences in order, the last one cut to a prefix), all
+    heads, one head per worker process, sized so that the timed work lasts
+    about target_s seconds; plus the same oracle on one core."""
     import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
 
     import kda_inputs
 
     global _CPU_X
     w = kda_inputs.WORKLOADS[name]
     _CPU_X = kda_inputs.make_inputs(w)
-    lens = [w.T] * w.B if w.seqlens is None else list(w.seqlens)
-    # calibrate on the shortest non-empty sequence, one head, in this process
-    i0 = min((i for i in range(len(lens)) if lens[i] > 0), key=lambda i: lens[i])
-    t_tok = _cpu_worker((0, [i0], 1)) / lens[i0]
-    workers = max(1, min(16, os.cpu_count() or 1, w.H))
+    host_cores = os.cpu_count() or 1
+    workers = max(1, min(CPU_SHARE, host_cores, w.H))
     rounds = math.ceil(w.H / workers)
-    # take sequences in order until the sample is large enough, then repeat it
-    seqs, tokens = [], 0
-    for i, L in enumerate(lens):
-        if tokens and tokens * t_tok * rounds >= target_s:
-            break
-        seqs.append(i)
-        tokens += L
-    reps = max(1, int(target_s / max(tokens * t_tok * rounds, 1e-9)))
+    # one core: one head over a growing prefix until about 2 s of work
+    n, t1 = 256, 0.0
+    with threadpool_limits(1):
+        while True:
+            sp = _sample_spans(w, _CPU_X, n)
+            t = time.perf_counter()
+            _oracle_on(_CPU_X, sp, 0)
+            t1 = time.perf_counter() - t
+            done = sum(s[2] for s in sp)
+            if t1 >= 2.0 or done < n:
+                break
+            n = int(n * min(8.0, max(2.0, 2.0 / max(t1, 1e-3))))
+    per_head_tok_s = done / t1
+    # all cores: a prefix sized for target_s
+    tokens = max(16, int(target_s * per_head_tok_s / rounds))
+    spans = _sample_spans(w, _CPU_X, tokens)
+    tokens = sum(s[2] for s in spans)
+    reps = 1
     ctx = mp.get_context("fork")
     t = time.perf_counter()
     with ctx.Pool(workers) as pool:
-        pool.map(_cpu_worker, [(h, seqs, reps) for h in range(w.H)])
+        pool.map(_cpu_worker, [(h, spans, reps) for h in range(w.H)])
     wall = time.perf_counter() - t
+    desc = ", ".join(f"seq {i}: {n} of its tokens" for _, _, n, i in spans)
     return {
         "value": tokens * reps / wall,
         "unit": "tokens/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"{w.name}: sequences {seqs} ({tokens} tokens) x {reps} passes, all {w.H} heads, fp64 token "
-                  f"recurrence, one head per process ({workers} processes), {wall:.1f} s wall",
+        "host_cores": host_cores,
+        "one_core": {"value": per_head_tok_s / w.H, "unit": "tokens/s",
+                     "sample": f"head 0 over the first {done} tokens, {t1:.1f} s, scaled to all {w.H} heads"},
+        "sample": f"{w.name}: the first {tokens} tokens ({desc}), all {w.H} heads, fp64 token recurrence, one "
+                  f"head per process ({workers} processes of the {host_cores} host cores), {wall:.1f} s wall",
     }
+
+
+def copy_bandwidth(dev, mib: int = 1024, reps: int = 20) -> dict:
+    """Device-to-device copy bandwidth (read + write bytes per second) of a
+    plain torch copy of `mib` MiB, timed with fence-free HIP events: the box's
+    measured HBM figure, reported beside the vendor peak."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    tev = HipTimingEvents()
+    a, b = tev.create(), tev.create()
+    tev.record(a, stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    tev.record(b, stream)
+    ms = tev.elapsed_ms(a, b) / reps
+    tev.close()
+    del src, dst
+    return {"GBs": round(2 * n / (ms / 1e3) / 1e9, 1), "bytes": n, "ms": round(ms, 4)}
 
 
 def main() -> int:
@@ -216,11 +285,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--preheat-ms", type=float, default=300.0,
                     help="untimed calls for this much wall time before the warmup steps (0 = none)")
-    ap.add_argument("--config", default="cfg2", help="cfg1..cfg5 (cfg4a/cfg4b)")
+    ap.add_argument("--config", default="cfg4a",
+                    help="workload: cfg1..cfg5 (cfg4a/cfg4b), or cfg4a_slow (T=65536 H=16 at lower_bound -0.1)")
     ap.add_argument("--cp", default="auto", help="auto | off | force")
     ap.add_argument("--seg", type=int, default=0, help="segment length in chunks (0 = library choice)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU baseline's all-core sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-bw", action="store_true", help="skip the device copy bandwidth measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (scale reference for HBM counters)")
     a = ap.parse_args()
@@ -307,6 +379,23 @@ def main() -> int:
     torch.cuda.synchronize()
     kda.profile_enable(False)
     stages = kda.profile_collect()
+    # Host time per call on the fast path: the call checked and marshalled once
+    # (kda.prepare), then only launched; inside it, the C ABI's own share
+    # (validation, planning and the launches), from the library's host timer.
+    prep = kda.prepare(q, k, v, g, beta, x["scale"], out, A_log=A_log, dt_bias=dt_bias, lower_bound=x["lower_bound"],
+                       workspace=ws, initial_state=init, final_state=final, cu_seqlens=cu, cp_mode=a.cp,
+                       seg_chunks=a.seg)
+    for _ in range(a.warmup):
+        prep()
+    torch.cuda.synchronize()
+    kda.profile_enable(False, host=True)
+    h0 = time.perf_counter()
+    for i in range(a.steps):
+        prep()
+    prep_host_us = (time.perf_counter() - h0) / a.steps * 1e6
+    kda.profile_enable(False, host=False)
+    cabi_us, cabi_calls = kda.profile_host()
+    torch.cuda.synchronize()
     # Timed region 3: the same call captured once in a HIP graph and replayed K
     # times (the call allocates nothing and never synchronises, so it can be
     # captured); reported beside the plain calls, not as the value.
@@ -325,6 +414,7 @@ def main() -> int:
     graph_ms = tev.elapsed_ms(gev[0], gev[1]) / a.steps
     tev.close()
     del graph
+    copy = None if a.no_copy_bw else copy_bandwidth(dev)
     q1, q3 = len(per) // 4, len(per) - len(per) // 4
     iqr_mean = float(np.mean(per[q1:q3])) if q3 > q1 else float(np.mean(per))
     ms = total_ms / a.steps
@@ -358,6 +448,9 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfl / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["traffic"] = measured_traffic(w.name, (1, 2) if seg > 0 else (0,))
+    if roof["bound"] == "hbm" and copy is not None:
+        roof["measured_copy_GBs"] = copy["GBs"]
+        roof["frac_of_measured_copy"] = round(gbs / copy["GBs"], 4)
     roof["kernel"] = "kda_chunk_kernel"
     roof["launches_per_step"] = launches
     roof["kernel_ms_per_step"] = round(chunk_ms, 4)
@@ -394,14 +487,19 @@ def main() -> int:
             "hbm_frac": round(path_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_frac": round(path_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "iqr_mean_ms": round(iqr_mean, 4),
-            # host time to submit one call (Python binding + C ABI validation + launches)
+            # host time to submit one call: fwd() from Python (argument checks, ctypes,
+            # C ABI validation, launches); the prepared call (kda.prepare) on the
+            # same buffers; and the C ABI's own share of the prepared call
             "host_us_per_call": round(host_us, 1),
+            "prepared_host_us_per_call": round(prep_host_us, 2),
+            "c_abi_host_us_per_call": round(cabi_us / max(cabi_calls, 1), 2),
             # the call captured in a HIP graph, replayed K times
             "graph_ms_per_step": round(graph_ms, 4),
             "graph_host_us_per_call": round(graph_host_us, 1),
         },
         "stages_ms_per_step": {n: round(t / a.steps, 4) for n, (t, c) in stages.items() if c},
     }
+    res["copy_bandwidth"] = copy
     if a.copy_probe_mib > 0:
         n = a.copy_probe_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -16,8 +16,13 @@
  * (caller-allocated uint8 workspace sized by get_workspace_size(B*T, H)) and
  * "State Management and Accumulator Types" (bf16 or fp32 states); cuLA PR #106,
  * commit list (K1 chunk prep / K2 recurrence, CHUNK = 16; segment split
- * K1 -> pre_scan -> merge -> segment K2, bit-identical to serial) and review
- * thread (use_intracard_cp auto / True / False; no implicit conversions).
+ * K1 -> pre_scan -> merge -> segment K2, said to be bit-identical to serial)
+ * and review thread (use_intracard_cp auto / True / False; no implicit
+ * conversions).  Here the segmented result has the serial path's bits
+ * whenever every segment's transition M underflows to exactly zero in fp32
+ * and the zero-start state has converged to the serial one by the segment's
+ * checkpoint (strong decay, e.g. lower_bound -5 over 256-chunk segments);
+ * otherwise it equals the serial result within rounding (fp32 merge).
  *
  * Conventions for every call below:
  *  - All tensor pointers are DEVICE pointers, contiguous, in the layouts stated.
@@ -202,8 +207,19 @@ typedef enum {
   KDA_NUM_STAGES
 } kda_stage;
 
+/* enable: KDA_PROFILE_KERNELS (the kernel events above), KDA_PROFILE_HOST
+ * (host time of each kda_fwd call on this thread, from its
+ * entry to its return: validation, planning and the launches, without the
+ * caller's own marshalling), both, or 0. */
+#define KDA_PROFILE_KERNELS 1
+#define KDA_PROFILE_HOST 2
 int32_t kda_profile_enable(int32_t enable);
 int32_t kda_profile_collect(double* stage_ms, int64_t* stage_calls, int32_t n_stages);
+
+/* The host microseconds summed over the forward calls timed since the last
+ * kda_profile_host call on this thread, and their count; then resets both.
+ * Either pointer may be NULL.  Returns KDA_OK. */
+int32_t kda_profile_host(double* host_us, int64_t* calls);
 
 /* Static description of a status code. */
 const char* kda_strerror(int32_t status);

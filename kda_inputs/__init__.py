@@ -105,6 +105,10 @@ WORKLOADS = {
                      scale=INV_SQRT_D, init_std=0.05, state_dtype="fp32", want_final=True, seed=4),
     "cfg5": Workload("kda_fwd_B8_T8192_H32", B=8, T=8192, H=32, seqlens=None, lower_bound=-1.0,
                      scale=INV_SQRT_D, init_std=0.05, state_dtype="fp32", want_final=True, seed=5),
+    # the long sequence with slowly decaying state (the gate's lower bound near 0): the regime in
+    # which a segment's transition M does not underflow to zero
+    "cfg4a_slow": Workload("kda_fwd_B1_T65536_H16_lb0.1", B=1, T=65536, H=16, seqlens=None, lower_bound=-0.1,
+                           scale=INV_SQRT_D, init_std=0.05, state_dtype="fp32", want_final=True, seed=4),
 }
 
 

@@ -26,6 +26,9 @@ from typing import Optional
 
 __all__ = [
     "fwd",
+    "prepare",
+    "PreparedFwd",
+    "read_counters",
     "chunk_kda",
     "get_workspace_size",
     "plan_seg_chunks",
@@ -37,6 +40,7 @@ __all__ = [
     "STAGES",
     "profile_enable",
     "profile_collect",
+    "profile_host",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +96,8 @@ def load_library():
     lib.kda_profile_enable.restype = i32
     lib.kda_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32]
     lib.kda_profile_collect.restype = i32
+    lib.kda_profile_host.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.kda_profile_host.restype = i32
     lib.kda_strerror.argtypes = [i32]
     lib.kda_strerror.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -157,6 +163,7 @@ def write_fixed_tables(B: int, T: int, H: int, cp_mode, seg_chunks: int, workspa
     import torch
 
     _check(workspace, "workspace", torch.uint8)
+    _check_devices((("workspace", workspace),))
     with torch.cuda.device_of(workspace):
         stream = torch.cuda.current_stream(workspace.device).cuda_stream
         st = load_library().kda_write_fixed_tables(int(B), int(T), int(H), _cp(cp_mode), int(seg_chunks),
@@ -168,9 +175,23 @@ def write_fixed_tables(B: int, T: int, H: int, cp_mode, seg_chunks: int, workspa
 STAGES = ["index", "recur0", "merge", "recur1"]
 
 
-def profile_enable(on: bool = True) -> None:
-    """Record HIP events around each kernel stage of every fwd on this thread."""
-    load_library().kda_profile_enable(1 if on else 0)
+PROFILE_KERNELS = 1
+PROFILE_HOST = 2
+
+
+def profile_enable(on: bool = True, host: bool = False) -> None:
+    """Record HIP events around each kernel stage of every fwd on this thread
+    (on), and the host time each forward call spends inside the library (host)."""
+    load_library().kda_profile_enable((PROFILE_KERNELS if on else 0) | (PROFILE_HOST if host else 0))
+
+
+def profile_host() -> tuple:
+    """(host microseconds, calls) of the forward calls timed since the last
+    call, inside the C ABI; then resets."""
+    us = ctypes.c_double()
+    n = ctypes.c_int64()
+    load_library().kda_profile_host(ctypes.byref(us), ctypes.byref(n))
+    return float(us.value), int(n.value)
 
 
 def profile_collect() -> dict:
@@ -185,12 +206,12 @@ def profile_collect() -> dict:
 
 
 def _check(t, name, dtype, shape=None):
+    """Type, dtype, layout and shape of one tensor (the device is checked once
+    for all tensors of a call, last: _check_devices)."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype}); no implicit conversion is made")
     if not t.is_contiguous():
@@ -199,25 +220,32 @@ def _check(t, name, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound: float, workspace=None,
-        initial_state=None, final_state=None, cu_seqlens=None, cp_mode="auto", seg_chunks: int = 0,
-        state_layout: str = "vk"):
-    """KDA forward.  Returns out (allocated if None).
+def _check_devices(named):
+    """Every given tensor is a GPU tensor, all on the first one's device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"all tensors must be on the same device ({name} is on {t.device}, not {dev})")
 
-    q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; A_log: fp32 [H];
-    q and k may have fewer heads H_qk (dividing H): head h then uses q/k head
-    h // (H // H_qk) (grouped value heads);
-    dt_bias: fp32 [H, 128]; lower_bound in [-5, 0];
-    initial_state / final_state: None or [N, H, 128, 128] in bf16 or fp32
-    (both the same dtype when both are given), [v][k] per head when
-    state_layout is "vk", [k][v] when it is "kv"; cu_seqlens: None or int32
-    [N + 1] (then B == 1); workspace: uint8 device buffer of at least
-    get_workspace_size(B*T, H, N, cp_mode, seg_chunks) bytes, 256-byte
-    aligned (allocated here when None); cp_mode: "auto" | "off" | "force".
-    """
+
+class _Checked:
+    """The checked shapes and dtypes of one forward call."""
+
+    __slots__ = ("B", "T", "H", "Hqk", "D", "N", "sdt", "out", "device")
+
+
+def _check_fwd(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, state_layout,
+               workspace=None) -> _Checked:
+    """Every check of a forward call's tensors, before any device work
+    (allocates out when it is None)."""
     import torch
 
-    lib = load_library()
     _check(q, "q", torch.bfloat16)
     _check(v, "v", torch.bfloat16)
     if q.dim() != 4 or v.dim() != 4:
@@ -247,46 +275,208 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
     for name, st in (("initial_state", initial_state), ("final_state", final_state)):
         if st is None:
             continue
+        if not isinstance(st, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
         if st.dtype not in (torch.float32, torch.bfloat16):
             raise TypeError(f"{name} must be float32 or bfloat16 (got {st.dtype})")
         _check(st, name, st.dtype, (N, H, D, D))
         if sdt is not None and st.dtype != sdt:
             raise TypeError("initial_state and final_state must have the same dtype")
         sdt = st.dtype
-    if out is None:
-        out = torch.empty_like(v)
-    else:
+    if out is not None:
         _check(out, "out", torch.bfloat16, v.shape)
-    tensors = [q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, workspace]
-    for t in tensors:
-        if t is not None and t.device != dev:
-            raise ValueError("all tensors must be on the same device")
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8)
     if state_layout not in ("vk", "kv"):
         raise ValueError(f"state_layout must be 'vk' or 'kv' (got {state_layout!r})")
-    cpm = _cp(cp_mode)
-    need = get_workspace_size(B * T, H, N, cpm, seg_chunks)
-    with torch.cuda.device_of(q):
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        _check(workspace, "workspace", torch.uint8)
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.kda_fwd(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), float(scale), out.data_ptr(),
-            A_log.data_ptr(), dt_bias.data_ptr(), float(lower_bound),
-            initial_state.data_ptr() if initial_state is not None else None,
-            final_state.data_ptr() if final_state is not None else None,
-            1 if sdt in (None, torch.float32) else 0, 1 if state_layout == "kv" else 0,
-            cu_seqlens.data_ptr() if cu_seqlens is not None else None, N if cu_seqlens is not None else 0,
-            B, T, H, Hqk, D, workspace.data_ptr(), workspace.numel(), cpm, int(seg_chunks), stream)
-    if st != 0:
-        _raise(st)
+    _check_devices((("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out), ("A_log", A_log),
+                    ("dt_bias", dt_bias), ("initial_state", initial_state), ("final_state", final_state),
+                    ("cu_seqlens", cu_seqlens), ("workspace", workspace)))
+    if out is None:
+        out = torch.empty_like(v)
+    c = _Checked()
+    c.B, c.T, c.H, c.Hqk, c.D, c.N, c.sdt, c.out, c.device = B, T, H, Hqk, D, N, sdt, out, dev
+    return c
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _fwd_args(c: _Checked, q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state, final_state,
+              cu_seqlens, state_layout):
+    """kda_fwd's arguments before the workspace."""
+    import torch
+
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(c.out), _ptr(A_log), _ptr(dt_bias),
+            float(lower_bound), _ptr(initial_state), _ptr(final_state),
+            1 if c.sdt in (None, torch.float32) else 0, 1 if state_layout == "kv" else 0,
+            _ptr(cu_seqlens), c.N if cu_seqlens is not None else 0, c.B, c.T, c.H, c.Hqk, c.D)
+
+
+def _log_call(c: _Checked, cpm: int, seg_chunks: int):
     if os.environ.get("KDA_LOG") == "1":
         import sys
 
-        seg = plan_seg_chunks(B * T, H, N, cpm, seg_chunks)
-        print(f"[kda] fwd B={B} T={T} H={H} N={N} plan={'serial' if seg == 0 else f'segments of {seg} chunks'}",
+        seg = plan_seg_chunks(c.B * c.T, c.H, c.N, cpm, seg_chunks)
+        print(f"[kda] fwd B={c.B} T={c.T} H={c.H} N={c.N} plan={'serial' if seg == 0 else f'segments of {seg} chunks'}",
               file=sys.stderr)
-    return out
+
+
+# counters[2] bits: repaired cu_seqlens faults (0x1-0x8), a chunk-kernel wait that gave up (0x100, 0x200)
+FLAG_OFFSETS_REPAIRED = 0x00F
+FLAG_WAIT_GAVE_UP = 0x300
+
+
+def read_counters(workspace, total_tokens: int, num_heads: int, num_seqs: int = 1, cp_mode="auto",
+                  seg_chunks: int = 0) -> dict:
+    """The counters a call left in its workspace (copies 16 bytes to the host,
+    which waits for the call): chunks, segments, flags (FLAG_* bits) and
+    early_stops.  The sizes and plan must be the call's."""
+    import numpy as np
+
+    offs = workspace_offsets(total_tokens, num_heads, num_seqs, cp_mode, seg_chunks)
+    o = offs["counters"]
+    c = workspace[o:o + 16].cpu().numpy().view(np.int32)
+    return {"chunks": int(c[0]), "segments": int(c[1]), "flags": int(c[2]), "early_stops": int(c[3])}
+
+
+def _raise_on_flags(workspace, c: _Checked, cpm: int, seg_chunks: int):
+    cnt = read_counters(workspace, c.B * c.T, c.H, c.N, cpm, seg_chunks)
+    f = cnt["flags"]
+    if f & FLAG_WAIT_GAVE_UP:
+        raise KdaError(-4, f"a chunk-kernel wait gave up (counters flags {f:#x}): the results are not valid")
+    if f & FLAG_OFFSETS_REPAIRED:
+        raise KdaError(-1, f"cu_seqlens was malformed and clamped on the device (counters flags {f:#x})")
+
+
+def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound: float, workspace=None,
+        initial_state=None, final_state=None, cu_seqlens=None, cp_mode="auto", seg_chunks: int = 0,
+        state_layout: str = "vk", check: bool = False):
+    """KDA forward.  Returns out (allocated if None).
+
+    q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; A_log: fp32 [H];
+    q and k may have fewer heads H_qk (dividing H): head h then uses q/k head
+    h // (H // H_qk) (grouped value heads);
+    dt_bias: fp32 [H, 128]; lower_bound in [-5, 0];
+    initial_state / final_state: None or [N, H, 128, 128] in bf16 or fp32
+    (both the same dtype when both are given), [v][k] per head when
+    state_layout is "vk", [k][v] when it is "kv"; cu_seqlens: None or int32
+    [N + 1] (then B == 1); workspace: uint8 device buffer of at least
+    get_workspace_size(B*T, H, N, cp_mode, seg_chunks) bytes, 256-byte
+    aligned (allocated here when None); cp_mode: "auto" | "off" | "force".
+
+    The call is asynchronous.  A wait inside the kernels that gives up, or a
+    malformed cu_seqlens that the kernels clamped, is recorded only in the
+    workspace's counters; check=True waits for the call, reads them and raises
+    KdaError when either is set (read_counters does the same for a caller's
+    workspace).
+    """
+    import torch
+
+    lib = load_library()
+    cpm = _cp(cp_mode)
+    c = _check_fwd(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, state_layout,
+                   workspace)
+    need = get_workspace_size(c.B * c.T, c.H, c.N, cpm, seg_chunks)
+    with torch.cuda.device_of(q):
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=c.device)
+        stream = torch.cuda.current_stream(c.device).cuda_stream
+        st = lib.kda_fwd(*_fwd_args(c, q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state,
+                                    final_state, cu_seqlens, state_layout),
+                         workspace.data_ptr(), workspace.numel(), cpm, int(seg_chunks), stream)
+    if st != 0:
+        _raise(st)
+    _log_call(c, cpm, seg_chunks)
+    if check:
+        _raise_on_flags(workspace, c, cpm, seg_chunks)
+    return c.out
+
+
+class PreparedFwd:
+    """A forward call checked and marshalled once (prepare()), for callers that
+    repeat the same call on the same buffers: __call__ only launches it, on the
+    stream chosen at preparation, with the ctypes arguments already built.
+    Refill the input tensors in place between calls; rebind() swaps tensors of
+    the same shape, dtype and device."""
+
+    _NAMES = ("q", "k", "v", "g", "beta", "out", "A_log", "dt_bias", "initial_state", "final_state", "cu_seqlens",
+              "workspace")
+
+    def __init__(self, tensors: dict, scale, lower_bound, cp_mode, seg_chunks, state_layout, stream):
+        import torch
+
+        lib = load_library()
+        t = dict(tensors)
+        cpm = _cp(cp_mode)
+        c = _check_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["out"], t["A_log"], t["dt_bias"],
+                       t["initial_state"], t["final_state"], t["cu_seqlens"], state_layout, t["workspace"])
+        t["out"] = c.out
+        need = get_workspace_size(c.B * c.T, c.H, c.N, cpm, seg_chunks)
+        if t["workspace"] is None:
+            t["workspace"] = torch.empty(need, dtype=torch.uint8, device=c.device)
+        elif t["workspace"].numel() < need:
+            raise ValueError(f"workspace of {t['workspace'].numel()} bytes, need {need}")
+        if stream is None:
+            stream = torch.cuda.current_stream(c.device)
+        self._c, self._cpm, self._seg = c, cpm, int(seg_chunks)
+        self._scale, self._lb, self._layout = float(scale), float(lower_bound), state_layout
+        self._t = t
+        self._stream = stream
+        # the function without argtypes, called with ready ctypes values
+        fn = ctypes.CDLL(_LIB_PATH).kda_fwd
+        fn.restype = ctypes.c_int32
+        self._fn = fn
+        self._types = lib.kda_fwd.argtypes
+        self._build()
+
+    def _build(self):
+        t, c = self._t, self._c
+        raw = _fwd_args(c, t["q"], t["k"], t["v"], t["g"], t["beta"], self._scale, t["A_log"], t["dt_bias"], self._lb,
+                        t["initial_state"], t["final_state"], t["cu_seqlens"], self._layout) + (
+            t["workspace"].data_ptr(), t["workspace"].numel(), self._cpm, self._seg, self._stream.cuda_stream)
+        self._args = tuple(ty(x) if x is not None else ty() for ty, x in zip(self._types, raw))
+
+    @property
+    def out(self):
+        return self._t["out"]
+
+    @property
+    def workspace(self):
+        return self._t["workspace"]
+
+    def rebind(self, **tensors):
+        """Use other tensors of the same shapes, dtypes and device (names as in fwd)."""
+        for name, new in tensors.items():
+            if name not in self._NAMES:
+                raise ValueError(f"unknown tensor {name!r}")
+            old = self._t[name]
+            if (old is None) != (new is None):
+                raise ValueError(f"{name}: presence cannot change after prepare()")
+            if old is not None:
+                _check(new, name, old.dtype, old.shape)
+                if new.device != old.device:
+                    raise ValueError(f"{name} must stay on {old.device}")
+        self._t.update(tensors)
+        self._build()
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            _raise(st)
+        return self._t["out"]
+
+
+def prepare(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound: float, workspace=None,
+            initial_state=None, final_state=None, cu_seqlens=None, cp_mode="auto", seg_chunks: int = 0,
+            state_layout: str = "vk", stream=None) -> PreparedFwd:
+    """Check and marshal a fwd call once; the returned object launches it
+    (on `stream`, default: the current stream now) each time it is called.
+    out and the workspace are allocated here when None."""
+    tensors = dict(q=q, k=k, v=v, g=g, beta=beta, out=out, A_log=A_log, dt_bias=dt_bias, initial_state=initial_state,
+                   final_state=final_state, cu_seqlens=cu_seqlens, workspace=workspace)
+    return PreparedFwd(tensors, scale, lower_bound, cp_mode, seg_chunks, state_layout, stream)
 
 
 def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state: bool = False, *, A_log,

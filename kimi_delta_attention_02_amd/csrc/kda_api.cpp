@@ -24,6 +24,7 @@
 // launches no merge at all.
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -56,7 +57,10 @@ constexpr int kWideMinChunks = 128; // units at least this long (on average) run
 
 // ---- optional per-kernel event timing (benchmarks) ----
 struct Profiler {
-  bool on = false;
+  bool on = false;     // kernel events
+  bool host = false;   // host time of each forward call
+  double host_us = 0.0;
+  int64_t host_calls = 0;
   std::vector<hipEvent_t> pool;
   struct Rec {
     int stage;
@@ -77,6 +81,21 @@ struct Profiler {
   }
 };
 thread_local Profiler g_prof;
+
+// Adds the host time from construction to destruction to the profiler while
+// host timing is on (every return path of a forward call).
+struct HostTimer {
+  bool on;
+  std::chrono::steady_clock::time_point t0;
+  HostTimer() : on(g_prof.host) {
+    if (on) t0 = std::chrono::steady_clock::now();
+  }
+  ~HostTimer() {
+    if (!on) return;
+    g_prof.host_us += std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+    g_prof.host_calls += 1;
+  }
+};
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -189,6 +208,132 @@ kda::Tables carve_tables(uint8_t* ws, const Layout& lay, int64_t fixed_T) {
   return t;
 }
 
+namespace {
+
+// The arguments of one forward call, as kda_fwd receives them.
+struct FwdArgs {
+  const void *q, *k, *v, *g, *beta;
+  float scale;
+  void* out;
+  const float *A_log, *dt_bias;
+  float lower_bound;
+  const void* initial_state;
+  void* final_state;
+  int32_t state_dtype, state_layout;
+  const int32_t* cu_seqlens;
+  int32_t num_seqs, B;
+  int64_t T;
+  int32_t H, H_qk, D, cp_mode, seg_chunks;
+};
+
+struct Prepared {
+  Layout lay;
+  int32_t N = 0, H_qk = 0;
+  int64_t total = 0;
+  bool nothing = false;  // a valid call with nothing to launch
+};
+
+// Every check of a forward call that needs no workspace, before any HIP call.
+int32_t prepare(const FwdArgs& a, Prepared* pr) {
+  if (a.D != kda::D) return fail(KDA_ERR_UNSUPPORTED, "head dimension %d unsupported (only 128)", a.D);
+  if (a.B < 0 || a.T < 0) return fail(KDA_ERR_INVALID_ARG, "B=%d and T=%lld must be >= 0", a.B, (long long)a.T);
+  if (a.H < 1) return fail(KDA_ERR_INVALID_ARG, "H=%d must be >= 1", a.H);
+  const int32_t H_qk = a.H_qk == 0 ? a.H : a.H_qk;
+  if (H_qk < 1 || H_qk > a.H || a.H % H_qk != 0)
+    return fail(KDA_ERR_INVALID_ARG, "H_qk=%d must divide H=%d", H_qk, a.H);
+  if (a.T > 0 && a.B > kMaxTokens / a.T) return fail(KDA_ERR_INVALID_ARG, "B*T too large");
+  const int64_t total = (int64_t)a.B * a.T;
+  if (!(a.lower_bound >= -5.0f && a.lower_bound <= 0.0f))
+    return fail(KDA_ERR_INVALID_ARG, "lower_bound %g outside [-5, 0]", (double)a.lower_bound);
+  if (!std::isfinite(a.scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite");
+  if (a.state_dtype != KDA_STATE_BF16 && a.state_dtype != KDA_STATE_FP32)
+    return fail(KDA_ERR_INVALID_ARG, "state_dtype %d invalid", a.state_dtype);
+  if (a.state_layout != KDA_STATE_VK && a.state_layout != KDA_STATE_KV)
+    return fail(KDA_ERR_INVALID_ARG, "state_layout %d invalid", a.state_layout);
+  int32_t N;
+  if (a.cu_seqlens) {
+    if (a.B != 1) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens requires B == 1 (got B=%d)", a.B);
+    if (a.num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must be >= 1 with cu_seqlens", a.num_seqs);
+    N = a.num_seqs;
+  } else {
+    if (a.num_seqs != 0 && a.num_seqs != a.B)
+      return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must equal B=%d without cu_seqlens", a.num_seqs, a.B);
+    N = a.B;
+  }
+  pr->N = N;
+  pr->H_qk = H_qk;
+  pr->total = total;
+  if (N < 1) {
+    // B == 0 without cu_seqlens: nothing to compute and no state to write
+    pr->nothing = true;
+    return KDA_OK;
+  }
+  if (total > 0 && (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.out))
+    return fail(KDA_ERR_INVALID_ARG, "q, k, v, g, beta and out must be non-NULL");
+  if (!a.A_log || !a.dt_bias) return fail(KDA_ERR_INVALID_ARG, "A_log and dt_bias must be non-NULL");
+  const int32_t st = layout(total, a.H, N, a.cp_mode, a.seg_chunks, &pr->lay);
+  if (st != KDA_OK) return st;
+  pr->nothing = total == 0 && !a.final_state;
+  return KDA_OK;
+}
+
+// Carves the workspace ws (already checked to hold pr.lay) and launches the
+// call's kernels on stream s.
+int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s) {
+  const Layout& lay = pr.lay;
+  const kda::Tables t = carve_tables(ws, lay, a.cu_seqlens ? -1 : a.T);
+  const bool cp = lay.seg > 0;
+  kda::Seg sg;
+  sg.M = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;
+  sg.R = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
+  sg.S = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_S]) : nullptr;
+  sg.chk = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_CHK]) : nullptr;
+  sg.fix = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_FIX]) : nullptr;
+  sg.mnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
+  sg.chk_chunks = cp ? kCheckChunks : 0;
+  sg.seg_chunks = cp ? (int)lay.seg : 0;
+  const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
+  const int64_t ms = lay.off[KDA_WS_MAX_SEGS];
+  const int32_t N = pr.N;
+
+  kda::Problem p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.g = static_cast<const uint16_t*>(a.g);
+  p.beta = static_cast<const uint16_t*>(a.beta);
+  p.out = static_cast<uint16_t*>(a.out);
+  p.A_log = a.A_log;
+  p.dt_bias = a.dt_bias;
+  p.init_state = a.initial_state;
+  p.final_state = a.final_state;
+  p.state_fp32 = a.state_dtype == KDA_STATE_FP32;
+  p.state_kv = a.state_layout == KDA_STATE_KV;
+  p.scale = a.scale;
+  p.lower_bound = a.lower_bound;
+  p.H = a.H;
+  p.Hqk = pr.H_qk;
+  p.N = N;
+  p.total_tokens = pr.total;
+
+  hipError_t e;
+  e = kda::launch_index(a.cu_seqlens, N, a.T, pr.total, lay.seg, mc, ms, t, s);
+  // Long units run their first (or only) pass with 4 consumer wavefronts of two
+  // state tiles each, short ones with 8 of one tile (measured: 2-3 % faster
+  // at 256-512 chunks per unit, 4 % slower at 36).  The second pass keeps 8:
+  // it usually only compares, and where it redoes chunks the 4-consumer
+  // kernel would spill.  Both give the same bits.
+  const int64_t unit_chunks = lay.seg > 0 ? lay.seg : (N > 0 ? mc / N : 0);
+  if (e == hipSuccess)
+    e = unit_chunks >= kWideMinChunks ? kda::launch_chunks_c4(p, t, sg, ms, 0, cp, s)
+                                      : kda::launch_chunks(p, t, sg, ms, 0, cp, s);
+  if (cp && e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
@@ -239,106 +384,33 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
                 int32_t num_seqs, int32_t B,
                 int64_t T, int32_t H, int32_t H_qk, int32_t D, void* workspace, size_t workspace_bytes, int32_t cp_mode,
                 int32_t seg_chunks, void* stream) {
+  HostTimer timer;
   g_last_error.clear();
-  // ---- pure argument checks (no HIP calls before these pass) ----
-  if (D != kda::D) return fail(KDA_ERR_UNSUPPORTED, "head dimension %d unsupported (only 128)", D);
-  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARG, "B=%d and T=%lld must be >= 0", B, (long long)T);
-  if (H < 1) return fail(KDA_ERR_INVALID_ARG, "H=%d must be >= 1", H);
-  if (H_qk == 0) H_qk = H;
-  if (H_qk < 1 || H_qk > H || H % H_qk != 0)
-    return fail(KDA_ERR_INVALID_ARG, "H_qk=%d must divide H=%d", H_qk, H);
-  if (T > 0 && B > kMaxTokens / T) return fail(KDA_ERR_INVALID_ARG, "B*T too large");
-  const int64_t total = (int64_t)B * T;
-  if (!(lower_bound >= -5.0f && lower_bound <= 0.0f))
-    return fail(KDA_ERR_INVALID_ARG, "lower_bound %g outside [-5, 0]", (double)lower_bound);
-  if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite");
-  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32)
-    return fail(KDA_ERR_INVALID_ARG, "state_dtype %d invalid", state_dtype);
-  if (state_layout != KDA_STATE_VK && state_layout != KDA_STATE_KV)
-    return fail(KDA_ERR_INVALID_ARG, "state_layout %d invalid", state_layout);
-  int32_t N;
-  if (cu_seqlens) {
-    if (B != 1) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens requires B == 1 (got B=%d)", B);
-    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must be >= 1 with cu_seqlens", num_seqs);
-    N = num_seqs;
-  } else {
-    if (num_seqs != 0 && num_seqs != B)
-      return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must equal B=%d without cu_seqlens", num_seqs, B);
-    N = B;
-  }
-  if (N < 1) {
-    // B == 0 without cu_seqlens: nothing to compute and no state to write
-    return KDA_OK;
-  }
-  if (total > 0 && (!q || !k || !v || !g || !beta || !out))
-    return fail(KDA_ERR_INVALID_ARG, "q, k, v, g, beta and out must be non-NULL");
-  if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARG, "A_log and dt_bias must be non-NULL");
-  Layout lay;
-  const int32_t st = layout(total, H, N, cp_mode, seg_chunks, &lay);
-  if (st != KDA_OK) return st;
-  if (total == 0 && !final_state) return KDA_OK;
+  const FwdArgs a{q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, final_state,
+                  state_dtype, state_layout, cu_seqlens, num_seqs, B, T, H, H_qk, D, cp_mode, seg_chunks};
+  Prepared pr;
+  int32_t st = prepare(a, &pr);
+  if (st != KDA_OK || pr.nothing) return st;
   if (!workspace) return fail(KDA_ERR_INVALID_ARG, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % KDA_WORKSPACE_ALIGN != 0)
     return fail(KDA_ERR_INVALID_ARG, "workspace must be %d-byte aligned", KDA_WORKSPACE_ALIGN);
-  if ((int64_t)workspace_bytes < lay.off[KDA_WS_TOTAL])
+  if ((int64_t)workspace_bytes < pr.lay.off[KDA_WS_TOTAL])
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %lld", workspace_bytes,
-                (long long)lay.off[KDA_WS_TOTAL]);
-
-  // ---- carve ----
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const kda::Tables t = carve_tables(ws, lay, cu_seqlens ? -1 : T);
-  const bool cp = lay.seg > 0;
-  kda::Seg sg;
-  sg.M = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_M]) : nullptr;
-  sg.R = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_R]) : nullptr;
-  sg.S = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_S]) : nullptr;
-  sg.chk = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_CHK]) : nullptr;
-  sg.fix = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_FIX]) : nullptr;
-  sg.mnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
-  sg.chk_chunks = cp ? kCheckChunks : 0;
-  sg.seg_chunks = cp ? (int)lay.seg : 0;
-  const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
-  const int64_t ms = lay.off[KDA_WS_MAX_SEGS];
-
-  kda::Problem p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.g = static_cast<const uint16_t*>(g);
-  p.beta = static_cast<const uint16_t*>(beta);
-  p.out = static_cast<uint16_t*>(out);
-  p.A_log = A_log;
-  p.dt_bias = dt_bias;
-  p.init_state = initial_state;
-  p.final_state = final_state;
-  p.state_fp32 = state_dtype == KDA_STATE_FP32;
-  p.state_kv = state_layout == KDA_STATE_KV;
-  p.scale = scale;
-  p.lower_bound = lower_bound;
-  p.H = H;
-  p.Hqk = H_qk;
-  p.N = N;
-  p.total_tokens = total;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  e = kda::launch_index(cu_seqlens, N, T, total, lay.seg, mc, ms, t, s);
-  // Long units run their first (or only) pass with 4 consumer wavefronts of two
-  // state tiles each, short ones with 8 of one tile (measured: 2-3 % faster
-  // at 256-512 chunks per unit, 4 % slower at 36).  The second pass keeps 8:
-  // it usually only compares, and where it redoes chunks the 4-consumer
-  // kernel would spill.  Both give the same bits.
-  const int64_t unit_chunks = lay.seg > 0 ? lay.seg : (N > 0 ? mc / N : 0);
-  if (e == hipSuccess)
-    e = unit_chunks >= kWideMinChunks ? kda::launch_chunks_c4(p, t, sg, ms, 0, cp, s)
-                                      : kda::launch_chunks(p, t, sg, ms, 0, cp, s);
-  if (cp && e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
-  if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
-  return KDA_OK;
+                (long long)pr.lay.off[KDA_WS_TOTAL]);
+  return launch(a, pr, static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int32_t kda_profile_enable(int32_t enable) {
-  g_prof.on = enable != 0;
+  g_prof.on = (enable & KDA_PROFILE_KERNELS) != 0;
+  g_prof.host = (enable & KDA_PROFILE_HOST) != 0;
+  return KDA_OK;
+}
+
+int32_t kda_profile_host(double* host_us, int64_t* calls) {
+  if (host_us) *host_us = g_prof.host_us;
+  if (calls) *calls = g_prof.host_calls;
+  g_prof.host_us = 0.0;
+  g_prof.host_calls = 0;
   return KDA_OK;
 }
 

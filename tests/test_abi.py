@@ -137,3 +137,4 @@ def test_empty_call_is_a_no_op(lib):
     # B*T == 0 without a final state returns OK with no launch (and no HIP call)
     assert _call(lib, T=0) == 0
     assert _call(lib, B=0, T=10) == 0
+

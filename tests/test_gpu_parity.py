@@ -280,7 +280,7 @@ def test_config2_full_size():
 
 
 def test_config3_full_size():
-    _full("cfg3", seqs=[0, 1, 2, 3, 4, 5, 6], heads=[3])
+    _full("cfg3", seqs=[0, 1, 2, 3, 4, 5, 6], heads=[0, 3, 15])
 
 
 def test_config5_full_size():
@@ -294,7 +294,7 @@ def test_config4_segmented_bit_identical_to_serial(name):
     x = kda_inputs.make_inputs(w)
     d = dev_inputs(x)
     out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
-    check_against_oracle(w, x, out_s, fin_s, seqs=[0] if name == "cfg4a" else [0, 5], heads=[5],
+    check_against_oracle(w, x, out_s, fin_s, seqs=[0] if name == "cfg4a" else [0, 5], heads=[0, 5, 15],
                          final_dtype=w.state_dtype)
     for seg in (0, 64):
         out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="force", seg_chunks=seg)
@@ -304,3 +304,54 @@ def test_config4_segmented_bit_identical_to_serial(name):
         say(f"{name} seg={seg}: out identical={same_o} final identical={same_f} early stops={stops}")
         assert same_o and same_f
         assert stops > 0  # the checkpoint path is the one measured at this size
+
+
+def test_config4_slow_decay_segmented():
+    """T=65536 H=16 at lower_bound -0.1: the start state's influence has not
+    decayed after a segment's first 4 chunks, so the second pass runs every
+    segment >= 1 again from its merged start state.  Segmented against serial
+    and both against the oracle; whether the bits agree is reported."""
+    w = kda_inputs.WORKLOADS["cfg4a_slow"]
+    say(f"case {w.name} serial vs segmented (slow decay)")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
+    out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="auto")
+    import kimi_delta_attention_02_amd as kda
+
+    seg = kda.plan_seg_chunks(w.B * w.T, w.H, w.N, "auto")
+    assert seg > 0
+    stops = _early_stops(w, ws, "auto", 0)
+    same_o = torch.equal(out_c.view(torch.int16), out_s.view(torch.int16))
+    same_f = torch.equal(fin_c, fin_s)
+    say(f"{w.name} seg={seg}: out identical={same_o} final identical={same_f} early stops={stops}")
+    for got_o, got_f in ((out_s, fin_s), (out_c, fin_c)):
+        check_against_oracle(w, x, got_o, got_f, heads=[0, 11], final_dtype=w.state_dtype)
+    # segmented against serial, every chain: the oracle's tolerance with serial as the reference
+    assert_close(to_f64(out_c).reshape(-1), to_f64(out_s).reshape(-1), "segmented vs serial out", stored="bf16")
+    assert_close(to_f64(fin_c).reshape(-1), to_f64(fin_s).reshape(-1), "segmented vs serial final", stored="fp32")
+
+
+def test_two_launch_index_path_end_to_end():
+    """5000 sequences of 3..40 tokens (past the one-workgroup index form's
+    4095): the index scan + fill launches, then the chunk kernel, every chain
+    against the oracle, serial and in 2-chunk segments."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    lens = rng.integers(3, 41, size=5000).tolist()
+    w = kda_inputs.custom(seqlens=lens, H=2, lower_bound=-2.0, seed=77, state_dtype="bf16", name="varlen5000_H2")
+    say(f"case {w.name} tokens={w.T}")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    outs, finals = O.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["A_log"], x["dt_bias"], x["scale"],
+                                 x["lower_bound"], x["initial_state"], x["cu_seqlens"])
+    ref_o = np.concatenate([o.reshape(-1) for o in outs])
+    for cp, seg in (("off", 0), ("force", 2)):
+        out, final, ws = run_gpu(w, x, d, cp_mode=cp, seg_chunks=seg)
+        import kimi_delta_attention_02_amd as kda
+
+        offs = kda.workspace_offsets(w.T, w.H, w.N, cp, seg)
+        cnt = read_ws(ws, offs, "counters", 4, np.int32)
+        assert cnt[0] == sum((L + 15) // 16 for L in lens) and cnt[2] == 0
+        got_o = to_f64(out[0]).reshape(-1)
+        assert_close(got_o, ref_o, f"{w.name} {cp} out", stored="bf16")
+        assert_close(to_f64(final).reshape(-1), finals.reshape(-1), f"{w.name} {cp} final", stored="bf16")
