@@ -122,6 +122,34 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
                 int32_t D, void* workspace, size_t workspace_bytes, int32_t cp_mode, int32_t seg_chunks,
                 void* stream);
 
+/* kda_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments, meaning and errors as kda_fwd, minus the workspace.  Its
+ * scratch is one array of KDA_NOALLOC_SCRATCH_BYTES bytes per GPU, built into
+ * the library and held from the library's first use of that GPU until the
+ * process ends.  The call itself allocates and frees nothing, and never
+ * synchronises.
+ *   - The call runs on the device of `stream` (the current device for NULL).
+ *   - A call whose kda_get_workspace_size(B*T, H, N, cp_mode, seg_chunks)
+ *     exceeds KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_WORKSPACE_TOO_SMALL
+ *     before any launch (a longer seg_chunks, or KDA_CP_OFF, needs less).
+ *     A segmented plan needs about 320 KiB per (segment, head) unit plus the
+ *     index tables: one sequence of 64K tokens at H = 16 on the automatic
+ *     plan takes 85 MiB, a serial plan of it 30 KiB.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; no part of it needs to start at zero.  Calls that may
+ *     overlap on one GPU (other streams, other host threads) race on it and
+ *     must be serialised by the caller.
+ *   - kda_workspace_offsets describes the array's layout for a call, but the
+ *     array is not exposed: its tables cannot be inspected from the host. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128ll << 20)
+
+int32_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                        const void* initial_state, void* final_state, int32_t state_dtype, int32_t state_layout,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T, int32_t H,
+                        int32_t H_qk, int32_t D, int32_t cp_mode, int32_t seg_chunks, void* stream);
+
 /* Byte offsets of the workspace regions for these sizes and plan, so a caller
  * can inspect the index tables and segment maps a kda_fwd call left in its
  * workspace (a varlen call stores its tables; a fixed-length call stores only
@@ -208,7 +236,7 @@ typedef enum {
 } kda_stage;
 
 /* enable: KDA_PROFILE_KERNELS (the kernel events above), KDA_PROFILE_HOST
- * (host time of each kda_fwd call on this thread, from its
+ * (host time of each kda_fwd / kda_fwd_noalloc call on this thread, from its
  * entry to its return: validation, planning and the launches, without the
  * caller's own marshalling), both, or 0. */
 #define KDA_PROFILE_KERNELS 1

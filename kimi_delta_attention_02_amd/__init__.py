@@ -26,6 +26,7 @@ from typing import Optional
 
 __all__ = [
     "fwd",
+    "fwd_noalloc",
     "prepare",
     "PreparedFwd",
     "read_counters",
@@ -92,6 +93,9 @@ def load_library():
     lib.kda_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, vp, i32, i32, vp, i32, i32, i64, i32, i32,
                             i32, vp, sz, i32, i32, vp]
     lib.kda_fwd.restype = i32
+    lib.kda_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, vp, i32, i32, vp, i32, i32, i64, i32,
+                                    i32, i32, i32, i32, vp]
+    lib.kda_fwd_noalloc.restype = i32
     lib.kda_profile_enable.argtypes = [i32]
     lib.kda_profile_enable.restype = i32
     lib.kda_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32]
@@ -305,7 +309,7 @@ def _ptr(t):
 
 def _fwd_args(c: _Checked, q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state, final_state,
               cu_seqlens, state_layout):
-    """kda_fwd's arguments before the workspace."""
+    """kda_fwd's arguments before the workspace (shared with kda_fwd_noalloc)."""
     import torch
 
     return (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(c.out), _ptr(A_log), _ptr(dt_bias),
@@ -391,6 +395,33 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
     _log_call(c, cpm, seg_chunks)
     if check:
         _raise_on_flags(workspace, c, cpm, seg_chunks)
+    return c.out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES of include/kda.h
+
+
+def fwd_noalloc(q, k, v, g, beta, scale: float, out, *, A_log, dt_bias, lower_bound: float, initial_state=None,
+                final_state=None, cu_seqlens=None, cp_mode="auto", seg_chunks: int = 0, state_layout: str = "vk"):
+    """fwd for callers that cannot allocate: the library's per-GPU scratch
+    array (NOALLOC_SCRATCH_BYTES) replaces the workspace, and out must be
+    given.  Calls that may overlap on one GPU race on that array.  A call that
+    needs more scratch raises KdaError (status -3) before any launch."""
+    import torch
+
+    if out is None:
+        raise ValueError("fwd_noalloc needs out: it allocates nothing")
+    lib = load_library()
+    cpm = _cp(cp_mode)
+    c = _check_fwd(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, state_layout)
+    with torch.cuda.device_of(q):
+        stream = torch.cuda.current_stream(c.device).cuda_stream
+        st = lib.kda_fwd_noalloc(*_fwd_args(c, q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state,
+                                            final_state, cu_seqlens, state_layout),
+                                 cpm, int(seg_chunks), stream)
+    if st != 0:
+        _raise(st)
+    _log_call(c, cpm, seg_chunks)
     return c.out
 
 

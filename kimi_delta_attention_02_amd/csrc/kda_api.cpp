@@ -29,6 +29,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -332,6 +333,45 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   return KDA_OK;
 }
 
+// ---- scratch of the no-allocation entry point ----
+// One array per GPU, held from the library's first use of that GPU until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address is taken once per device with that device
+// current (hipGetSymbolAddress) and only that address is used.
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<uint8_t*> g_scratch_ptr;  // by device ordinal; null until first use there
+
+// The device address of `scratch` on the device stream s runs on (the current
+// device for the null stream).
+int32_t scratch_for_stream(hipStream_t s, uint8_t** out) {
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(KDA_ERR_HIP, "cannot find the stream's device: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || !p)
+      return fail(KDA_ERR_HIP, "hipGetSymbolAddress of the scratch array failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    if (reinterpret_cast<uintptr_t>(p) % KDA_WORKSPACE_ALIGN != 0)
+      return fail(KDA_ERR_HIP, "scratch array on device %d is not %d-byte aligned", dev, KDA_WORKSPACE_ALIGN);
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -398,6 +438,30 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %lld", workspace_bytes,
                 (long long)pr.lay.off[KDA_WS_TOTAL]);
   return launch(a, pr, static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int32_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                        void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                        const void* initial_state, void* final_state, int32_t state_dtype, int32_t state_layout,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t H_qk,
+                        int32_t D, int32_t cp_mode, int32_t seg_chunks, void* stream) {
+  HostTimer timer;
+  g_last_error.clear();
+  const FwdArgs a{q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, final_state,
+                  state_dtype, state_layout, cu_seqlens, num_seqs, B, T, H, H_qk, D, cp_mode, seg_chunks};
+  Prepared pr;
+  int32_t st = prepare(a, &pr);
+  if (st != KDA_OK || pr.nothing) return st;
+  if (pr.lay.off[KDA_WS_TOTAL] > (int64_t)KDA_NOALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %lld bytes of scratch, more than the %lld bytes the no-allocation entry point "
+                "holds (a longer seg_chunks, or cp_mode off, needs less)",
+                (long long)pr.lay.off[KDA_WS_TOTAL], (long long)KDA_NOALLOC_SCRATCH_BYTES);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = nullptr;
+  st = scratch_for_stream(s, &ws);
+  if (st != KDA_OK) return st;
+  return launch(a, pr, ws, s);
 }
 
 int32_t kda_profile_enable(int32_t enable) {

@@ -138,3 +138,41 @@ def test_empty_call_is_a_no_op(lib):
     assert _call(lib, T=0) == 0
     assert _call(lib, B=0, T=10) == 0
 
+
+def _call_noalloc(lib, **kw):
+    """kda_fwd_noalloc with fake, never-dereferenced pointers (every case here
+    fails validation before any device access or HIP call)."""
+    P = ctypes.c_void_p(0x10000)
+    a = dict(q=P, k=P, v=P, g=P, beta=P, scale=0.1, out=P, A_log=P, dt_bias=P, lower_bound=-1.0,
+             initial_state=None, final_state=None, state_dtype=1, state_layout=0, cu_seqlens=None, num_seqs=0, B=1,
+             T=64, H=2, H_qk=0, D=128, cp_mode=0, seg_chunks=0, stream=None)
+    a.update(kw)
+    return lib.kda_fwd_noalloc(*a.values())
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == kda.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    # one-chunk segments over 64K tokens at H = 16: 4097 x 16 units of 320 KiB
+    (dict(T=65536, H=16, cp_mode=2, seg_chunks=1), -3, "scratch"),
+    (dict(D=64), -2, "head dimension"),
+    (dict(lower_bound=0.5), -1, "lower_bound"),
+    (dict(q=None), -1, "non-NULL"),
+    (dict(B=2, cu_seqlens=ctypes.c_void_p(0x2000), num_seqs=2), -1, "B == 1"),
+])
+def test_noalloc_rejects_before_launch(lib, kw, status, msg):
+    st = _call_noalloc(lib, **kw)
+    assert st == status
+    assert msg in lib.kda_last_error().decode()
+
+
+def test_noalloc_limit_covers_every_workload_plan():
+    import kda_inputs
+
+    for w in kda_inputs.WORKLOADS.values():
+        for cp in ("auto", "off"):
+            assert kda.get_workspace_size(w.B * w.T, w.H, w.N, cp) <= kda.NOALLOC_SCRATCH_BYTES, (w.name, cp)

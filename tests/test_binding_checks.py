@@ -100,6 +100,19 @@ def test_fwd_argument_checks(over, exc, msg):
     assert msg in str(ei.value)
 
 
+def test_noalloc_needs_out_and_applies_the_same_checks():
+    t = _tensors()
+    with pytest.raises(ValueError, match="needs out"):
+        kda.fwd_noalloc(t["q"], t["k"], t["v"], t["g"], t["beta"], 0.1, None, A_log=t["A_log"], dt_bias=t["dt_bias"],
+                        lower_bound=-1.0)
+    with pytest.raises(TypeError, match="beta must be torch.bfloat16"):
+        kda.fwd_noalloc(t["q"], t["k"], t["v"], t["g"], t["beta"].float(), 0.1, torch.zeros_like(t["q"]),
+                        A_log=t["A_log"], dt_bias=t["dt_bias"], lower_bound=-1.0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.fwd_noalloc(t["q"], t["k"], t["v"], t["g"], t["beta"], 0.1, torch.zeros_like(t["q"]), A_log=t["A_log"],
+                        dt_bias=t["dt_bias"], lower_bound=-1.0)
+
+
 def test_prepare_applies_the_same_checks():
     t = _tensors()
     with pytest.raises(TypeError, match="dt_bias must be torch.float32"):
