@@ -63,6 +63,13 @@ enum Role { RECUR = 0, PRE = 1 };
 #ifndef KDA_CONSUMERS
 #define KDA_CONSUMERS 8
 #endif
+// Row tiles of the state update whose LDS operands a consumer step reads
+// together with the chunk's other operands, before its first product (the
+// rest are read during the update).  Four measured best in both builds
+// (1.5-2.8 % faster than none; eight spills in the first-pass kernels).
+#ifndef KDA_HOIST
+#define KDA_HOIST 4
+#endif
 constexpr int NPW = 4;                  // producer wavefronts
 constexpr int NCW = KDA_CONSUMERS;      // consumer wavefronts
 constexpr int TPW = (D / 16) / NCW;     // 16-column state tiles per consumer wavefront
@@ -426,16 +433,29 @@ __device__ __forceinline__ UOps tile_u(f32x4 Y, u32x4 tf, const u32x2* v) {
 // the sum is formed at that scale before the decay: its fp32 rounding is then
 // relative to the Khat^T U term, as in the unscaled form.
 template <int NT>
-__device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const UOps (&u)[NT], const Slot& sl, int g, int c) {
+__device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const UOps (&u)[NT], u32x4 (&kp)[8],
+                                             f32x4 (&gc)[8], const Slot& sl, int g, int c) {
+#pragma unroll
+  for (int tt = KDA_HOIST; tt < 8; ++tt) {
+    kp[tt] = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
+    gc[tt] = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
+  }
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    const u32x4 kp = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
-    const f32x4 gc = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
 #pragma unroll
     for (int jj = 0; jj < NT; ++jj) {
-      const f32x4 acc = mfma_k32(kp, u[jj].b1, S[jj][tt]);
-      S[jj][tt] = mfma_k32(kp, u[jj].b2, acc) * gc;
+      const f32x4 acc = mfma_k32(kp[tt], u[jj].b1, S[jj][tt]);
+      S[jj][tt] = mfma_k32(kp[tt], u[jj].b2, acc) * gc[tt];
     }
+  }
+}
+
+// The Ktil and gamma_C fragments of the update, for every row tile
+__device__ __forceinline__ void update_operands(const Slot& sl, int g, int c, u32x4 (&kp)[8], f32x4 (&gc)[8]) {
+#pragma unroll
+  for (int tt = 0; tt < KDA_HOIST; ++tt) {
+    kp[tt] = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
+    gc[tt] = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
   }
 }
 
@@ -890,13 +910,17 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       if (WO) qb[s] = sl.qbf[s][L];
     }
     const u32x4 tf = sl.tf[L];
+    u32x4 kp[8];
+    f32x4 gc[8];
+    update_operands(sl, g, c, kp, gc);
     u32x2 v[TPW];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) v[jj] = slot_v(sl, g, col0 + 16 * jj + c);
+    // every read of the slot is issued here, before any of it is used
+    __builtin_amdgcn_sched_barrier(0);
     u32x2 Sb[TPW][8];
 #pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) {
-      v[jj] = slot_v(sl, g, col0 + 16 * jj + c);
-      pack_tile(S[jj], Sb[jj]);
-    }
+    for (int jj = 0; jj < TPW; ++jj) pack_tile(S[jj], Sb[jj]);
     // Y = Kbar S and O^T: independent MFMA chains
     f32x4 Y[TPW], Ot[TPW];
     tiles_y<TPW>(Sb, kb, Y);
@@ -922,7 +946,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj) *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot[jj]);
     }
-    tiles_update<TPW>(S, u, sl, g, c);
+    tiles_update<TPW>(S, u, kp, gc, sl, g, c);
     wg_store(&sm.done[slot][cw], lc);
     seen = __builtin_amdgcn_readfirstlane(peek);
     return true;
