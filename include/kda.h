@@ -185,7 +185,13 @@ typedef enum {
                                shorter last segments, each group in segment order (all -1 past the
                                live count) */
   KDA_WS_SEG_FIX,           /* fp32 [max_segs][H][128][128] state after a segment's first 4 chunks as the
-                               first pass's block of the previous segment reached it (CP only) */
+                               first pass's block of the previous segment reached it, stored only when
+                               that block could not compare it with the checkpoint (CP only) */
+  KDA_WS_SEG_SYNC,          /* uint32 [max_segs][H][16] per segment and 16-column block b of the state:
+                               word b, the call's number once its first-pass block has stored those
+                               checkpoint columns; word 8 + b, (call number << 2) | result of the
+                               comparison made at the end of the previous segment's first-pass block
+                               (1 equal, 2 differ, 3 not compared); cleared by the second pass (CP only) */
   KDA_WS_MAX_CHUNKS,        /* (count, not an offset) chunk-table capacity */
   KDA_WS_MAX_SEGS,          /* (count, not an offset) segment-table capacity */
   KDA_WS_TOTAL,             /* total bytes (= kda_get_workspace_size) */

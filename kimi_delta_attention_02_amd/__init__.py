@@ -53,7 +53,8 @@ CHUNK = 16
 WS_ALIGN = 256
 WS_FIELDS = [
     "counters", "seq_start", "seq_len", "seq_chunk_off", "seq_seg_off", "chunk_tab", "seg_tab",
-    "seg_m", "seg_r", "seg_s", "seg_mnz", "seg_chk", "seq_full_off", "unit_tab", "seg_fix", "max_chunks", "max_segs", "total",
+    "seg_m", "seg_r", "seg_s", "seg_mnz", "seg_chk", "seq_full_off", "unit_tab", "seg_fix", "seg_sync", "max_chunks",
+    "max_segs", "total",
 ]
 _CP = {"auto": 0, "off": 1, "force": 2, None: 0, False: 1, True: 2}
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP error"}

@@ -24,6 +24,8 @@
 // launches no merge at all.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -105,6 +107,16 @@ int64_t max_chunks_for(int64_t total, int32_t N) {
   return (total + 15 * (int64_t)N) / kda::C;
 }
 
+// A number for each call, written into the sync words of its segments: words
+// an earlier call left in a workspace then never match the current call's.
+// Zero is skipped, since fresh memory often holds zeros.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
 // segment length in chunks (0 = serial); negative status on bad arguments
 int32_t plan(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg_chunks) {
   if (total < 0 || total > kMaxTokens) return fail(KDA_ERR_INVALID_ARG, "total_tokens %lld out of range", (long long)total);
@@ -161,6 +173,7 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
   take(KDA_WS_SEQ_FULL_OFF, 4 * ((int64_t)N + 1));
   take(KDA_WS_UNIT_TAB, 32 * ms);
   take(KDA_WS_SEG_FIX, seg_bytes);
+  take(KDA_WS_SEG_SYNC, seg > 0 ? ms * H * 16 * 4 : 0);
   out->off[KDA_WS_MAX_CHUNKS] = mc;
   out->off[KDA_WS_MAX_SEGS] = ms;
   out->off[KDA_WS_TOTAL] = o;
@@ -291,6 +304,8 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   sg.chk = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_CHK]) : nullptr;
   sg.fix = cp ? reinterpret_cast<float*>(ws + lay.off[KDA_WS_SEG_FIX]) : nullptr;
   sg.mnz = cp ? reinterpret_cast<int32_t*>(ws + lay.off[KDA_WS_SEG_MNZ]) : nullptr;
+  sg.sync = cp ? reinterpret_cast<uint32_t*>(ws + lay.off[KDA_WS_SEG_SYNC]) : nullptr;
+  sg.epoch = next_epoch();
   sg.chk_chunks = cp ? kCheckChunks : 0;
   sg.seg_chunks = cp ? (int)lay.seg : 0;
   const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
@@ -310,6 +325,11 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   p.final_state = a.final_state;
   p.state_fp32 = a.state_dtype == KDA_STATE_FP32;
   p.state_kv = a.state_layout == KDA_STATE_KV;
+  {
+    const uintptr_t bytes = (uintptr_t)N * (uintptr_t)a.H * kda::D * kda::D * (p.state_fp32 ? 4u : 2u);
+    const uintptr_t f = (uintptr_t)a.final_state, i = (uintptr_t)a.initial_state;
+    p.final_early = a.final_state && (!a.initial_state || f + bytes <= i || i + bytes <= f);
+  }
   p.scale = a.scale;
   p.lower_bound = a.lower_bound;
   p.H = a.H;
@@ -325,10 +345,20 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   // it usually only compares, and where it redoes chunks the 4-consumer
   // kernel would spill.  Both give the same bits.
   const int64_t unit_chunks = lay.seg > 0 ? lay.seg : (N > 0 ? mc / N : 0);
+  // A fixed-length call knows its unit count, N sequences of ns segments: its
+  // grid has no idle rows, which would be dispatched only once a CU frees up,
+  // after the busy blocks.  (A varlen call's count is known on the device
+  // only; its grid covers the table's capacity.)
+  int64_t rows = ms;
+  if (!a.cu_seqlens) {
+    const int64_t nc = (a.T + kda::C - 1) / kda::C;
+    const int64_t nsq = lay.seg > 0 ? (nc > 0 ? (nc + lay.seg - 1) / lay.seg : 1) : 1;
+    rows = std::min(ms, (int64_t)N * nsq);
+  }
   if (e == hipSuccess)
-    e = unit_chunks >= kWideMinChunks ? kda::launch_chunks_c4(p, t, sg, ms, 0, cp, s)
-                                      : kda::launch_chunks(p, t, sg, ms, 0, cp, s);
-  if (cp && e == hipSuccess) e = kda::launch_chunks(p, t, sg, ms, 1, cp, s);
+    e = unit_chunks >= kWideMinChunks ? kda::launch_chunks_c4(p, t, sg, rows, 0, cp, s)
+                                      : kda::launch_chunks(p, t, sg, rows, 0, cp, s);
+  if (cp && e == hipSuccess) e = kda::launch_chunks(p, t, sg, rows, 1, cp, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   return KDA_OK;
 }

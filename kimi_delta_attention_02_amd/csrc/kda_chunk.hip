@@ -52,8 +52,6 @@ namespace kda {
 
 namespace {
 
-enum Role { RECUR = 0, PRE = 1 };
-
 // Consumer wavefronts: 8, one 16-column state tile each (kda_chunk_kernel).
 // The file is also built with KDA_CONSUMERS=4, two tiles each, into
 // kda_chunk_kernel_c4: a consumer then shares its per-chunk operand loads,
@@ -564,6 +562,51 @@ __device__ __forceinline__ void store_state_kv(const f32x4 (&S)[NT][8], float* d
       }
 }
 
+// A state handed between blocks of one launch, which may run on different
+// XCDs, each with its own L2: it is written and read with device-coherent
+// (agent-scope) accesses, 8 bytes at a time, so no cache needs to be written
+// back or invalidated around it.  [V][K] fp32 layout as store_state.
+__device__ __forceinline__ uint64_t pair_bits(float a, float b) {
+  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+}
+
+template <int NT>
+__device__ __forceinline__ void store_state_coherent(const f32x4 (&S)[NT][8], float* dst, long long base, int col0,
+                                                     int g, int c) {
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      uint64_t* d = reinterpret_cast<uint64_t*>(dst + base + (long long)(col0 + 16 * jj + c) * D + 16 * tt + 4 * g);
+      __hip_atomic_store(d, pair_bits(S[jj][tt][0], S[jj][tt][1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(d + 1, pair_bits(S[jj][tt][2], S[jj][tt][3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// True if every state entry of this lane equals the state at src bit for bit
+// (device-coherent loads, all issued before any compare).
+template <int NT>
+__device__ __forceinline__ bool same_bits_coherent(const f32x4 (&S)[NT][8], float* src, long long base, int col0,
+                                                   int g, int c) {
+  uint64_t x[NT][8][2];
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      uint64_t* d = reinterpret_cast<uint64_t*>(src + base + (long long)(col0 + 16 * jj + c) * D + 16 * tt + 4 * g);
+      x[jj][tt][0] = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      x[jj][tt][1] = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  uint64_t diff = 0;
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      diff |= (pair_bits(S[jj][tt][0], S[jj][tt][1]) ^ x[jj][tt][0]) |
+              (pair_bits(S[jj][tt][2], S[jj][tt][3]) ^ x[jj][tt][1]);
+  return diff == 0u;
+}
+
 // Segment merge for this wavefront's column tiles: S <- M S + R, the affine map
 // of one segment (M from a start state, R from zero).  M and R are stored
 // [v][k] like the states (Mt[p][k] = M[k][p]); bit b of nz is set when columns
@@ -614,6 +657,20 @@ __device__ __forceinline__ void store_final_piece(const Problem& p, long long st
     reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + state_base)[i] = v;
   } else {
     reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + state_base)[i] = pack4(v);
+  }
+}
+
+// A segment's R written to the caller's final state by the whole block (all
+// loads issued before any store).
+__device__ __forceinline__ void final_from_R(const Problem& p, const Seg& sg, long long seg_base, long long state_base) {
+  const f32x4* r = reinterpret_cast<const f32x4*>(sg.R + seg_base);
+  f32x4 vr[PIECES];
+#pragma unroll
+  for (int q = 0; q < PIECES; ++q) vr[q] = r[min((int)threadIdx.x + NTHREADS * q, D * D / 4 - 1)];
+#pragma unroll
+  for (int q = 0; q < PIECES; ++q) {
+    const int i = threadIdx.x + NTHREADS * q;
+    if (i < D * D / 4) store_final_piece(p, state_base, i, vr[q]);
   }
 }
 
@@ -673,9 +730,15 @@ struct Unit {
   int sidx, seq, cb, ce, j, start, len;
 };
 
-template <int ROLE, int phase>
+// MODE 0: a sequence of a serial call from its initial state.
+// MODE 1: first pass of a segmented call: segment 0 of each sequence from the
+//         initial state, every later segment (pre) from a zero state, with its
+//         transition M while that is nonzero.
+// MODE 2: second pass of a segmented call: segments >= 1 from their start states.
+template <int MODE>
 __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tables& t, const Seg& sg,
                                            const Unit& u, int h) {
+  constexpr int phase = MODE == 2 ? 1 : 0;
   const int sidx = u.sidx;
   const int seq = u.seq;
   const int cb = u.cb;
@@ -689,14 +752,8 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   const int seg_c = sg.seg_chunks;
   const int ns = seg_c > 0 ? (seq_nc > 0 ? (seq_nc + seg_c - 1) / seg_c : 1) : 1;
   const int first_chunk = cb - j * seg_c;
-  // RECUR, phase 0: segment 0 of every sequence from the initial state;
-  // RECUR, phase 1: segments >= 1 from their merged start states;
-  // PRE (first pass of a segmented call): segments >= 1 from a zero state.
-  if (ROLE == RECUR) {
-    if (phase == 0 ? (j != 0) : (j == 0)) return;
-  } else {
-    if (j == 0) return;
-  }
+  if (MODE == 2 && j == 0) return;  // segment 0 has its true start state in the first pass
+  const bool pre = MODE == 1 && j > 0;
 
   const int H = p.H;
   const int hq = h / (H / p.Hqk);  // q/k head of this head
@@ -718,11 +775,11 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   // so each consumer compares its own columns; the block stops when all agree.
   const int K = sg.chk_chunks;
   const bool has_chk = j > 0 && K > 0 && nch > K;
-  const int o_from = ROLE == PRE ? (has_chk ? K : nch) : 0;  // first chunk whose output this pass writes
-  const bool may_stop = ROLE == RECUR && phase == 1 && has_chk;
+  const int o_from = pre ? (has_chk ? K : nch) : 0;  // first chunk whose output this pass writes
+  const bool may_stop = MODE == 2 && has_chk;
   // a last segment without a checkpoint: the first pass has nothing to hand on
   // (no segment after it needs its map, and the second pass runs it whole)
-  if (ROLE == PRE && j == ns - 1 && !has_chk) return;
+  if (pre && j == ns - 1 && !has_chk) return;
   // The first pass goes on for K chunks into the next segment of the sequence
   // (when that one has a checkpoint) from its own end state, which is the next
   // segment's start state when this is segment 0 or its M is exactly zero.
@@ -742,14 +799,47 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   // its start state (the previous segment's R, kept when that segment's M is
   // zero; or S_1).  If the state it reached equals the checkpoint bit for bit,
   // every output of the segment is final and the block has nothing to do.
-  if (ROLE == RECUR && phase == 1 && has_chk) {
-    const int32_t* nzf = j >= 2 ? sg.mnz + ((long long)(sidx - 1) * H + h) * (D / 16) : nullptr;
-    const bool decided = (j == ns - 1 && p.final_state)
-                             ? decided_at_checkpoint<true>(p, sg, nzf, seg_base, state_base)
-                             : decided_at_checkpoint<false>(p, sg, nzf, seg_base, state_base);
-    if (decided) {
-      if (threadIdx.x == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
-      return;
+  // The previous segment's block compared the two at its end, per 16-column
+  // block, and left the results in this segment's sync words (1: equal, 2:
+  // not, 3: not compared, that block's fix columns stored for the comparison
+  // here).  The sync words have served the first pass once read; they are
+  // cleared for the next call, so that a later call (a replayed graph, whose
+  // epoch does not change, too) never reads this call's words.
+  if (MODE == 2) {
+    uint32_t* sy = sg.sync + ((long long)sidx * H + h) * 16;
+    uint32_t w[D / 16];
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b) w[b] = sy[8 + b];
+    __syncthreads();  // every thread has read them before they are cleared
+    if (threadIdx.x < 16) sy[threadIdx.x] = 0u;
+    if (has_chk) {
+      const int32_t* nzf = j >= 2 ? sg.mnz + ((long long)(sidx - 1) * H + h) * (D / 16) : nullptr;
+      bool nz = false;  // the previous segment's M is not exactly zero: its R is not this start state
+      int n_equal = 0, n_differ = 0;
+#pragma unroll
+      for (int b = 0; b < D / 16; ++b) {
+        if (nzf) nz = nz || nzf[b] != 0;
+        const uint32_t code = (w[b] >> 2) == (sg.epoch & 0x3FFFFFFFu) ? (w[b] & 3u) : 3u;
+        n_equal += code == 1u;
+        n_differ += code == 2u;
+      }
+      // the final state is this segment's R; the first pass wrote it already
+      // unless it may alias the initial state
+      const bool last_final = j == ns - 1 && p.final_state && !p.final_early;
+      bool decided = false;
+      if (!nz && n_differ == 0) {
+        if (n_equal == D / 16) {
+          decided = true;
+          if (last_final) final_from_R(p, sg, seg_base, state_base);
+        } else {
+          decided = last_final ? decided_at_checkpoint<true>(p, sg, nzf, seg_base, state_base)
+                               : decided_at_checkpoint<false>(p, sg, nzf, seg_base, state_base);
+        }
+      }
+      if (decided) {
+        if (threadIdx.x == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
+        return;
+      }
     }
   }
 
@@ -952,31 +1042,59 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     return true;
   };
 
-  if (ROLE == RECUR) {
-    f32x4 S[TPW][8];
-    if (phase == 1) {
-      // Start state of segment j >= 1 (merge): S_j = M_{j-1} S_{j-1} + R_{j-1}.
-      // Walk back to the nearest segment i0 whose start state is stored as is:
-      // segment 1 (S_1, from segment 0's block) or a segment after one whose M
-      // is exactly zero (then S_i0 = R_{i0-1}); then apply the maps of
-      // segments i0 .. j-1 in order.  With every M zero this is one load.
-      auto seg_at = [&](int m) { return ((long long)(sidx - (j - m)) * H + h) * D * D; };
-      auto nz_bits = [&](int m) {
-        const int32_t* f = sg.mnz + ((long long)(sidx - (j - m)) * H + h) * (D / 16);
-        uint32_t b = 0;
+  // The first pass's K chunks into the next segment (ext > 0), from this
+  // block's end state S.  Each consumer then compares its columns with the
+  // next segment's checkpoint, which the same wavefront of that segment's
+  // block (same launch) has usually published by then, and leaves the result
+  // for the second pass per 16-column block; where the checkpoint is not yet
+  // published (that block has not run far enough), the comparison is left to
+  // the second pass, for which these columns are stored in fix.  Whether S was
+  // the next segment's true start state is not decided here: the second pass
+  // reads this segment's M flags for that.  (A stale fix column of a block
+  // found equal here can only match the checkpoint if it holds the same bits.)
+  auto extend = [&](f32x4 (&S)[TPW][8], bool ok) {
+    for (int e = 0; ok && e < ext; ++e) ok = step_s(nch + e, S, WithOut{});
+    uint32_t* nsy = sg.sync + ((long long)(sidx + 1) * H + h) * 16;
+    const int b0 = col0 / 16;  // this wavefront's first 16-column block
+    uint32_t code = 3u;
+    if (ok) {
+      // the checkpoint's columns are read only once their flags are seen (a
+      // branch on the flags' values) and with coherent loads, so they are the
+      // ones stored before the flags
+      bool ready = true;
 #pragma unroll
-        for (int q = 0; q < D / 16; ++q) b |= (f[q] != 0 ? 1u : 0u) << q;
-        return b;
-      };
-      int i0 = j;
-      while (i0 >= 2 && nz_bits(i0 - 1) != 0) --i0;
-      load_state<TPW>(S, i0 == 1 ? sg.S + seg_at(1) : sg.R + seg_at(i0 - 1), true, 0, col0, g, c);
-      for (int m = i0; m < j; ++m) apply_map<TPW>(S, sg.M + seg_at(m), sg.R + seg_at(m), nz_bits(m), col0, g, c);
-    } else if (p.state_kv && p.init_state) {
-      load_state_kv<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
-    } else {
-      load_state<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
+      for (int jj = 0; jj < TPW; ++jj)
+        ready = ready && (uint32_t)__builtin_amdgcn_readfirstlane((int)__hip_atomic_load(
+                             &nsy[b0 + jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == sg.epoch;
+      if (ready)
+        code = __builtin_amdgcn_ballot_w64(!same_bits_coherent<TPW>(S, sg.chk, fix_base, col0, g, c)) == 0 ? 1u : 2u;
     }
+    if (code == 3u && ok) store_state<TPW>(S, sg.fix, nullptr, fix_base, col0, g, c);
+    if (L == 0) {
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) nsy[8 + b0 + jj] = (sg.epoch << 2) | code;
+    }
+  };
+
+  if constexpr (MODE == 2) {
+    f32x4 S[TPW][8];
+    // Start state of segment j >= 1 (merge): S_j = M_{j-1} S_{j-1} + R_{j-1}.
+    // Walk back to the nearest segment i0 whose start state is stored as is:
+    // segment 1 (S_1, from segment 0's block) or a segment after one whose M
+    // is exactly zero (then S_i0 = R_{i0-1}); then apply the maps of
+    // segments i0 .. j-1 in order.  With every M zero this is one load.
+    auto seg_at = [&](int m) { return ((long long)(sidx - (j - m)) * H + h) * D * D; };
+    auto nz_bits = [&](int m) {
+      const int32_t* f = sg.mnz + ((long long)(sidx - (j - m)) * H + h) * (D / 16);
+      uint32_t b = 0;
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q) b |= (f[q] != 0 ? 1u : 0u) << q;
+      return b;
+    };
+    int i0 = j;
+    while (i0 >= 2 && nz_bits(i0 - 1) != 0) --i0;
+    load_state<TPW>(S, i0 == 1 ? sg.S + seg_at(1) : sg.R + seg_at(i0 - 1), true, 0, col0, g, c);
+    for (int m = i0; m < j; ++m) apply_map<TPW>(S, sg.M + seg_at(m), sg.R + seg_at(m), nz_bits(m), col0, g, c);
     int lc = 0;
     bool ok = true;
     const int lim = may_stop ? K : nch;
@@ -1010,102 +1128,146 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       if (stopped && cw == 0 && L == 0) atomicAdd(&t.counters[CNT_EARLY_STOPS], 1);
       for (; ok && !stopped && lc < nch; ++lc) ok = step_s(lc, S, WithOut{});
     }
-    if (j == ns - 1) {
-      if (p.final_state) {  // the caller's final state, in its dtype and layout
-        // stopped: the end state is the first pass's R of this segment
-        if (stopped) load_state<TPW>(S, sg.R, true, seg_base, col0, g, c);
-        float* dst32 = p.state_fp32 ? static_cast<float*>(p.final_state) : nullptr;
-        uint16_t* dst16 = p.state_fp32 ? nullptr : static_cast<uint16_t*>(p.final_state);
-        if (p.state_kv)
-          store_state_kv<TPW>(S, dst32, dst16, state_base, col0, g, c);
-        else
-          store_state<TPW>(S, dst32, dst16, state_base, col0, g, c);
+    // the caller's final state, in its dtype and layout; stopped: the end
+    // state is the first pass's R of this segment, which that pass has written
+    // there already unless the final state may alias the initial state
+    if (j == ns - 1 && p.final_state && !(stopped && p.final_early)) {
+      if (stopped) load_state<TPW>(S, sg.R, true, seg_base, col0, g, c);
+      float* dst32 = p.state_fp32 ? static_cast<float*>(p.final_state) : nullptr;
+      uint16_t* dst16 = p.state_fp32 ? nullptr : static_cast<uint16_t*>(p.final_state);
+      if (p.state_kv)
+        store_state_kv<TPW>(S, dst32, dst16, state_base, col0, g, c);
+      else
+        store_state<TPW>(S, dst32, dst16, state_base, col0, g, c);
+    }
+  } else {
+    // First pass (or a serial call): the state S from the initial state, or,
+    // for a segment >= 1 (pre), R from a zero state together with M from the
+    // identity (V = 0).  A column of M evolves on its own (U = -T' Kbar M
+    // needs only that column), and a column that is exactly zero stays zero
+    // (every product with it is zero and gamma_C is finite).  Once this
+    // wavefront's columns of M have underflowed to zero they are no longer
+    // computed or stored, and R goes on alone through the same step as S.
+    f32x4 S[TPW][8];
+    int lc = 0;
+    bool ok = true;
+    // a stored checkpoint's flags, once its coherent stores have completed (one
+    // chunk later, so that the wait costs nothing)
+    bool pub = false;
+    auto publish = [&]() {
+      if (!pub) return;
+      pub = false;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);  // every count zero: the stores are complete
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (L == 0) {
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj)
+          __hip_atomic_store(&sg.sync[((long long)sidx * H + h) * 16 + col0 / 16 + jj], sg.epoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
-    } else if (phase == 0) {
+    };
+    if (!pre) {
+      if (p.state_kv && p.init_state)
+        load_state_kv<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
+      else
+        load_state<TPW>(S, p.init_state, p.state_fp32, state_base, col0, g, c);
+    } else {
+      f32x4 Ms[TPW][8];
+      bool mzero = false;
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj)
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          S[jj][tt] = zero4();
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = (16 * tt + 4 * g + i == col0 + 16 * jj + c) ? 1.f : 0.f;
+          Ms[jj][tt] = x;
+        }
+      // R and M, with R's output when wo is set (R updated as step_s does)
+      auto step_rm = [&](int lc, auto wo) -> bool {
+        constexpr bool WO = decltype(wo)::value;
+        const int slot = lc % NSLOT;
+        if (!wait_ready(slot, lc)) return false;
+        const Slot& sl = sm.slot[slot];
+        u32x4 kb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
+        const u32x4 tf = sl.tf[L];
+        UOps ur[TPW], um[TPW];
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) {  // one R and one M tile at a time: bounded live range
+          const u32x2 v = slot_v(sl, g, col0 + 16 * jj + c);
+          u32x2 Sb[2][8];
+          pack_tile(S[jj], Sb[0]);
+          pack_tile(Ms[jj], Sb[1]);
+          f32x4 Y[2];
+          tiles_y<2>(Sb, kb, Y);
+          ur[jj] = tile_u(Y[0], tf, &v);
+          um[jj] = tile_u(Y[1], tf, nullptr);
+          if constexpr (WO) {
+            f32x4 Ot = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Ot = mfma_k32(cat(Sb[0][2 * s], Sb[0][2 * s + 1]), sl.qbf[s][L], Ot);
+            Ot = mfma_k32(ur[jj].ua, sl.aqa[L], Ot);
+            Ot = mfma_k32(ur[jj].ua, sl.aqb[L], Ot);
+            Slot& slw = sm.slot[slot];
+            *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint32_t bits = tiles_update2<TPW>(S, ur, Ms, um, sl, g, c);
+        wg_store(&sm.done[slot][cw], lc);
+        mzero = __builtin_amdgcn_ballot_w64((bits & 0x7FFFFFFFu) != 0u) == 0;
+        return true;
+      };
+      const int k1 = min(nch, o_from);
+      for (; ok && lc < k1 && !mzero; ++lc) ok = step_rm(lc, NoOut{});
+      for (; ok && lc < k1; ++lc) ok = step_s(lc, S, NoOut{});
+      if (ok && has_chk) {
+        // published to the previous segment's block, which compares it at its
+        // end: coherent stores, whose flags follow after the next chunk
+        store_state_coherent<TPW>(S, sg.chk, seg_base, col0, g, c);
+        pub = true;
+      }
+      for (; ok && lc < nch && !mzero; ++lc) {
+        ok = step_rm(lc, WithOut{});
+        publish();
+      }
+      // M is final here (it has underflowed to zero or seen every chunk)
+      if (j < ns - 1) {  // the second pass's merge reads the maps of middle segments
+        if (!mzero) store_state<TPW>(Ms, sg.M, nullptr, seg_base, col0, g, c);
+        if (L == 0) {
+#pragma unroll
+          for (int jj = 0; jj < TPW; ++jj)
+            sg.mnz[((long long)sidx * H + h) * (D / 16) + col0 / 16 + jj] = mzero ? 0 : 1;
+        }
+      }
+    }
+    for (; ok && lc < nch; ++lc) {
+      ok = step_s(lc, S, WithOut{});
+      publish();
+    }
+    // a sequence's last segment: its end state is the caller's final state,
+    // from the initial state (segment 0) or, in a segment >= 1, if the second
+    // pass finds its start state changes nothing (else that pass rewrites it)
+    const bool write_final = j == ns - 1 && p.final_state && (!pre || p.final_early);
+    if (pre && !(write_final && has_chk)) store_state<TPW>(S, sg.R, nullptr, seg_base, col0, g, c);
+    if (write_final) {  // the caller's final state, in its dtype and layout
+      float* dst32 = p.state_fp32 ? static_cast<float*>(p.final_state) : nullptr;
+      uint16_t* dst16 = p.state_fp32 ? nullptr : static_cast<uint16_t*>(p.final_state);
+      if (p.state_kv)
+        store_state_kv<TPW>(S, dst32, dst16, state_base, col0, g, c);
+      else
+        store_state<TPW>(S, dst32, dst16, state_base, col0, g, c);
+    } else if (!pre && j < ns - 1) {
       // segment 0's end state is S_1, where the second pass's merge starts
       // (slot sidx + 1).  The second pass stores nothing here: the next
       // segment's block may be reading its start state in that launch.
       store_state<TPW>(S, sg.S, nullptr, seg_base + (long long)H * D * D, col0, g, c);
     }
-    if (ext > 0 && ok) {  // into the next segment (see above)
-      for (int e = 0; ok && e < ext; ++e) ok = step_s(nch + e, S, WithOut{});
-      if (ok) store_state<TPW>(S, sg.fix, nullptr, fix_base, col0, g, c);
-    }
-  } else {
-    // first pass on the same columns: R (start 0, with Ut) and M (start I,
-    // Ut = 0).  A column of M evolves on its own (U = -T' Kbar M needs only
-    // that column), and a column that is exactly zero stays zero (every product
-    // with it is zero and gamma_C is finite).  Once this wavefront's columns
-    // of M have underflowed to zero they are no longer computed or stored.
-    f32x4 Rs[TPW][8], Ms[TPW][8];
-    bool mzero = false;
-#pragma unroll
-    for (int jj = 0; jj < TPW; ++jj)
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        Rs[jj][tt] = zero4();
-        f32x4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (16 * tt + 4 * g + i == col0 + 16 * jj + c) ? 1.f : 0.f;
-        Ms[jj][tt] = x;
-      }
-    // R and M, with R's output when wo is set (R updated as step_s does)
-    auto step_rm = [&](int lc, auto wo) -> bool {
-      constexpr bool WO = decltype(wo)::value;
-      const int slot = lc % NSLOT;
-      if (!wait_ready(slot, lc)) return false;
-      const Slot& sl = sm.slot[slot];
-      u32x4 kb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
-      const u32x4 tf = sl.tf[L];
-      UOps ur[TPW], um[TPW];
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) {  // one R and one M tile at a time: bounded live range
-        const u32x2 v = slot_v(sl, g, col0 + 16 * jj + c);
-        u32x2 Sb[2][8];
-        pack_tile(Rs[jj], Sb[0]);
-        pack_tile(Ms[jj], Sb[1]);
-        f32x4 Y[2];
-        tiles_y<2>(Sb, kb, Y);
-        ur[jj] = tile_u(Y[0], tf, &v);
-        um[jj] = tile_u(Y[1], tf, nullptr);
-        if constexpr (WO) {
-          f32x4 Ot = zero4();
-#pragma unroll
-          for (int s = 0; s < 4; ++s) Ot = mfma_k32(cat(Sb[0][2 * s], Sb[0][2 * s + 1]), sl.qbf[s][L], Ot);
-          Ot = mfma_k32(ur[jj].ua, sl.aqa[L], Ot);
-          Ot = mfma_k32(ur[jj].ua, sl.aqb[L], Ot);
-          Slot& slw = sm.slot[slot];
-          *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const uint32_t bits = tiles_update2<TPW>(Rs, ur, Ms, um, sl, g, c);
-      wg_store(&sm.done[slot][cw], lc);
-      mzero = __builtin_amdgcn_ballot_w64((bits & 0x7FFFFFFFu) != 0u) == 0;
-      return true;
-    };
-    int lc = 0;
-    bool ok = true;
-    const int k1 = min(nch, o_from);
-    for (; ok && lc < k1 && !mzero; ++lc) ok = step_rm(lc, NoOut{});
-    for (; ok && lc < k1; ++lc) ok = step_s(lc, Rs, NoOut{});
-    if (ok && has_chk) store_state<TPW>(Rs, sg.chk, nullptr, seg_base, col0, g, c);
-    for (; ok && lc < nch && !mzero; ++lc) ok = step_rm(lc, WithOut{});
-    for (; ok && lc < nch; ++lc) ok = step_s(lc, Rs, WithOut{});
-    store_state<TPW>(Rs, sg.R, nullptr, seg_base, col0, g, c);
-    if (j < ns - 1) {  // the second pass's merge reads the maps of middle segments
-      if (!mzero) store_state<TPW>(Ms, sg.M, nullptr, seg_base, col0, g, c);
-      if (L == 0) {
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) sg.mnz[((long long)sidx * H + h) * (D / 16) + col0 / 16 + jj] = mzero ? 0 : 1;
-      }
-    }
-    if (ext > 0 && ok) {  // into the next segment (see above)
-      for (int e = 0; ok && e < ext; ++e) ok = step_s(nch + e, Rs, WithOut{});
-      if (ok) store_state<TPW>(Rs, sg.fix, nullptr, fix_base, col0, g, c);
-    }
+    if (ext > 0) extend(S, ok);  // into the next segment (see above)
   }
 }
 
@@ -1152,14 +1314,7 @@ __global__ __launch_bounds__(NTHREADS) void KDA_CHUNK_KERNEL(Problem p, Tables t
     if (r0.x < 0) return;
     u = Unit{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z};
   }
-  if (MODE == 0)
-    chunk_body<RECUR, 0>(sm, p, t, sg, u, h);
-  else if (MODE == 2)
-    chunk_body<RECUR, 1>(sm, p, t, sg, u, h);
-  else if (u.j == 0)
-    chunk_body<RECUR, 0>(sm, p, t, sg, u, h);
-  else
-    chunk_body<PRE, 0>(sm, p, t, sg, u, h);
+  chunk_body<MODE>(sm, p, t, sg, u, h);
 }
 
 hipError_t KDA_LAUNCH_CHUNKS(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,

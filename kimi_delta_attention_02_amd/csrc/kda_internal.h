@@ -59,6 +59,10 @@ struct Problem {
   void* final_state;
   int state_fp32;
   int state_kv;  // caller's states are [N][H][K][V] (else [N][H][V][K])
+  // final_state shares no byte with initial_state: a segmented call's first
+  // pass may then write the final state of a sequence's last segment itself
+  // (while segment 0's blocks may still be reading the initial state).
+  int final_early;
   float scale;
   float lower_bound;
   int H;    // heads of v, g, beta, out and the states
@@ -74,7 +78,12 @@ struct Problem {
 //   chk  : R after the first chk_chunks chunks of segments >= 1 (first pass);
 //   fix  : the state after a segment's first chk_chunks chunks as the first
 //          pass's block of the previous segment reached it (first pass);
-//   mnz  : per (segment, head, 16-column block of M) 1 if nonzero, 0 if exactly zero.
+//   mnz  : per (segment, head, 16-column block of M) 1 if nonzero, 0 if exactly zero;
+//   sync : per (segment, head) 16 words: the checkpoint's publication by each
+//          consumer wavefront (words 0..7, this call's epoch once stored) and the
+//          previous segment's decision about it (word 8 epoch, word 9 code).
+// epoch is a number no earlier call on the same workspace wrote (nonzero), so
+// words left by an earlier call never pass for this call's.
 struct Seg {
   float* M;
   float* R;
@@ -82,6 +91,8 @@ struct Seg {
   float* chk;
   float* fix;
   int32_t* mnz;
+  uint32_t* sync;
+  uint32_t epoch;
   int chk_chunks;
   int seg_chunks;  // segment length in chunks (0: serial, one segment per sequence)
 };

@@ -66,7 +66,7 @@ def test_workspace_layout_consistent():
         off = kda.workspace_offsets(*args)
         assert off["total"] == size
         prev = -1
-        for name in kda.WS_FIELDS[:15]:
+        for name in kda.WS_FIELDS[:16]:
             assert off[name] % kda.WS_ALIGN == 0
             assert off[name] >= prev
             prev = off[name]
@@ -85,7 +85,8 @@ def test_workspace_layout_consistent():
             assert off["seq_full_off"] - off["seg_chk"] >= mat
         assert off["unit_tab"] - off["seq_full_off"] >= 4 * (N + 1)
         assert off["seg_fix"] - off["unit_tab"] >= 32 * off["max_segs"]
-        assert off["total"] - off["seg_fix"] >= (mat if seg else 0)
+        assert off["seg_sync"] - off["seg_fix"] >= (mat if seg else 0)
+        assert off["total"] - off["seg_sync"] >= (off["max_segs"] * H * 16 * 4 if seg else 0)
 
 
 def _call(lib, **kw):

@@ -60,6 +60,16 @@ def test_final_state_may_alias_initial(sdt):
     _case(kda_inputs.custom(B=1, T=90, H=2, state_dtype=sdt, seed=23, name=f"alias_{sdt}"), alias=True)
 
 
+@pytest.mark.parametrize("alias", [False, True])
+@pytest.mark.parametrize("layout_sdt", ["fp32", "bf16"])
+def test_segmented_final_state_with_and_without_alias(alias, layout_sdt):
+    # Segmented: without aliasing the first pass writes the final state of a
+    # sequence's last segment itself; with aliasing the second pass does.
+    w = kda_inputs.custom(B=2, T=700, H=2, lower_bound=-3.0, state_dtype=layout_sdt, seed=25,
+                          name=f"segfinal_{layout_sdt}_{alias}")
+    _case(w, cp_mode="force", seg_chunks=8, alias=alias)
+
+
 @pytest.mark.parametrize("seg", [1, 2, 3])
 def test_segment_path_small(seg):
     w = kda_inputs.custom(seqlens=[200, 16, 48, 1, 130], H=2, lower_bound=-1.0, seed=24, name=f"segsmall{seg}")
