@@ -33,7 +33,7 @@
 //   substitution (4 lanes per column, DPP quad sums), T' = T Diag(b);
 //   Aqk = LowerInclusive(Qbar Ktil^T)
 // and the consumers, with S the K x V state entering the chunk:
-//   Y = Kbar S;  X = T' Y (= W S, W = T' Kbar);  Ut = T' V;  U = Ut - X
+//   Y = Kbar S;  U = T' V - T' Y (one accumulation: the consumers hold -Kbar)
 //   O = Qbar S + Aqk U;  S <- Diag(gamma_C) (S + Ktil^T U)  (Khat = Ktil gamma_C)
 // (M starts at I with Ut = 0 and writes no output).
 //
@@ -81,7 +81,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 // MFMA operand that reads it, so the consumers read 16 bytes per lane and use
 // them as they are.
 struct Slot {
-  u32x4 kbf[4][64];   // Kbar bf16, A operand of Kbar S: k-step s, lane (g, c) = token c
+  u32x4 kbf[4][64];   // -Kbar bf16, A operand of -Kbar S: k-step s, lane (g, c) = token c (negated:
+                      // its product is -Y, whose bf16 is the operand U = T' V + T' (-Yb) needs)
   u32x4 qbf[4][64];   // Qbar bf16, B operand of S^T Qbar^T, same arrangement
   u32x4 ktp[D][4];    // [channel][(g + channel/2) % 4]: Ktil high part of tokens 4g..4g+3, then the
                       // low part (the rotation spreads a column read over all LDS banks)
@@ -300,7 +301,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
         const float ep = __builtin_amdgcn_exp2f(G2), em = __builtin_amdgcn_exp2f(-G2);
         ep_last[e] = ep;
         const float kr = kv * rk;
-        Kb[h] = kr * ep;
+        Kb[h] = -(kr * ep);  // -Kbar (see Slot::kbf)
         Kt[h] = kr * em;
         Qb[h] = (qv * rq) * ep;
       }
@@ -318,7 +319,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
     }
     const u32x4 kbh4 = {kbh[0], kbh[1], kbh[2], kbh[3]};
     const u32x4 kth4 = {kth[0], kth[1], kth[2], kth[3]}, ktl4 = {ktl[0], ktl[1], ktl[2], ktl[3]};
-    Araw = mfma_k32(kbh4, kth4, Araw);  // D[4g+i][c] += Kbar_{4g+i} . Ktil_c over this k-step
+    Araw = mfma_k32(kbh4, kth4, Araw);  // D[4g+i][c] -= Kbar_{4g+i} . Ktil_c over this k-step
     sl.kbf[s][L] = kbh4;
     {
       const u32x4 qbh4 = {qbh[0], qbh[1], qbh[2], qbh[3]}, qbl4 = {qbl[0], qbl[1], qbl[2], qbl[3]};
@@ -339,7 +340,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * g + i;
-    sm.Aq[pw][row][4 * (c & 3) + (c >> 2)] = (c < row) ? sm.bt[pw][row] * Araw[i] : 0.f;
+    sm.Aq[pw][row][4 * (c & 3) + (c >> 2)] = (c < row) ? -(sm.bt[pw][row] * Araw[i]) : 0.f;  // Araw = -A_raw
   }
   {
     f32x4 aq;
@@ -400,7 +401,8 @@ __device__ __forceinline__ void pack_tile(const f32x4 (&S)[8], u32x2 (&Sb)[8]) {
   for (int tt = 0; tt < 8; ++tt) Sb[tt] = pack4(S[tt]);
 }
 
-// Y = Kbar S for NT column tiles, interleaved so consecutive MFMAs are independent
+// -Y = -Kbar S for NT column tiles (kb holds -Kbar), interleaved so
+// consecutive MFMAs are independent
 template <int NT>
 __device__ __forceinline__ void tiles_y(const u32x2 (&Sb)[NT][8], const u32x4 (&kb)[4], f32x4 (&Y)[NT]) {
 #pragma unroll
@@ -411,11 +413,12 @@ __device__ __forceinline__ void tiles_y(const u32x2 (&Sb)[NT][8], const u32x4 (&
     for (int jj = 0; jj < NT; ++jj) Y[jj] = mfma_k32(kb[s], cat(Sb[jj][2 * s], Sb[jj][2 * s + 1]), Y[jj]);
 }
 
-// U = Ut - T' Y (Ut = T' V, or 0 when v is null) as MFMA operands
-__device__ __forceinline__ UOps tile_u(f32x4 Y, u32x4 tf, const u32x2* v) {
-  const u32x2 Yb = pack4(Y);
-  const f32x4 X = mfma_k32(tf, cat(Yb, Yb), zero4());
-  const f32x4 U = v ? mfma_k32(tf, cat(*v, *v), zero4()) - X : -X;
+// U = T' V + T' (-Yb) (no V term when v is null) as MFMA operands, from
+// nY = -Y = -Kbar S; the second product accumulates onto the first
+__device__ __forceinline__ UOps tile_u(f32x4 nY, u32x4 tf, const u32x2* v) {
+  const u32x2 nYb = pack4(nY);
+  const f32x4 Ut = v ? mfma_k32(tf, cat(*v, *v), zero4()) : zero4();
+  const f32x4 U = mfma_k32(tf, cat(nYb, nYb), Ut);
   u32x2 uh, ul;
   split4(U, uh, ul);
   UOps o;
@@ -1011,7 +1014,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
     u32x2 Sb[TPW][8];
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) pack_tile(S[jj], Sb[jj]);
-    // Y = Kbar S and O^T: independent MFMA chains
+    // -Y = -Kbar S and O^T: independent MFMA chains
     f32x4 Y[TPW], Ot[TPW];
     tiles_y<TPW>(Sb, kb, Y);
     if constexpr (WO) {
