@@ -286,7 +286,8 @@ def main() -> int:
     ap.add_argument("--preheat-ms", type=float, default=300.0,
                     help="untimed calls for this much wall time before the warmup steps (0 = none)")
     ap.add_argument("--config", default="cfg4a",
-                    help="workload: cfg1..cfg5 (cfg4a/cfg4b), or cfg4a_slow (T=65536 H=16 at lower_bound -0.1)")
+                    help="workload: cfg1..cfg5 (cfg4a/cfg4b), cfg4a_slow (T=65536 H=16 at lower_bound -0.1) or "
+                         "cfg4a_nodecay (the same at lower_bound 0)")
     ap.add_argument("--cp", default="auto", help="auto | off | force")
     ap.add_argument("--seg", type=int, default=0, help="segment length in chunks (0 = library choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,

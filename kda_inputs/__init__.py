@@ -109,6 +109,10 @@ WORKLOADS = {
     # which a segment's transition M does not underflow to zero
     "cfg4a_slow": Workload("kda_fwd_B1_T65536_H16_lb0.1", B=1, T=65536, H=16, seqlens=None, lower_bound=-0.1,
                            scale=INV_SQRT_D, init_std=0.05, state_dtype="fp32", want_final=True, seed=4),
+    # no decay at all (lower bound 0): no segment's transition M ever vanishes, so every merge
+    # multiplies by the M of each earlier segment
+    "cfg4a_nodecay": Workload("kda_fwd_B1_T65536_H16_lb0", B=1, T=65536, H=16, seqlens=None, lower_bound=0.0,
+                              scale=INV_SQRT_D, init_std=0.05, state_dtype="fp32", want_final=True, seed=4),
 }
 
 

@@ -342,6 +342,30 @@ def test_config4_slow_decay_segmented():
     assert_close(to_f64(fin_c).reshape(-1), to_f64(fin_s).reshape(-1), "segmented vs serial final", stored="fp32")
 
 
+def test_config4_no_decay_segmented():
+    """T=65536 H=16 at lower_bound 0: no decay, so every segment's M stays
+    nonzero and the second pass merges each start state through all the
+    earlier segments' maps (fp32 products) before running the segment again.
+    Segmented against serial within the tolerance, both against the oracle."""
+    w = kda_inputs.WORKLOADS["cfg4a_nodecay"]
+    say(f"case {w.name} serial vs segmented (no decay)")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
+    out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="auto")
+    import kimi_delta_attention_02_amd as kda
+
+    seg = kda.plan_seg_chunks(w.B * w.T, w.H, w.N, "auto")
+    assert seg > 0
+    stops = _early_stops(w, ws, "auto", 0)
+    say(f"{w.name} seg={seg}: out identical={torch.equal(out_c.view(torch.int16), out_s.view(torch.int16))} "
+        f"early stops={stops}")
+    for got_o, got_f in ((out_s, fin_s), (out_c, fin_c)):
+        check_against_oracle(w, x, got_o, got_f, heads=[0, 11], final_dtype=w.state_dtype)
+    assert_close(to_f64(out_c).reshape(-1), to_f64(out_s).reshape(-1), "segmented vs serial out", stored="bf16")
+    assert_close(to_f64(fin_c).reshape(-1), to_f64(fin_s).reshape(-1), "segmented vs serial final", stored="fp32")
+
+
 def test_two_launch_index_path_end_to_end():
     """5000 sequences of 3..40 tokens (past the one-workgroup index form's
     4095): the index scan + fill launches, then the chunk kernel, every chain
