@@ -44,6 +44,7 @@
 // the RMS.  A 16x16 accumulator tile holds rows 4g..4g+3 of column c in lane
 // 16g+c, which is also the bf16 operand layout of the next chunk's products,
 // so the state never leaves registers within a segment.
+#include <cfloat>
 #include <type_traits>
 
 #include "kda_internal.h"
@@ -221,7 +222,22 @@ __device__ __forceinline__ u32x2 slot_v(const Slot& sl, int g, int col) {
 }
 
 // ---------------------------------------------------------------- producer
-__device__ __forceinline__ float pick4(f32x4 v, int i) { return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3]; }
+// a.lo b.lo + a.hi b.hi + acc for two packed bf16 pairs
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                         false);
+}
+
+// x summed over the lanes L, L^16, L^32, L^48 (the four lane groups g of one
+// c); every lane of the four gets the same bits (each step adds two values in
+// either order)
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // Prepares one chunk into a ring slot: V rows, Kbar, Ktil, Qbar, gamma_C, beta,
 // Aqk and T' (the first pass of a segmented call needs Qbar and Aqk too, since
@@ -247,22 +263,28 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
     }
     load_vrows(in, next);
   }
-  // |q_c|^2, |k_c|^2: diagonals of the Gram matrices q q^T, k k^T from bf16 MFMAs
-  // (bf16 products are exact in fp32); token c's entry is element c%4 of lane
-  // 16(c/4)+c
-  f32x4 gq = zero4(), gk = zero4();
+  // |q_c|^2, |k_c|^2: this lane's 32 channels by bf16 pair dot products (the
+  // products are exact in fp32), then the sum over the four lanes of token c
+  float sq0 = 0.f, sq1 = 0.f, sk0 = 0.f, sk1 = 0.f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    gq = mfma_k32(in.q[s], in.q[s], gq);
-    gk = mfma_k32(in.k[s], in.k[s], gk);
-  }
-  const int diag = 16 * (c >> 2) + c;
-  const float sq = __shfl(pick4(gq, c & 3), diag, 64);
-  const float sk = __shfl(pick4(gk, c & 3), diag, 64);
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      sq0 = dot2_bf16(in.q[s][i], in.q[s][i], sq0);
+      sq1 = dot2_bf16(in.q[s][i + 1], in.q[s][i + 1], sq1);
+      sk0 = dot2_bf16(in.k[s][i], in.k[s][i], sk0);
+      sk1 = dot2_bf16(in.k[s][i + 1], in.k[s][i + 1], sk1);
+    }
+  const float sq = sum_lane_groups(sq0 + sq1);
+  const float sk = sum_lane_groups(sk0 + sk1);
   // rows past the chunk end: zero key, query, beta and log decay
   const float rq = ok ? p.scale * __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;
   const float rk = ok ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 0.f;
-  const float lb2 = ok ? p.lower_bound * LOG2E : 0.f;
+  // 1 / (log2(e) lower_bound); rows past the chunk end, and a bound of 0, take
+  // -FLT_MAX, whose reciprocal below is 0 or a denormal that adds nothing to a
+  // log decay (exp2 of it is 1)
+  const float lb2 = p.lower_bound * LOG2E;
+  const float ilb = (ok && lb2 < -1e-30f) ? 1.0f / lb2 : -FLT_MAX;
   const float bt =
       ok ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * __uint_as_float(in.b << 16))) : 0.f;
   sm.bt[pw][c] = bt;  // the four lanes of a token store the same value
@@ -294,9 +316,11 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
         const float gv = __uint_as_float(h ? (gw & 0xFFFF0000u) : (gw << 16));
         const int e = 2 * i + h;
         const float ad = (e < 4) ? adt0[e] : adt1[e - 4];
-        // l2 = log2(e) lower_bound sigmoid(exp(A_log) (g + dt_bias))
+        // l2 = log2(e) lower_bound sigmoid(exp(A_log) (g + dt_bias)), formed as
+        // 1 / ((1 + e^-x) / (log2(e) lower_bound))
         const float x2 = fmaf(a2, gv, ad);
-        const float l2 = lb2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x2));
+        const float ex = __builtin_amdgcn_exp2f(-x2);
+        const float l2 = __builtin_amdgcn_rcpf(fmaf(ex, ilb, ilb));
         const float G2 = row_scan(l2);
         const float ep = __builtin_amdgcn_exp2f(G2), em = __builtin_amdgcn_exp2f(-G2);
         ep_last[e] = ep;
@@ -364,7 +388,13 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
 #pragma unroll
     for (int i = 1; i < C; ++i) {
       const f32x4 ar = *reinterpret_cast<const f32x4*>(&sm.Aq[pw][i][4 * q]);  // A[i][q+4k], k = 0..3
-      float part = fmaf(ar[1], t1, ar[0] * t0) + fmaf(ar[3], t3, ar[2] * t2);
+      // A[i][p] = 0 for p >= i, so only the terms k <= (i - 1) / 4 can be nonzero
+      const int kmax = (i - 1) >> 2;
+      float part;
+      if (kmax == 0) part = ar[0] * t0;
+      else if (kmax == 1) part = fmaf(ar[1], t1, ar[0] * t0);
+      else if (kmax == 2) part = fmaf(ar[2], t2, fmaf(ar[1], t1, ar[0] * t0));
+      else part = fmaf(ar[1], t1, ar[0] * t0) + fmaf(ar[3], t3, ar[2] * t2);
       part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0xB1, 0xF, 0xF, false));  // quad xor 1
       part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0x4E, 0xF, 0xF, false));  // quad xor 2
       // row i is held by the lanes with q = i % 4, as t_{i/4}
