@@ -85,12 +85,12 @@ struct Slot {
   u32x4 kbf[4][64];   // -Kbar bf16, A operand of -Kbar S: k-step s, lane (g, c) = token c (negated:
                       // its product is -Y, whose bf16 is the operand U = T' V + T' (-Yb) needs)
   u32x4 qbf[4][64];   // Qbar bf16, B operand of S^T Qbar^T, same arrangement
-  u32x4 ktp[D][4];    // [channel][(g + channel/2) % 4]: Ktil high part of tokens 4g..4g+3, then the
-                      // low part (the rotation spreads a column read over all LDS banks)
+  u32x2 ktp[D][4];    // [channel][(g + (channel % 16) / 4) % 4]: Khat = Ktil gamma_C (at most 1 in
+                      // magnitude) as fp16, tokens 4g..4g+3 (the rotation spreads a column read
+                      // over the LDS banks)
   float gC[D];        // gamma_C per key channel
   u32x4 tf[64];       // [T'_hi | T'_lo] of row c, columns 4g..4g+3
-  u32x4 aqa[64];      // [Aqk_hi | Aqk_hi] of row c, columns 4g..4g+3
-  u32x4 aqb[64];      // [Aqk_lo | 0]
+  u32x2 aq[64];       // Aqk as fp16, row c, columns 4g..4g+3
   uint16_t vo[C][D + 8];  // V rows of the chunk (producer), overwritten column slice by column slice
                           // with O by the consumer owning those columns; written out whole rows
                           // (16 bytes of padding per row move consecutive rows to other banks)
@@ -291,11 +291,10 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
   in.b = next.b[next.brow];
 
   // A_raw = Kbar Ktil^T from bf16 operands (one MFMA per k-step), Aqk^T =
-  // Ktil Qbar^T from bf16 high/low operands (hi.hi + hi.lo + lo.hi)
-  // Ktil of token c, channel ch goes to ktp[ch][(c/4 + ch/2) % 4], element c % 4 (high part)
-  // or 4 + c % 4 (low part); ch/2 % 4 = (2g + i % 2) % 4 for the channels this lane holds
-  uint16_t* ktp16 = reinterpret_cast<uint16_t*>(&sl.ktp[0][0]) + (c & 3);
-  const int kpos0 = 8 * (((c >> 2) + 2 * g) & 3), kpos1 = 8 * (((c >> 2) + 2 * g + 1) & 3);
+  // Ktil Qbar^T from bf16 high/low operands (hi.hi + hi.lo + lo.hi).
+  // Khat = Ktil gamma_C of token c, channel ch goes to ktp[ch][(c/4 + (ch % 16)/4) % 4],
+  // element c % 4, as fp16; (ch % 16) / 4 = g for every channel this lane holds
+  uint16_t* khp16 = reinterpret_cast<uint16_t*>(&sl.ktp[0][0]) + 4 * (((c >> 2) + g) & 3) + (c & 3);
   f32x4 Araw = zero4(), AqkT = zero4();
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -308,7 +307,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t qw = in.q[s][i], kw = in.k[s][i], gw = in.g[s][i];
-      float Kb[2], Kt[2], Qb[2];
+      float Kb[2], Kt[2], Qb[2], Kh[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const float qv = __uint_as_float(h ? (qw & 0xFFFF0000u) : (qw << 16));
@@ -328,18 +327,17 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
         Kb[h] = -(kr * ep);  // -Kbar (see Slot::kbf)
         Kt[h] = kr * em;
         Qb[h] = (qv * rq) * ep;
+        // gamma_C of this channel is e^G of token 15, held by lane 15 of the row
+        Kh[h] = Kt[h] * __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ep), 0x15F, 0xF, 0xF, false));
       }
       kbh[i] = pack2(Kb[0], Kb[1]);
       split_pair(Kt[0], Kt[1], kth[i], ktl[i]);
       split_pair(Qb[0], Qb[1], qbh[i], qbl[i]);
-      // Ktil, channel-major: ktp[ch][(c/4 + ch/2) % 4] holds tokens 4(c/4)..+3,
-      // high parts then low parts
+      // Khat, channel-major (16 fp16 per channel row)
       const int ch = 32 * s + 16 * (i >> 1) + 4 * g + 2 * (i & 1);
-      const int kp = (i & 1) ? kpos1 : kpos0;
-      ktp16[32 * ch + kp] = (uint16_t)(kth[i] & 0xFFFFu);
-      ktp16[32 * (ch + 1) + kp] = (uint16_t)(kth[i] >> 16);
-      ktp16[32 * ch + kp + 4] = (uint16_t)(ktl[i] & 0xFFFFu);
-      ktp16[32 * (ch + 1) + kp + 4] = (uint16_t)(ktl[i] >> 16);
+      const uint32_t kh = pack2_f16(Kh[0], Kh[1]);
+      khp16[16 * ch] = (uint16_t)(kh & 0xFFFFu);
+      khp16[16 * (ch + 1)] = (uint16_t)(kh >> 16);
     }
     const u32x4 kbh4 = {kbh[0], kbh[1], kbh[2], kbh[3]};
     const u32x4 kth4 = {kth[0], kth[1], kth[2], kth[3]}, ktl4 = {ktl[0], ktl[1], ktl[2], ktl[3]};
@@ -370,10 +368,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
     f32x4 aq;
 #pragma unroll
     for (int i = 0; i < 4; ++i) aq[i] = (4 * g + i <= c) ? AqkT[i] : 0.f;
-    u32x2 ah, al;
-    split4(aq, ah, al);
-    sl.aqa[L] = cat(ah, ah);
-    sl.aqb[L] = u32x4{al.x, al.y, 0u, 0u};
+    sl.aq[L] = pack4_f16(aq);
   }
 
   wave_lds_sync();
@@ -418,13 +413,45 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
 
 // ---------------------------------------------------------------- consumer
 // A state column tile is f32x4 S[8]: S[t] holds rows 16t+4g+0..3 of column c.
-// U of a column tile is carried as three MFMA operands built from its
-// high/low parts: ua = [U_hi | U_lo] (A operand, for Aqk U), and the B
-// operands b1 = [U_hi ; U_hi], b2 = [U_lo ; 0] of the state update
-//   [Ktil_hi | Ktil_lo] b1 + [Ktil_hi | Ktil_lo] b2 = Ktil_hi U_hi + Ktil_lo U_hi + Ktil_hi U_lo.
-struct UOps {
-  u32x4 ua, b1, b2;
+// U of a column tile is the fp16 B operand of the state update Khat^T U and
+// the A operand of Aqk U (U^T is the A operand of O^T += U^T Aqk^T): lane
+// (g, c) holds U[4g+i][c], i = 0..3, times sc = 2^k.  k = 0 while the tile's
+// largest |U| lies in [2^-12, 2^15) (or the tile is zero): fp16 then keeps 11
+// bits of every value down to 2^-14 and an absolute error of at most 2^-25
+// below, small against that largest value.  Outside that range (or for
+// non-finite values) 2^k brings the largest |U| to [2^13, 2^14); the state
+// tile is scaled by 2^k around the update and by isc = 2^-k after it, exactly.
+// The pre-scan's M (up = false) is only scaled down: its values shrink to
+// exact zero as the start state's influence dies out, and small ones weigh
+// nothing against R, so they are left to fp16's range.
+struct U16 {
+  u32x2 u;
+  float sc, isc;
+  bool scaled;  // wavefront-uniform
 };
+
+__device__ __forceinline__ U16 to_u16(f32x4 U, bool up = true) {
+  const float m = fmaxf(fmaxf(fabsf(U[0]), fabsf(U[1])), fmaxf(fabsf(U[2]), fabsf(U[3])));
+  const uint64_t big = __builtin_amdgcn_ballot_w64(!(m < 32768.f));
+  const uint64_t fit = __builtin_amdgcn_ballot_w64(m >= 0x1p-12f);
+  const uint64_t nz = __builtin_amdgcn_ballot_w64(m != 0.f);
+  U16 r;
+  r.scaled = big != 0 || (up && fit == 0 && nz != 0);
+  r.sc = 1.f;
+  r.isc = 1.f;
+  if (r.scaled) {
+    float w = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) w = fmaxf(w, __shfl_xor(w, o, 64));
+    w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w)));  // every lane holds the maximum
+    const int e = __builtin_isfinite(w) ? __builtin_amdgcn_frexp_expf(w) : 0;  // w in [2^(e-1), 2^e)
+    r.sc = __builtin_ldexpf(1.f, 14 - e);
+    r.isc = __builtin_ldexpf(1.f, e - 14);
+    U = U * r.sc;
+  }
+  r.u = pack4_f16(U);
+  return r;
+}
 
 __device__ __forceinline__ void pack_tile(const f32x4 (&S)[8], u32x2 (&Sb)[8]) {
 #pragma unroll
@@ -443,49 +470,50 @@ __device__ __forceinline__ void tiles_y(const u32x2 (&Sb)[NT][8], const u32x4 (&
     for (int jj = 0; jj < NT; ++jj) Y[jj] = mfma_k32(kb[s], cat(Sb[jj][2 * s], Sb[jj][2 * s + 1]), Y[jj]);
 }
 
-// U = T' V + T' (-Yb) (no V term when v is null) as MFMA operands, from
-// nY = -Y = -Kbar S; the second product accumulates onto the first
-__device__ __forceinline__ UOps tile_u(f32x4 nY, u32x4 tf, const u32x2* v) {
+// U = T' V + T' (-Yb) (no V term when v is null) in fp32, from nY = -Y =
+// -Kbar S; the second product accumulates onto the first
+__device__ __forceinline__ f32x4 tile_u(f32x4 nY, u32x4 tf, const u32x2* v) {
   const u32x2 nYb = pack4(nY);
   const f32x4 Ut = v ? mfma_k32(tf, cat(*v, *v), zero4()) : zero4();
-  const f32x4 U = mfma_k32(tf, cat(nYb, nYb), Ut);
-  u32x2 uh, ul;
-  split4(U, uh, ul);
-  UOps o;
-  o.ua = cat(uh, ul);
-  o.b1 = cat(uh, uh);
-  o.b2 = u32x4{ul.x, ul.y, 0u, 0u};
-  return o;
+  return mfma_k32(tf, cat(nYb, nYb), Ut);
 }
 
-// S <- Diag(gamma_C) (S + Ktil^T U) (= Diag(gamma_C) S + Khat^T U) for NT column
-// tiles; the Ktil / gamma_C fragments of a row tile are read once and used by
-// every column tile.  Ktil = k^ e^-G reaches e^80 where gamma_C is e^-80, and
-// the sum is formed at that scale before the decay: its fp32 rounding is then
-// relative to the Khat^T U term, as in the unscaled form.
 template <int NT>
-__device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const UOps (&u)[NT], u32x4 (&kp)[8],
+__device__ __forceinline__ void scale_tiles(f32x4 (&S)[NT][8], const U16 (&u)[NT], bool before) {
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+    if (u[jj].scaled) {
+      const float f = before ? u[jj].sc : u[jj].isc;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) S[jj][tt] = S[jj][tt] * f;
+    }
+}
+
+// S <- Diag(gamma_C) S + Khat^T U for NT column tiles, one fp16 product per
+// row tile (Khat = Ktil gamma_C = k^ e^(G_C - G)); the Khat / gamma_C
+// fragments of a row tile are read once and used by every column tile.
+template <int NT>
+__device__ __forceinline__ void tiles_update(f32x4 (&S)[NT][8], const U16 (&u)[NT], u32x2 (&kp)[8],
                                              f32x4 (&gc)[8], const Slot& sl, int g, int c) {
 #pragma unroll
   for (int tt = KDA_HOIST; tt < 8; ++tt) {
-    kp[tt] = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
+    kp[tt] = sl.ktp[16 * tt + c][(g + (c >> 2)) & 3];
     gc[tt] = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
   }
+  scale_tiles<NT>(S, u, true);
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
 #pragma unroll
-    for (int jj = 0; jj < NT; ++jj) {
-      const f32x4 acc = mfma_k32(kp[tt], u[jj].b1, S[jj][tt]);
-      S[jj][tt] = mfma_k32(kp[tt], u[jj].b2, acc) * gc[tt];
-    }
+    for (int jj = 0; jj < NT; ++jj) S[jj][tt] = mfma_f16_k16(kp[tt], u[jj].u, S[jj][tt] * gc[tt]);
   }
+  scale_tiles<NT>(S, u, false);
 }
 
-// The Ktil and gamma_C fragments of the update, for every row tile
-__device__ __forceinline__ void update_operands(const Slot& sl, int g, int c, u32x4 (&kp)[8], f32x4 (&gc)[8]) {
+// The Khat and gamma_C fragments of the update, for the first row tiles
+__device__ __forceinline__ void update_operands(const Slot& sl, int g, int c, u32x2 (&kp)[8], f32x4 (&gc)[8]) {
 #pragma unroll
   for (int tt = 0; tt < KDA_HOIST; ++tt) {
-    kp[tt] = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
+    kp[tt] = sl.ktp[16 * tt + c][(g + (c >> 2)) & 3];
     gc[tt] = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
   }
 }
@@ -493,24 +521,39 @@ __device__ __forceinline__ void update_operands(const Slot& sl, int g, int c, u3
 // The same update for two sets of column tiles (R and M of the pre-scan);
 // returns the OR of the bit patterns of the new S2 entries
 template <int NT>
-__device__ __forceinline__ uint32_t tiles_update2(f32x4 (&S1)[NT][8], const UOps (&u1)[NT], f32x4 (&S2)[NT][8],
-                                                  const UOps (&u2)[NT], const Slot& sl, int g, int c) {
-  uint32_t bits = 0;
+__device__ __forceinline__ uint32_t tiles_update2(f32x4 (&S1)[NT][8], const U16 (&u1)[NT], f32x4 (&S2)[NT][8],
+                                                  const U16 (&u2)[NT], const Slot& sl, int g, int c) {
+  scale_tiles<NT>(S1, u1, true);
+  scale_tiles<NT>(S2, u2, true);
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
-    const u32x4 kp = sl.ktp[16 * tt + c][(g + (c >> 1)) & 3];
+    const u32x2 kp = sl.ktp[16 * tt + c][(g + (c >> 2)) & 3];
     const f32x4 gc = *reinterpret_cast<const f32x4*>(&sl.gC[16 * tt + 4 * g]);
 #pragma unroll
     for (int jj = 0; jj < NT; ++jj) {
-      const f32x4 a1 = mfma_k32(kp, u1[jj].b1, S1[jj][tt]);
-      const f32x4 a2 = mfma_k32(kp, u2[jj].b1, S2[jj][tt]);
-      S1[jj][tt] = mfma_k32(kp, u1[jj].b2, a1) * gc;
-      S2[jj][tt] = mfma_k32(kp, u2[jj].b2, a2) * gc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bits |= __float_as_uint(S2[jj][tt][i]);
+      S1[jj][tt] = mfma_f16_k16(kp, u1[jj].u, S1[jj][tt] * gc);
+      S2[jj][tt] = mfma_f16_k16(kp, u2[jj].u, S2[jj][tt] * gc);
     }
   }
+  scale_tiles<NT>(S1, u1, false);
+  scale_tiles<NT>(S2, u2, false);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bits |= __float_as_uint(S2[jj][tt][i]);
   return bits;
+}
+
+// O^T += U^T Aqk^T for one column tile (fp16 product, scaled back by isc)
+__device__ __forceinline__ f32x4 add_aqk_u(f32x4 Ot, const U16& u, u32x2 aq) {
+  const f32x4 P = mfma_f16_k16(u.u, aq, zero4());
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = fmaf(P[i], u.isc, Ot[i]);
+  return r;
 }
 
 // All loads are issued before any value is converted, so they overlap.
@@ -1033,7 +1076,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       if (WO) qb[s] = sl.qbf[s][L];
     }
     const u32x4 tf = sl.tf[L];
-    u32x4 kp[8];
+    u32x2 kp[8];
     f32x4 gc[8];
     update_operands(sl, g, c, kp, gc);
     u32x2 v[TPW];
@@ -1055,15 +1098,13 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 #pragma unroll
         for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(cat(Sb[jj][2 * s], Sb[jj][2 * s + 1]), qb[s], Ot[jj]);
     }
-    UOps u[TPW];
+    U16 u[TPW];
 #pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) u[jj] = tile_u(Y[jj], tf, &v[jj]);
+    for (int jj = 0; jj < TPW; ++jj) u[jj] = to_u16(tile_u(Y[jj], tf, &v[jj]));
     if constexpr (WO) {
-      const u32x4 aqa = sl.aqa[L], aqb = sl.aqb[L];
+      const u32x2 aq = sl.aq[L];
 #pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqa, Ot[jj]);
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = mfma_k32(u[jj].ua, aqb, Ot[jj]);
+      for (int jj = 0; jj < TPW; ++jj) Ot[jj] = add_aqk_u(Ot[jj], u[jj], aq);
       // O^T tile: token c, columns col0 + 16jj + 4g..+3
       Slot& slw = sm.slot[slot];
 #pragma unroll
@@ -1228,7 +1269,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
 #pragma unroll
         for (int s = 0; s < 4; ++s) kb[s] = sl.kbf[s][L];
         const u32x4 tf = sl.tf[L];
-        UOps ur[TPW], um[TPW];
+        U16 ur[TPW], um[TPW];
 #pragma unroll
         for (int jj = 0; jj < TPW; ++jj) {  // one R and one M tile at a time: bounded live range
           const u32x2 v = slot_v(sl, g, col0 + 16 * jj + c);
@@ -1237,14 +1278,13 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
           pack_tile(Ms[jj], Sb[1]);
           f32x4 Y[2];
           tiles_y<2>(Sb, kb, Y);
-          ur[jj] = tile_u(Y[0], tf, &v);
-          um[jj] = tile_u(Y[1], tf, nullptr);
+          ur[jj] = to_u16(tile_u(Y[0], tf, &v));
+          um[jj] = to_u16(tile_u(Y[1], tf, nullptr), false);
           if constexpr (WO) {
             f32x4 Ot = zero4();
 #pragma unroll
             for (int s = 0; s < 4; ++s) Ot = mfma_k32(cat(Sb[0][2 * s], Sb[0][2 * s + 1]), sl.qbf[s][L], Ot);
-            Ot = mfma_k32(ur[jj].ua, sl.aqa[L], Ot);
-            Ot = mfma_k32(ur[jj].ua, sl.aqb[L], Ot);
+            Ot = add_aqk_u(Ot, ur[jj], sl.aq[L]);
             Slot& slw = sm.slot[slot];
             *reinterpret_cast<u32x2*>(&slw.vo[c][col0 + 16 * jj + 4 * g]) = pack4(Ot);
           }

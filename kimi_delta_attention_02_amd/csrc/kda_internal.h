@@ -2,6 +2,7 @@
 //
 // MFMA lane layouts used throughout (wave64, lane L, g = L / 16, c = L % 16):
 //   v_mfma_f32_16x16x32_bf16 : A[c][8g+e], B[8g+e][c] (e = 0..7), D[4g+i][c]
+//   v_mfma_f32_16x16x16_f16  : A[c][4g+e], B[4g+e][c] (e = 0..3), D[4g+i][c]
 //   v_mfma_f32_16x16x4_f32   : A[c][g],    B[g][c],                D[4g+i][c]
 // A 16x16 fp32 accumulator tile therefore holds rows 4g..4g+3 of column c in
 // lane L.  For the 16x16x32 MFMA over a K range made of two 16-row tiles
@@ -151,6 +152,21 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
   lo = pack2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
 }
 
+// fp32 -> fp16 with round to nearest even: one v_cvt_pk_f16_f32 per pair.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+__device__ __forceinline__ u32x2 pack4_f16(f32x4 x) {
+  u32x2 r;
+  r.x = pack2_f16(x[0], x[1]);
+  r.y = pack2_f16(x[2], x[3]);
+  return r;
+}
+
 __device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo) {
   uint32_t h0, l0, h1, l1;
   split_pair(x[0], x[1], h0, l0);
@@ -172,6 +188,10 @@ __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) {
 
 __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16_k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {

@@ -166,6 +166,60 @@ def test_degenerate_rows_and_saturated_gates(cp, seg):
     check_against_oracle(w, x, out, final, final_dtype=w.state_dtype)
 
 
+def _scale_bf16(a: np.ndarray, p2) -> np.ndarray:
+    """bf16 bit patterns times 2**p2 (exact while the values stay normal)."""
+    f = (a.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** p2)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# Values far from 1: V and the start state times 2^20 or 2^-20.  The update's
+# fp16 operand U then leaves the range it is used in unscaled, and every tile
+# takes the power-of-two scaled form; the result must not depend on the scale.
+@pytest.mark.parametrize("p2", [20, -20])
+@pytest.mark.parametrize("cp,seg", [("off", 0), ("force", 5)])
+def test_value_scale_extremes(p2, cp, seg):
+    w = kda_inputs.custom(seqlens=[300, 77], H=4, lower_bound=-5.0, seed=91, name=f"v x 2^{p2} {cp}")
+    say(f"case {w.name} seed={w.seed} cp={cp} seg={seg}")
+    x = dict(kda_inputs.make_inputs(w))
+    x["v"] = _scale_bf16(x["v"], p2)
+    x["initial_state"] = (x["initial_state"] * np.float32(2.0 ** p2)).astype(np.float32)
+    d = dev_inputs(x)
+    out, final, _ = run_gpu(w, x, d, cp, seg)
+    check_against_oracle(w, x, out, final, final_dtype=w.state_dtype)
+
+
+# Column blocks of V at different scales (2^20, 2^-20, 1): the scaled and
+# unscaled forms run side by side in one call, each tile deciding on its own
+# values, so the 4-consumer first pass (two tiles per wavefront) and the
+# 8-consumer second pass give the serial call's bits; each block is checked
+# against the oracle at its own scale.
+def test_mixed_value_scales_segmented_bit_identical():
+    w = kda_inputs.custom(seqlens=[4096], H=2, lower_bound=-5.0, seed=92, name="mixed V scales")
+    say(f"case {w.name} seed={w.seed}")
+    x = dict(kda_inputs.make_inputs(w))
+    v = x["v"].copy()
+    s0 = x["initial_state"].copy()
+    blocks = {(0, 16): 20, (16, 32): -20, (48, 64): 20, (96, 112): -20}
+    for (a, b), p2 in blocks.items():
+        v[..., a:b] = _scale_bf16(v[..., a:b], p2)
+        s0[:, :, a:b, :] *= np.float32(2.0 ** p2)  # state layout [N, H, V, K]
+    x["v"] = v
+    x["initial_state"] = s0
+    d = dev_inputs(x)
+    out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
+    out_c, fin_c, _ = run_gpu(w, x, d, cp_mode="force", seg_chunks=128)
+    same_o = torch.equal(out_c.view(torch.int16), out_s.view(torch.int16))
+    same_f = torch.equal(fin_c, fin_s)
+    say(f"mixed scales: out identical={same_o} final identical={same_f}")
+    assert same_o and same_f
+    outs, finals = O.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["A_log"], x["dt_bias"], x["scale"],
+                                 x["lower_bound"], x["initial_state"], x["cu_seqlens"], seqs=[0], heads=[0])
+    got = to_f64(out_s[0, :, [0]]).reshape(4096, 1, -1)
+    ref = outs[0].reshape(4096, 1, -1)
+    for (a, b) in list(blocks) + [(32, 48), (112, 128)]:
+        assert_close(got[..., a:b].reshape(-1), ref[..., a:b].reshape(-1), f"out columns {a}:{b}")
+
+
 # ------------------------------------------------------------------- index tables, bit-exact
 @pytest.mark.parametrize("lens,seg,fixed", [
     ([1023, 1025, 1, 16, 4097, 8191, 65537], 64, False), ([0, 1, 15, 16, 17, 0], 1, False),
