@@ -73,7 +73,10 @@ constexpr int NPW = 4;                  // producer wavefronts
 constexpr int NCW = KDA_CONSUMERS;      // consumer wavefronts
 constexpr int TPW = (D / 16) / NCW;     // 16-column state tiles per consumer wavefront
 constexpr int NTHREADS = 64 * (NPW + NCW);
-constexpr int NSLOT = 6;
+#ifndef KDA_NSLOT
+#define KDA_NSLOT 8
+#endif
+constexpr int NSLOT = KDA_NSLOT;  // ring slots
 constexpr int MP = 20;               // fp32 16x16 matrix pitch
 constexpr int SPIN_LIMIT = 1 << 24;  // polls (each with s_sleep) before a wait gives up
 constexpr float LOG2E = 1.4426950408889634f;
@@ -973,10 +976,13 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
       const Slot& sl = sm.slot[lc % NSLOT];
       const int tok = L >> 2;
       if (tok < chunk_m(lc)) {
-        uint16_t* o = p.out + ((chunk_tok0(lc) + tok) * H + h) * D + 32 * (L & 3);
+        // a wavefront-uniform chunk base and a 32-bit lane offset
+        uint16_t* ob = p.out + (chunk_tok0(lc) * H + h) * D;
+        const uint32_t o = __umul24((uint32_t)tok, (uint32_t)(H * D)) + 32 * (L & 3);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x4*>(o + 8 * i) = *reinterpret_cast<const u32x4*>(&sl.vo[tok][32 * (L & 3) + 8 * i]);
+          *reinterpret_cast<u32x4*>(ob + o + 8 * i) =
+              *reinterpret_cast<const u32x4*>(&sl.vo[tok][32 * (L & 3) + 8 * i]);
       }
     };
     // Producer pw takes chunks lc = pw, pw + NPW, ...: before preparing chunk
