@@ -430,7 +430,7 @@ __device__ __forceinline__ void produce(Smem& sm, Slot& sl, int pw, ProdIn& in, 
 struct U16 {
   u32x2 u;
   float sc, isc;
-  bool scaled;  // wavefront-uniform
+  uint32_t scaled;  // wavefront-uniform (a word, not a bool: keeps the struct in whole registers)
 };
 
 __device__ __forceinline__ U16 to_u16(f32x4 U, bool up = true) {
@@ -439,7 +439,7 @@ __device__ __forceinline__ U16 to_u16(f32x4 U, bool up = true) {
   const uint64_t fit = __builtin_amdgcn_ballot_w64(m >= 0x1p-12f);
   const uint64_t nz = __builtin_amdgcn_ballot_w64(m != 0.f);
   U16 r;
-  r.scaled = big != 0 || (up && fit == 0 && nz != 0);
+  r.scaled = (big != 0 || (up && fit == 0 && nz != 0)) ? 1u : 0u;
   r.sc = 1.f;
   r.isc = 1.f;
   if (r.scaled) {
