@@ -643,23 +643,30 @@ __device__ __forceinline__ void store_state_kv(const f32x4 (&S)[NT][8], float* d
 
 // A state handed between blocks of one launch, which may run on different
 // XCDs, each with its own L2: it is written and read with device-coherent
-// (agent-scope) accesses, 8 bytes at a time, so no cache needs to be written
-// back or invalidated around it.  [V][K] fp32 layout as store_state.
-__device__ __forceinline__ uint64_t pair_bits(float a, float b) {
-  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+// accesses (the sc1 cache policy, which agent-scope atomics also use), 16 bytes
+// per lane, so no cache needs to be written back or invalidated around it and
+// every store fills whole 64-byte pieces of a column.  [V][K] fp32 layout as
+// store_state; the buffer resource spans the one 128x128 state at dst + base.
+constexpr int CPOL_SC1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, D * D * 4, 0x00020000);
+}
+
+__device__ __forceinline__ int state_off(int col0, int jj, int tt, int g, int c) {
+  return 4 * ((col0 + 16 * jj + c) * D + 16 * tt + 4 * g);
 }
 
 template <int NT>
 __device__ __forceinline__ void store_state_coherent(const f32x4 (&S)[NT][8], float* dst, long long base, int col0,
                                                      int g, int c) {
+  const __amdgpu_buffer_rsrc_t r = state_rsrc(dst + base);
 #pragma unroll
   for (int jj = 0; jj < NT; ++jj)
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      uint64_t* d = reinterpret_cast<uint64_t*>(dst + base + (long long)(col0 + 16 * jj + c) * D + 16 * tt + 4 * g);
-      __hip_atomic_store(d, pair_bits(S[jj][tt][0], S[jj][tt][1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(d + 1, pair_bits(S[jj][tt][2], S[jj][tt][3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int tt = 0; tt < 8; ++tt)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[jj][tt]), r, state_off(col0, jj, tt, g, c),
+                                             0, CPOL_SC1);
 }
 
 // True if every state entry of this lane equals the state at src bit for bit
@@ -667,22 +674,21 @@ __device__ __forceinline__ void store_state_coherent(const f32x4 (&S)[NT][8], fl
 template <int NT>
 __device__ __forceinline__ bool same_bits_coherent(const f32x4 (&S)[NT][8], float* src, long long base, int col0,
                                                    int g, int c) {
-  uint64_t x[NT][8][2];
-#pragma unroll
-  for (int jj = 0; jj < NT; ++jj)
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      uint64_t* d = reinterpret_cast<uint64_t*>(src + base + (long long)(col0 + 16 * jj + c) * D + 16 * tt + 4 * g);
-      x[jj][tt][0] = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      x[jj][tt][1] = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  uint64_t diff = 0;
+  const __amdgpu_buffer_rsrc_t r = state_rsrc(src + base);
+  u32x4 x[NT][8];
 #pragma unroll
   for (int jj = 0; jj < NT; ++jj)
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
-      diff |= (pair_bits(S[jj][tt][0], S[jj][tt][1]) ^ x[jj][tt][0]) |
-              (pair_bits(S[jj][tt][2], S[jj][tt][3]) ^ x[jj][tt][1]);
+      x[jj][tt] = __builtin_amdgcn_raw_buffer_load_b128(r, state_off(col0, jj, tt, g, c), 0, CPOL_SC1);
+  uint32_t diff = 0;
+#pragma unroll
+  for (int jj = 0; jj < NT; ++jj)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const u32x4 d = __builtin_bit_cast(u32x4, S[jj][tt]) ^ x[jj][tt];
+      diff |= d.x | d.y | d.z | d.w;
+    }
   return diff == 0u;
 }
 
