@@ -56,7 +56,10 @@ constexpr int kTargetUnits = 256;   // (segment, head) units the automatic plan 
 constexpr int kMinSegChunks = 16;   // shortest automatic segment (256 tokens)
 constexpr int kCheckChunks = 4;     // chunks the second pass redoes before comparing with the checkpoint
 constexpr int kSerialChains = 256;  // chains that already fill the chip without splitting
-constexpr int kWideMinChunks = 128; // units at least this long (on average) run the 4-consumer kernel
+#ifndef KDA_WIDE_MIN_CHUNKS
+#define KDA_WIDE_MIN_CHUNKS 128
+#endif
+constexpr int kWideMinChunks = KDA_WIDE_MIN_CHUNKS;  // units at least this long (on average) run the 4-consumer kernel
 
 // ---- optional per-kernel event timing (benchmarks) ----
 struct Profiler {
