@@ -355,6 +355,10 @@ def main() -> int:
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    # the segment length the calls used (with the library's own plan it may be
+    # longer than the planned one once the sequence lengths are known)
+    c0 = kda.workspace_offsets(total, w.H, w.N, a.cp, a.seg)["counters"]
+    seg = int(ws[c0:c0 + 20].cpu().numpy().view(np.int32)[4])
     stream = torch.cuda.current_stream(dev)
     # Timed region 1: the K steps as a caller runs them (events only around
     # whole steps).  Timed region 2, right after it: the same K steps again

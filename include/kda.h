@@ -65,15 +65,31 @@ typedef enum { KDA_STATE_VK = 0, KDA_STATE_KV = 1 } kda_state_layout;
  * the cuLA PR #106 page, with its automatic, off and on settings). */
 typedef enum { KDA_CP_AUTO = 0, KDA_CP_OFF = 1, KDA_CP_FORCE = 2 } kda_cp_mode;
 
-/* Segment length, in chunks of 16 tokens, that kda_fwd will use for these
- * sizes: 0 means serial (one segment per sequence).  Pure host arithmetic.
+/* Planned segment length, in chunks of 16 tokens, for these sizes: 0 means
+ * serial (one segment per sequence).  Pure host arithmetic.
  *   total_tokens : B*T (all batch rows, or the packed varlen length)
  *   num_heads    : H >= 1;  num_seqs: N >= 1 (B for fixed length)
  *   cp_mode      : kda_cp_mode;  seg_chunks: > 0 forces that segment length in
  *                  AUTO and FORCE modes, 0 lets the library choose.
+ * With seg_chunks > 0 the call uses exactly this length.  With seg_chunks 0
+ * it is the shortest length the call may use, and the one the workspace is
+ * sized for: once the sequence lengths are known (on the device, for a varlen
+ * call; kda_fixed_seg_chunks, for a fixed-length one) the call may take a
+ * longer one, by at most a quarter and 63 chunks, where a model of how the
+ * hardware places the (segment, head) workgroups predicts a shorter run.  It
+ * does so for at most 16 sequences, H a multiple of 8 and N*H <= 256, and, in
+ * a varlen call, where the planned length is at least 128 chunks.  The
+ * length in use is in the counters and in every unit_tab row of the
+ * workspace (kda_ws_offset).  Every length gives the same results.
  * Returns a negative kda_status on invalid arguments. */
 int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num_seqs,
                             int32_t cp_mode, int32_t seg_chunks);
+
+/* Segment length a fixed-length kda_fwd call (B sequences of T tokens, no
+ * cu_seqlens) uses, with the arguments of that call: kda_plan_seg_chunks(B*T,
+ * num_heads, B, cp_mode, seg_chunks), possibly lengthened as described there.
+ * Pure host arithmetic.  Returns a negative kda_status on invalid arguments. */
+int32_t kda_fixed_seg_chunks(int32_t B, int64_t T, int32_t num_heads, int32_t cp_mode, int32_t seg_chunks);
 
 /* Workspace bytes kda_fwd needs for these sizes and this plan (the pages'
  * get_workspace_size(B*T, H), plus the sequence count and segment plan, since
@@ -156,15 +172,16 @@ int32_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const void*
  * the counters, see kda_write_fixed_tables).  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
  * order of kda_ws_offset.  Returns KDA_OK or a negative kda_status. */
 typedef enum {
-  KDA_WS_COUNTERS = 0,      /* int32[4]: n_chunks, n_segs, flags, early_stops; flags bits 0x1..0x8 name
-                               repaired cu_seqlens faults (first != 0, decreasing, last != total,
-                               out of range), 0x100 / 0x200 a chunk-kernel wait that gave up;
-                               early_stops counts the (segment, head) pairs whose second pass
-                               matched the checkpoint and stopped there */
+  KDA_WS_COUNTERS = 0,      /* int32[5]: n_chunks, n_segs, flags, early_stops, seg_chunks; flags bits
+                               0x1..0x8 name repaired cu_seqlens faults (first != 0, decreasing,
+                               last != total, out of range), 0x100 / 0x200 a chunk-kernel wait that
+                               gave up; early_stops counts the (segment, head) pairs whose second
+                               pass matched the checkpoint and stopped there; seg_chunks is the
+                               segment length the call used (0: serial) */
   KDA_WS_SEQ_START,         /* int32[N+1]   clamped sequence boundaries (last = end of the last sequence) */
   KDA_WS_SEQ_LEN,           /* int32[N]     clamped length */
   KDA_WS_SEQ_CHUNK_OFF,     /* int32[N+1]   prefix sums of ceil(len/16) */
-  KDA_WS_SEQ_SEG_OFF,       /* int32[N+1]   prefix sums of max(1, ceil(chunks/seg)) */
+  KDA_WS_SEQ_SEG_OFF,       /* int32[N+1]   prefix sums of max(1, ceil(chunks/seg)), seg the length in use */
   KDA_WS_CHUNK_TAB,         /* int32[max_chunks][2] (sequence, chunk in sequence) */
   KDA_WS_SEG_TAB,           /* int32[max_segs][4] (sequence, chunk begin, chunk end, segment in sequence) */
   KDA_WS_SEG_M,             /* fp32 [max_segs][H][128][128] segment transitions M^T (CP only) */
@@ -181,7 +198,8 @@ typedef enum {
                                (floor(chunks/seg); 1 per sequence when serial) */
   KDA_WS_UNIT_TAB,          /* int32[max_segs][8] the segments in dispatch order: (segment, sequence,
                                chunk begin, chunk end, segment in sequence, sequence start token,
-                               sequence length, -1); every full-length segment first, then the
+                               sequence length, segment length in use (0: serial)); every
+                               full-length segment first, then the
                                shorter last segments, each group in segment order (all -1 past the
                                live count) */
   KDA_WS_SEG_FIX,           /* fp32 [max_segs][H][128][128] state after a segment's first 4 chunks as the

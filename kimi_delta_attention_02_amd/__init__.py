@@ -33,6 +33,7 @@ __all__ = [
     "chunk_kda",
     "get_workspace_size",
     "plan_seg_chunks",
+    "fixed_seg_chunks",
     "workspace_offsets",
     "library_path",
     "load_library",
@@ -85,6 +86,8 @@ def load_library():
     i32, i64, sz, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
     lib.kda_plan_seg_chunks.argtypes = [i64, i32, i32, i32, i32]
     lib.kda_plan_seg_chunks.restype = i32
+    lib.kda_fixed_seg_chunks.argtypes = [i32, i64, i32, i32, i32]
+    lib.kda_fixed_seg_chunks.restype = i32
     lib.kda_get_workspace_size.argtypes = [i64, i32, i32, i32, i32]
     lib.kda_get_workspace_size.restype = sz
     lib.kda_workspace_offsets.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
@@ -131,9 +134,19 @@ def _raise(status: int):
 
 
 def plan_seg_chunks(total_tokens: int, num_heads: int, num_seqs: int = 1, cp_mode="auto", seg_chunks: int = 0) -> int:
-    """Segment length (chunks of 16 tokens) the library will use; 0 = serial."""
+    """Planned segment length (chunks of 16 tokens); 0 = serial.  It sizes the
+    workspace; with seg_chunks 0 a call may use a longer one (fixed_seg_chunks
+    for a fixed-length call; a varlen call's is in its workspace counters)."""
     r = load_library().kda_plan_seg_chunks(int(total_tokens), int(num_heads), int(num_seqs), _cp(cp_mode),
                                            int(seg_chunks))
+    if r < 0:
+        _raise(r)
+    return r
+
+
+def fixed_seg_chunks(B: int, T: int, num_heads: int, cp_mode="auto", seg_chunks: int = 0) -> int:
+    """Segment length a fixed-length call (B sequences of T tokens) uses; 0 = serial."""
+    r = load_library().kda_fixed_seg_chunks(int(B), int(T), int(num_heads), _cp(cp_mode), int(seg_chunks))
     if r < 0:
         _raise(r)
     return r

@@ -147,6 +147,39 @@ struct Layout {
   int32_t seg;
 };
 
+// The segment length of a fixed-length call (N sequences of T tokens): the
+// planned one, or, where the library chooses the plan (choose), the length
+// from seg .. seg + min(seg/4, 63) that the placement model seg_span predicts
+// fastest (the varlen index kernel makes the same choice on the device).  The
+// last shape's answer is kept per host thread.
+int32_t fixed_seg(int32_t seg, int32_t N, int64_t T, int32_t H, bool choose) {
+  if (!choose || !kda::span_model_applies(seg, N, H)) return seg;
+  struct Memo {
+    int32_t seg = -1, N = 0, H = 0, out = 0;
+    int64_t T = -1;
+  };
+  thread_local Memo m;
+  if (m.seg == seg && m.N == N && m.H == H && m.T == T) return m.out;
+  int nc[kda::kSpanMaxSeqs];
+  for (int32_t i = 0; i < N; ++i) nc[i] = (int)((T + kda::C - 1) / kda::C);
+  int cu[32];
+  int best = INT32_MAX;
+  int32_t out = seg;
+  for (int c = 0; c < kda::span_candidates(seg); ++c) {
+    const int span = kda::seg_span<1>(seg + c, N, nc, H, kCheckChunks, cu);
+    if (span < best) {
+      best = span;
+      out = seg + c;
+    }
+  }
+  m.seg = seg;
+  m.N = N;
+  m.H = H;
+  m.T = T;
+  m.out = out;
+  return out;
+}
+
 int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg_chunks, Layout* out) {
   const int32_t seg = plan(total, H, N, cp_mode, seg_chunks);
   if (seg < 0) return seg;
@@ -160,7 +193,7 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
     out->off[idx] = o;
     o = align_up(o + bytes, A);
   };
-  take(KDA_WS_COUNTERS, 16);
+  take(KDA_WS_COUNTERS, 4 * 5);
   take(KDA_WS_SEQ_START, 4 * ((int64_t)N + 1));
   take(KDA_WS_SEQ_LEN, 4 * (int64_t)N);
   take(KDA_WS_SEQ_CHUNK_OFF, 4 * ((int64_t)N + 1));
@@ -310,7 +343,11 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   sg.sync = cp ? reinterpret_cast<uint32_t*>(ws + lay.off[KDA_WS_SEG_SYNC]) : nullptr;
   sg.epoch = next_epoch();
   sg.chk_chunks = cp ? kCheckChunks : 0;
-  sg.seg_chunks = cp ? (int)lay.seg : 0;
+  // where the library chooses the plan, the tables may use a longer segment
+  // length than the planned one (fixed length: chosen here; varlen: by the
+  // index kernel)
+  const bool choose = a.seg_chunks == 0;
+  sg.seg_chunks = cp ? (a.cu_seqlens ? (int)lay.seg : fixed_seg(lay.seg, pr.N, a.T, a.H, choose)) : 0;
   const int64_t mc = lay.off[KDA_WS_MAX_CHUNKS];
   const int64_t ms = lay.off[KDA_WS_MAX_SEGS];
   const int32_t N = pr.N;
@@ -341,7 +378,7 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   p.total_tokens = pr.total;
 
   hipError_t e;
-  e = kda::launch_index(a.cu_seqlens, N, a.T, pr.total, lay.seg, mc, ms, t, s);
+  e = kda::launch_index(a.cu_seqlens, N, a.T, pr.total, lay.seg, a.H, kCheckChunks, choose, mc, ms, t, s);
   // Long units run their first (or only) pass with 4 consumer wavefronts of two
   // state tiles each, short ones with 8 of one tile (measured: 2-3 % faster
   // at 256-512 chunks per unit, 4 % slower at 36).  The second pass keeps 8:
@@ -355,7 +392,8 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   int64_t rows = ms;
   if (!a.cu_seqlens) {
     const int64_t nc = (a.T + kda::C - 1) / kda::C;
-    const int64_t nsq = lay.seg > 0 ? (nc > 0 ? (nc + lay.seg - 1) / lay.seg : 1) : 1;
+    const int64_t sgc = sg.seg_chunks;
+    const int64_t nsq = sgc > 0 ? (nc > 0 ? (nc + sgc - 1) / sgc : 1) : 1;
     rows = std::min(ms, (int64_t)N * nsq);
   }
   if (e == hipSuccess)
@@ -414,6 +452,15 @@ int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num
   return plan(total_tokens, num_heads, num_seqs, cp_mode, seg_chunks);
 }
 
+int32_t kda_fixed_seg_chunks(int32_t B, int64_t T, int32_t num_heads, int32_t cp_mode, int32_t seg_chunks) {
+  g_last_error.clear();
+  if (B < 1 || T < 0) return fail(KDA_ERR_INVALID_ARG, "B=%d must be >= 1 and T=%lld >= 0", B, (long long)T);
+  if (T > 0 && B > kMaxTokens / T) return fail(KDA_ERR_INVALID_ARG, "B*T too large");
+  const int32_t seg = plan((int64_t)B * T, num_heads, B, cp_mode, seg_chunks);
+  if (seg < 0) return seg;
+  return fixed_seg(seg, B, T, num_heads, seg_chunks == 0);
+}
+
 size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,
                               int32_t seg_chunks) {
   Layout lay;
@@ -446,7 +493,8 @@ int32_t kda_write_fixed_tables(int32_t B, int64_t T, int32_t H, int32_t cp_mode,
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %lld", workspace_bytes,
                 (long long)lay.off[KDA_WS_TOTAL]);
   const kda::Tables t = carve_tables(static_cast<uint8_t*>(workspace), lay, T);
-  const hipError_t e = kda::launch_index_fixed(B, (int)T, lay.seg, t, static_cast<hipStream_t>(stream));
+  const hipError_t e = kda::launch_index_fixed(B, (int)T, fixed_seg(lay.seg, B, T, H, seg_chunks == 0), t,
+                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   return KDA_OK;
 }

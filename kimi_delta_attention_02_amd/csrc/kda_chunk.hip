@@ -810,9 +810,10 @@ __device__ __forceinline__ bool decided_at_checkpoint(const Problem& p, const Se
 
 // One row of the dispatch table: segment (row of the segment tables), its
 // sequence, its chunk range [cb, ce) in global chunk numbers, its index in the
-// sequence, and the sequence's first token and length.
+// sequence, the sequence's first token and length, and the segment length of
+// the call (0: serial).
 struct Unit {
-  int sidx, seq, cb, ce, j, start, len;
+  int sidx, seq, cb, ce, j, start, len, seg;
 };
 
 // MODE 0: a sequence of a serial call from its initial state.
@@ -834,7 +835,7 @@ __device__ __forceinline__ void chunk_body(Smem& sm, const Problem& p, const Tab
   // one segment per sequence)
   const int seq_len = u.len;
   const int seq_nc = (seq_len + C - 1) / C;
-  const int seg_c = sg.seg_chunks;
+  const int seg_c = u.seg;
   const int ns = seg_c > 0 ? (seq_nc > 0 ? (seq_nc + seg_c - 1) / seg_c : 1) : 1;
   const int first_chunk = cb - j * seg_c;
   if (MODE == 2 && j == 0) return;  // segment 0 has its true start state in the first pass
@@ -1390,14 +1391,14 @@ __global__ __launch_bounds__(NTHREADS) void KDA_CHUNK_KERNEL(Problem p, Tables t
     if (MODE != 2 && blockIdx.x == 0 && threadIdx.x == 0) fixed_counters(p.N, t.fixed_T, sg.seg_chunks, t);
     int32_t row[8];
     if (!fixed_unit_row(p.N, t.fixed_T, sg.seg_chunks, k, row)) return;
-    u = Unit{row[0], row[1], row[2], row[3], row[4], row[5], row[6]};
+    u = Unit{row[0], row[1], row[2], row[3], row[4], row[5], row[6], row[7]};
   } else {
     // the whole row in one read (rows past the live units hold -1); the grid
     // has one row of blocks per table row
     const int4 r0 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k];
     const int4 r1 = reinterpret_cast<const int4*>(t.unit_tab)[2 * k + 1];
     if (r0.x < 0) return;
-    u = Unit{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z};
+    u = Unit{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
   }
   chunk_body<MODE>(sm, p, t, sg, u, h);
 }

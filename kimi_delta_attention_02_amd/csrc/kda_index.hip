@@ -30,9 +30,17 @@
 //       first, then the shorter last segments of their sequences, so that the
 //       long units start first).  Rows past the live counts are -1.
 // A unit_tab row is (segment, seq, first chunk, end chunk, segment in seq,
-// sequence start token, sequence length, -1): everything the chunk kernel needs
-// to place its unit, in one 32-byte row, so that its first input loads wait
-// for a single table read.
+// sequence start token, sequence length, segment length): everything the
+// chunk kernel needs to place its unit, in one 32-byte row, so that its first
+// input loads wait for a single table read.
+//
+// Where the library chooses the plan (seg_chunks 0) and plans segments of at
+// least kSpanDeviceMinSeg chunks, step 1 may lengthen the planned segment
+// length once the sequence lengths are known: wavefront 0 scores up to 64
+// lengths from the planned one up, one per lane, with the placement model
+// seg_span (kda_internal.h), and the best one is used for every table and
+// recorded in the counters and in every unit_tab row.  The planned length
+// sizes the workspace; a longer one needs fewer rows.
 #include "kda_internal.h"
 
 namespace kda {
@@ -84,9 +92,12 @@ struct AddOp {
 // (step 1 of the header).  When sst/coff/soff are given (LDS, N + 1 entries
 // each), the boundaries and the chunk and segment prefix sums are also kept
 // there, and the lengths are computed from the LDS copy.
-__device__ void index_scan_body(const int32_t* __restrict__ cu, int N, long long T_row, long long total,
-                                int seg_chunks, Tables t, long long* smem, int* flags, int* sst, int* coff,
-                                int* soff, int* foff) {
+// Returns the segment length the tables use.  With choose set, span_cu (LDS,
+// 32 x 64 + kSpanMaxSeqs ints) and seg_sel (LDS) serve the choice of the
+// segment length.
+__device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long T_row, long long total,
+                               int seg_chunks, int H, int K, bool choose, Tables t, long long* smem, int* flags,
+                               int* sst, int* coff, int* soff, int* foff, int* span_cu, int* seg_sel) {
   if (threadIdx.x == 0) *flags = 0;
   __syncthreads();
   // pass 1: boundaries b_i, i = 0..N (clamped running maximum of the offsets)
@@ -119,6 +130,32 @@ __device__ void index_scan_body(const int32_t* __restrict__ cu, int N, long long
   }
   __threadfence_block();
   __syncthreads();
+  // the segment length: lane s of wavefront 0 scores length seg_chunks + s
+  if (choose && seg_chunks >= kSpanDeviceMinSeg && span_model_applies(seg_chunks, N, H)) {
+    int* nc = span_cu + 32 * 64;  // chunks of each sequence
+    if (threadIdx.x < N) {
+      const int32_t* bnd = sst ? sst : t.seq_start;
+      nc[threadIdx.x] = (bnd[threadIdx.x + 1] - bnd[threadIdx.x] + C - 1) / C;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int lane = (int)threadIdx.x;
+      unsigned long long key = ~0ull;
+      if (lane < span_candidates(seg_chunks)) {
+        const int len = seg_chunks + lane;
+        const int span = seg_span<64>(len, N, nc, H, K, span_cu + lane);
+        key = ((unsigned long long)(unsigned)span << 32) | (unsigned)len;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long y = __shfl_xor(key, o, 64);
+        key = y < key ? y : key;
+      }
+      if (lane == 0) *seg_sel = (int)(key & 0xFFFFFFFFu);
+    }
+    __syncthreads();
+    seg_chunks = *seg_sel;
+  }
   // pass 2: lengths, chunk and segment counts, exclusive prefix sums
   long long c_carry = 0, s_carry = 0, f_carry = 0;
   if (threadIdx.x == 0) {
@@ -161,14 +198,19 @@ __device__ void index_scan_body(const int32_t* __restrict__ cu, int N, long long
     t.counters[CNT_N_SEGS] = (int32_t)s_carry;
     t.counters[CNT_FLAGS] = *flags;
     t.counters[CNT_EARLY_STOPS] = 0;
+    t.counters[CNT_SEG_CHUNKS] = seg_chunks;
   }
+  return seg_chunks;
 }
 
 __global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __restrict__ cu, int N, long long T_row,
-                                                               long long total, int seg_chunks, Tables t) {
+                                                               long long total, int seg_chunks, int H, int K,
+                                                               int choose, Tables t) {
   __shared__ long long smem[SCAN_WAVES];
-  __shared__ int flags;
-  index_scan_body(cu, N, T_row, total, seg_chunks, t, smem, &flags, nullptr, nullptr, nullptr, nullptr);
+  __shared__ int flags, seg_sel;
+  __shared__ int span_cu[32 * 64 + kSpanMaxSeqs];
+  index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, t, smem, &flags, nullptr, nullptr, nullptr,
+                  nullptr, span_cu, &seg_sel);
 }
 
 // largest j in [0, n) with off[j] <= x, given off[0] = 0 <= x and off non-decreasing
@@ -210,7 +252,7 @@ __device__ __forceinline__ void seg_row(int32_t* row, int sq, int idx, const int
 // the full-length segments in segment order, then the others (a sequence's
 // shorter last segment) in segment order.
 __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32_t* row, const int* soff,
-                                         const int* foff, int n_full, int seq_start, int seq_len) {
+                                         const int* foff, int n_full, int seq_start, int seq_len, int seg) {
   const int sq = row[0], j = row[3];
   const int full_here = foff[sq + 1] - foff[sq];
   const int rank = j < full_here ? foff[sq] + j : n_full + (soff[sq] - foff[sq]);
@@ -222,14 +264,14 @@ __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32
   u[4] = row[3];
   u[5] = seq_start;
   u[6] = seq_len;
-  u[7] = -1;
+  u[7] = seg;
 }
 
-__global__ __launch_bounds__(256) void kda_index_fill(int N, int seg_chunks, long long max_chunks, long long max_segs,
-                                                      Tables t) {
+__global__ __launch_bounds__(256) void kda_index_fill(int N, long long max_chunks, long long max_segs, Tables t) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int n_chunks = t.counters[CNT_N_CHUNKS];
   const int n_segs = t.counters[CNT_N_SEGS];
+  const int seg_chunks = t.counters[CNT_SEG_CHUNKS];  // the length kda_index_scan chose
   if (idx < max_chunks) {
     int a = -1, b = -1;
     if (idx < n_chunks) {
@@ -249,7 +291,7 @@ __global__ __launch_bounds__(256) void kda_index_fill(int N, int seg_chunks, lon
       while (s + 1 <= N && t.seq_seg_off[s + 1] <= (int)idx) ++s;
       seg_row(row, s, (int)idx, t.seq_chunk_off, t.seq_seg_off, seg_chunks);
       put_unit(t.unit_tab, (int)idx, row, t.seq_seg_off, t.seq_full_off, t.seq_full_off[N], t.seq_start[s],
-               t.seq_len[s]);
+               t.seq_len[s], seg_chunks);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) t.unit_tab[8 * idx + k] = -1;
@@ -263,12 +305,14 @@ __global__ __launch_bounds__(256) void kda_index_fill(int N, int seg_chunks, lon
 // rows: one binary search in the LDS copy of the prefix sums for its first
 // row, then a forward walk (the owner of consecutive rows never decreases).
 __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* __restrict__ cu, int N, long long T_row,
-                                                                long long total, int seg_chunks, int max_chunks,
-                                                                int max_segs, Tables t) {
+                                                                long long total, int seg_chunks, int H, int K,
+                                                                int choose, int max_chunks, int max_segs, Tables t) {
   __shared__ long long smem[SCAN_WAVES];
-  __shared__ int flags;
+  __shared__ int flags, seg_sel;
   __shared__ int sst[FUSED_MAX_N + 1], coff[FUSED_MAX_N + 1], soff[FUSED_MAX_N + 1], foff[FUSED_MAX_N + 1];
-  index_scan_body(cu, N, T_row, total, seg_chunks, t, smem, &flags, sst, coff, soff, foff);
+  __shared__ int span_cu[32 * 64 + kSpanMaxSeqs];
+  seg_chunks = index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, t, smem, &flags, sst, coff, soff,
+                               foff, span_cu, &seg_sel);
   __syncthreads();
   const int n_chunks = coff[N], n_segs = soff[N];
   {
@@ -297,7 +341,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* _
       if (r < n_segs) {
         while (a + 1 <= N && soff[a + 1] <= r) ++a;
         seg_row(row, a, r, coff, soff, seg_chunks);
-        put_unit(t.unit_tab, r, row, soff, foff, foff[N], sst[a], sst[a + 1] - sst[a]);
+        put_unit(t.unit_tab, r, row, soff, foff, foff[N], sst[a], sst[a + 1] - sst[a], seg_chunks);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) t.unit_tab[8 * r + k] = -1;
@@ -327,27 +371,28 @@ hipError_t launch_index_fixed(int N, int L, int seg, Tables t, hipStream_t st) {
 }
 
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
-                        int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st) {
+                        int H, int K, bool choose, int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st) {
   if (!cu_seqlens) return hipSuccess;  // fixed length: written by the first chunk-kernel launch
   if (N <= FUSED_MAX_N && max_chunks <= FUSED_MAX_ROWS && max_segs <= FUSED_MAX_ROWS) {
     hipEvent_t e0, e1;
     stage_events(KDA_STAGE_INDEX, &e0, &e1);
     hipExtLaunchKernelGGL(kda_index_fused, dim3(1), dim3(SCAN_THREADS), 0, st, e0, e1, 0, cu_seqlens, N,
-                          (long long)T_row, (long long)total_tokens, seg_chunks, (int)max_chunks, (int)max_segs, t);
+                          (long long)T_row, (long long)total_tokens, seg_chunks, H, K, (int)choose, (int)max_chunks,
+                          (int)max_segs, t);
     return hipGetLastError();
   }
   hipEvent_t e0, e1;
   stage_events(KDA_STAGE_INDEX, &e0, &e1);
   hipExtLaunchKernelGGL(kda_index_scan, dim3(1), dim3(SCAN_THREADS), 0, st, e0, e1, 0, cu_seqlens, N,
-                        (long long)T_row, (long long)total_tokens, seg_chunks, t);
+                        (long long)T_row, (long long)total_tokens, seg_chunks, H, K, (int)choose, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = max_chunks > max_segs ? max_chunks : max_segs;
   if (rows > 0) {
     const unsigned blocks = (unsigned)((rows + 255) / 256);
     stage_events(KDA_STAGE_INDEX, &e0, &e1);
-    hipExtLaunchKernelGGL(kda_index_fill, dim3(blocks), dim3(256), 0, st, e0, e1, 0, N, seg_chunks,
-                          (long long)max_chunks, (long long)max_segs, t);
+    hipExtLaunchKernelGGL(kda_index_fill, dim3(blocks), dim3(256), 0, st, e0, e1, 0, N, (long long)max_chunks,
+                          (long long)max_segs, t);
     e = hipGetLastError();
   }
   return e;

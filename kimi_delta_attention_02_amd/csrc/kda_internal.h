@@ -27,6 +27,7 @@ constexpr int CNT_N_CHUNKS = 0;
 constexpr int CNT_N_SEGS = 1;
 constexpr int CNT_FLAGS = 2;
 constexpr int CNT_EARLY_STOPS = 3;  // (segment, head) pairs whose second pass stopped at the checkpoint
+constexpr int CNT_SEG_CHUNKS = 4;   // segment length in use (0: serial)
 
 // Pointers into a carved workspace (device addresses).
 struct Tables {
@@ -95,7 +96,7 @@ struct Seg {
   uint32_t* sync;
   uint32_t epoch;
   int chk_chunks;
-  int seg_chunks;  // segment length in chunks (0: serial, one segment per sequence)
+  int seg_chunks;  // segment length in chunks of a fixed-length call (0: serial); a varlen call's is in unit_tab
 };
 
 // ---- launchers (host functions defined next to their kernels) ----
@@ -105,8 +106,10 @@ struct Seg {
 // start and end; otherwise both stay null and the launch is a plain one.
 void stage_events(int stage, hipEvent_t* start, hipEvent_t* stop);
 hipError_t launch_index_fixed(int N, int L, int seg, Tables t, hipStream_t st);
+// choose: the library chooses the plan (seg_chunks is the planned, shortest
+// length; the tables may use a longer one, see seg_span); K: chk_chunks
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
-                        int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
+                        int H, int K, bool choose, int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
 // producer/consumer chunk kernel: one launch per pass (phase 0: every segment,
 // phase 1: segments >= 1 from their start states, merged in the same launch)
 hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,
@@ -244,7 +247,7 @@ __device__ __forceinline__ bool fixed_unit_row(int N, int L, int seg, int r, int
   row[4] = j;
   row[5] = sq * L;
   row[6] = L;
-  row[7] = -1;
+  row[7] = seg;
   return true;
 }
 
@@ -255,6 +258,7 @@ __device__ __forceinline__ void fixed_counters(int N, int L, int seg, const Tabl
   t.counters[CNT_N_SEGS] = N * s.ns;
   t.counters[CNT_FLAGS] = 0;
   t.counters[CNT_EARLY_STOPS] = 0;
+  t.counters[CNT_SEG_CHUNKS] = seg;
 }
 
 // Every table row of a fixed-length call, rows tid, tid + nthr, ... (the same
@@ -295,6 +299,87 @@ __device__ __forceinline__ void fixed_tables(int tid, int nthr, int N, int L, in
       for (int q = 0; q < 4; ++q) t.seg_tab[4 * (long long)r + q] = -1;
     }
   }
+}
+
+// ---- segment length of a plan the library chooses ----
+// The host plans the shortest segment length, which sizes the workspace: one
+// that would give 256 (segment, head) units if every sequence split evenly.
+// How the units of a length s then pack onto the chip depends on the
+// sequence lengths (a sequence's last segment is shorter, a short sequence is
+// one short unit) and on how the hardware places workgroups: it deals them to
+// the 8 XCDs in turn and, inside an XCD, to its 4 shader engines in turn (8
+// CUs each, one chunk-kernel workgroup per CU), in order, so that a workgroup
+// whose engine has no free CU holds back every later one of its XCD, although
+// another engine may have one free (seen in per-workgroup clock stamps).
+// seg_span replays that placement for one XCD (H a multiple of 8, so that
+// every XCD gets the same share) and returns the first pass's predicted span
+// in chunk steps: a unit costs the chunks it runs plus a fixed start cost.
+// The units come in dispatch-table order: every full-length segment, then
+// the other ones, each group in segment order.  A full segment runs K chunks
+// into the next one when that one is longer than K; a later segment of K
+// chunks or fewer ends at once; a sequence shorter than s is one unit.
+// Sequence i has nc[i] chunks; cu holds 32 ints at stride STRIDE (the CUs of
+// one XCD, engine-major).
+constexpr int kSpanStartCost = 4;    // a unit's fixed start cost, in chunk steps (measured 2 to 7)
+constexpr int kSpanCandidates = 64;  // lengths tried: seg .. seg + min(seg / 4, 63)
+constexpr int kSpanMaxSeqs = 16;
+// The index kernel spends a few microseconds on the choice (one wavefront
+// replays up to 64 placements per candidate); it makes it only for a planned
+// length of at least this many chunks, whose first pass takes ~180 us or more.
+constexpr int kSpanDeviceMinSeg = 128;
+
+__host__ __device__ inline bool span_model_applies(int seg, int N, int H) {
+  return seg > 0 && N >= 1 && N <= kSpanMaxSeqs && H % 8 == 0 && N * H <= 256;
+}
+
+__host__ __device__ inline int span_candidates(int seg) {
+  const int q = seg / 4;
+  return 1 + (q < kSpanCandidates - 1 ? q : kSpanCandidates - 1);
+}
+
+template <int STRIDE>
+__host__ __device__ inline int seg_span(int s, int N, const int* nc, int H, int K, int* cu) {
+  for (int k = 0; k < 32; ++k) cu[k * STRIDE] = 0;
+  const int per = H / 8;  // workgroups of a unit's row per XCD
+  int last = 0, span = 0, blk = 0;
+  auto place = [&](int cost) {
+    for (int m = 0; m < per; ++m, ++blk) {
+      int* e = cu + (blk & 3) * 8 * STRIDE;  // its shader engine's 8 CUs
+      if (blk < 32) {  // the first 32 fill the empty CUs: engine blk % 4, its CU blk / 4, at once
+        e[(blk >> 2) * STRIDE] = cost + kSpanStartCost;
+        span = cost + kSpanStartCost > span ? cost + kSpanStartCost : span;
+        continue;
+      }
+      int best = e[0], bk = 0;
+      for (int c = 1; c < 8; ++c) {
+        const int v = e[c * STRIDE];
+        if (v < best) {
+          best = v;
+          bk = c;
+        }
+      }
+      const int st = best > last ? best : last;  // in order: never before the previous one
+      last = st;
+      const int fin = st + cost + kSpanStartCost;
+      e[bk * STRIDE] = fin;
+      span = fin > span ? fin : span;
+    }
+  };
+  for (int i = 0; i < N; ++i) {
+    const int n = nc[i], f = n / s, rem = n - f * s;
+    for (int j = 0; j < f; ++j) {
+      const int nn = j + 1 < f ? s : rem;  // the next segment's chunks
+      place(s + (nn > K ? K : 0));
+    }
+  }
+  for (int i = 0; i < N; ++i) {
+    const int n = nc[i], f = n / s, rem = n - f * s;
+    if (f == 0)
+      place(n);
+    else if (rem > 0)
+      place(rem > K ? rem : 0);
+  }
+  return span;
 }
 
 }  // namespace kda

@@ -60,6 +60,53 @@ def test_plan_modes():
         kda.plan_seg_chunks(100, 0, 1)
 
 
+def test_placement_model_worked_example():
+    """Three sequences of 8192 tokens (512 chunks) at H = 16, planned length 96,
+    by hand: 15 full segments of 96 + 4 run-on chunks (finish at 104 with the
+    start cost), then three last segments of 32.  Per XCD a segment is two
+    workgroups, local indices 2r and 2r + 1, so even rows take engines 0 and 1
+    and odd rows engines 2 and 3; the 8 even full rows fill engines 0 and 1.
+    The odd last segment starts at once, but the even one after it waits for
+    engine 0/1 until 104 and ends at 104 + 32 + 4 = 140, the next in order with
+    it.  At 102, 512 = 5 * 102 + 2: the last segments (2 <= K chunks) end at once
+    and the fifth full segment runs on no further, so the span is 102 + 4 + 4."""
+    from tests.span_model import chosen_seg, first_pass_span, unit_costs
+
+    assert unit_costs(96, [512] * 3) == [100] * 15 + [32] * 3
+    assert first_pass_span(96, [512] * 3, 16) == 140
+    assert first_pass_span(102, [512] * 3, 16) == 110
+    assert chosen_seg(96, [8192] * 3, 16) == 102
+    # a single sequence that splits evenly is kept: 16 units of 256 (+4) fill the chip once
+    assert chosen_seg(256, [65536], 16) == 256
+
+
+def test_fixed_seg_chunks_follows_placement_model():
+    """Where the library chooses the plan, a fixed-length call may lengthen
+    the planned segment length, by at most a quarter and 63 chunks, to the one
+    the placement model predicts fastest; explicit lengths, serial plans and
+    shapes outside the model (more than 16 sequences, H not a multiple of 8)
+    keep the planned one."""
+    from tests.span_model import chosen_seg
+
+    for B, T, H in [(1, 65536, 16), (2, 4096, 16), (3, 8192, 16), (1, 70656, 16), (3, 20000, 16), (5, 7777, 16),
+                    (2, 100000, 8), (7, 5000, 8), (16, 2000, 8), (1, 65536, 32), (4, 10000, 8), (2, 30000, 24),
+                    (2, 30000, 12), (17, 9000, 8)]:
+        p = kda.plan_seg_chunks(B * T, H, B, "auto")
+        got = kda.fixed_seg_chunks(B, T, H)
+        assert got == chosen_seg(p, [T] * B, H), (B, T, H)
+        assert p <= got <= p + min(p // 4, 63)
+        assert kda.fixed_seg_chunks(B, T, H, "force") == chosen_seg(kda.plan_seg_chunks(B * T, H, B, "force"),
+                                                                    [T] * B, H)
+    assert kda.fixed_seg_chunks(3, 8192, 16) == 102
+    assert kda.fixed_seg_chunks(3, 8192, 16, "auto", 96) == 96
+    assert kda.fixed_seg_chunks(3, 8192, 16, "off") == 0
+    assert kda.fixed_seg_chunks(2, 30000, 12) == kda.plan_seg_chunks(60000, 12, 2, "auto")
+    with pytest.raises(kda.KdaError):
+        kda.fixed_seg_chunks(0, 100, 16)
+    with pytest.raises(kda.KdaError):
+        kda.fixed_seg_chunks(1, 100, 0)
+
+
 def test_workspace_layout_consistent():
     for args in [(256, 2, 1, "off", 0), (8192, 16, 2, "auto", 0), (79890, 16, 7, "force", 64), (0, 4, 3, "auto", 0)]:
         size = kda.get_workspace_size(*args)

@@ -221,21 +221,46 @@ def test_mixed_value_scales_segmented_bit_identical():
 
 
 # ------------------------------------------------------------------- index tables, bit-exact
-@pytest.mark.parametrize("lens,seg,fixed", [
-    ([1023, 1025, 1, 16, 4097, 8191, 65537], 64, False), ([0, 1, 15, 16, 17, 0], 1, False),
-    ([65536] + [1024] * 5, 0, False), ([65537], 37, False),
-    # past the one-workgroup form's limits (4095 sequences, 16384 rows): the two-launch form
-    ([3] * 5000, 0, False), ([300000], 64, False),
-    # fixed length (no cu_seqlens): the closed-form tables
-    ([100] * 3, 2, True), ([4096] * 2, 32, True), ([33] * 7, 0, True), ([512], 16, True)])
-def test_index_tables_bit_exact(lens, seg, fixed):
-    if fixed:
-        w = kda_inputs.custom(B=len(lens), T=lens[0], H=1, seed=28, name="tables fixed", init_std=None)
+def _zero_inputs(w):
+    """Inputs of the workload's shapes, all zero, made on the device (the index
+    tables depend on the sequence lengths only)."""
+    z = {n: torch.zeros((w.B, w.T, w.H, 128), dtype=torch.bfloat16, device="cuda") for n in ("q", "k", "v", "g")}
+    z["beta"] = torch.zeros((w.B, w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    z["A_log"] = torch.zeros(w.H, dtype=torch.float32, device="cuda")
+    z["dt_bias"] = torch.zeros((w.H, 128), dtype=torch.float32, device="cuda")
+    z["initial_state"] = None
+    cu = None
+    if w.seqlens is not None:
+        cu = np.concatenate([[0], np.cumsum(np.asarray(w.seqlens, dtype=np.int64))]).astype(np.int32)
+        z["cu_seqlens"] = torch.from_numpy(cu).to("cuda")
     else:
-        w = kda_inputs.custom(seqlens=lens, H=1, seed=28, name="tables", init_std=None)
-    x = kda_inputs.make_inputs(w)
-    d = dev_inputs(x)
-    mode = "force" if seg else "off"
+        z["cu_seqlens"] = None
+    x = {"scale": float(np.float32(w.scale)), "lower_bound": float(np.float32(w.lower_bound)), "cu_seqlens": cu}
+    return x, z
+
+
+@pytest.mark.parametrize("lens,seg,fixed,H,mode", [
+    ([1023, 1025, 1, 16, 4097, 8191, 65537], 64, False, 1, None), ([0, 1, 15, 16, 17, 0], 1, False, 1, None),
+    ([65536] + [1024] * 5, 0, False, 1, None), ([65537], 37, False, 1, None),
+    # past the one-workgroup form's limits (4095 sequences, 16384 rows): the two-launch form
+    ([3] * 5000, 0, False, 1, None), ([300000], 64, False, 1, None),
+    # fixed length (no cu_seqlens): the closed-form tables
+    ([100] * 3, 2, True, 1, None), ([4096] * 2, 32, True, 1, None), ([33] * 7, 0, True, 1, None),
+    ([512], 16, True, 1, None),
+    # the library's own plan at H = 16: the segment length follows the placement model
+    # (varlen: chosen on the device, one and two-launch forms; fixed length: on the host)
+    ([65536] + [1024] * 5, 0, False, 16, "auto"), ([1023, 1025, 1, 16, 4097, 8191, 65537], 0, False, 16, "auto"),
+    ([300000, 5000, 70], 0, False, 16, "auto"), ([8192] * 3, 0, True, 16, "auto"), ([65536], 0, False, 16, "auto"),
+    ([24000, 3000, 1000], 0, False, 16, "auto")])
+def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
+    from tests.span_model import chosen_seg
+
+    if fixed:
+        w = kda_inputs.custom(B=len(lens), T=lens[0], H=H, seed=28, name="tables fixed", init_std=None)
+    else:
+        w = kda_inputs.custom(seqlens=lens, H=H, seed=28, name="tables", init_std=None)
+    x, d = _zero_inputs(w)
+    mode = mode or ("force" if seg else "off")
     _, _, ws = run_gpu(w, x, d, cp_mode=mode, seg_chunks=seg, want_final=False)
     import kimi_delta_attention_02_amd as kda
 
@@ -244,10 +269,18 @@ def test_index_tables_bit_exact(lens, seg, fixed):
         torch.cuda.synchronize()
 
     offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, mode, seg)
-    ref = O.index_tables(lens, 16, seg if seg else None)
+    planned = kda.plan_seg_chunks(w.B * w.T, w.H, w.N, mode, seg)
+    used = chosen_seg(planned, lens, H, varlen=not fixed) if seg == 0 else planned
+    if mode == "auto":
+        assert used > 0
+        if fixed:
+            assert kda.fixed_seg_chunks(w.B, w.T, w.H, mode, seg) == used
+    say(f"tables {len(lens)} sequences H={H} {mode}: planned {planned}, used {used}")
+    ref = O.index_tables(lens, 16, used if used else None)
     N = len(lens)
-    cnt = read_ws(ws, offs, "counters", 4, np.int32)
+    cnt = read_ws(ws, offs, "counters", 5, np.int32)
     assert cnt[0] == ref["seq_chunk_off"][-1] and cnt[1] == ref["seq_seg_off"][-1] and cnt[2] == 0
+    assert cnt[4] == used
     np.testing.assert_array_equal(read_ws(ws, offs, "seq_chunk_off", N + 1, np.int32), ref["seq_chunk_off"])
     np.testing.assert_array_equal(read_ws(ws, offs, "seq_seg_off", N + 1, np.int32), ref["seq_seg_off"])
     nch, nsg = int(cnt[0]), int(cnt[1])
@@ -260,12 +293,13 @@ def test_index_tables_bit_exact(lens, seg, fixed):
     assert (read_ws(ws, offs, "seg_tab", 4 * ms, np.int32)[4 * nsg:] == -1).all()
     # dispatch order: every full-length segment (seg chunks), then the others,
     # each group in segment order (serial: every sequence counts as full); a
-    # row also carries its sequence's first token and length
+    # row also carries its sequence's first token and length and the segment
+    # length in use
     st = ref["seg_tab"]
     starts = np.concatenate([[0], np.cumsum(lens)])
-    full = [i for i in range(nsg) if not seg or st[i][2] - st[i][1] == seg]
-    rest = [i for i in range(nsg) if seg and st[i][2] - st[i][1] != seg]
-    want = np.array([[i, *st[i], starts[st[i][0]], lens[st[i][0]], -1] for i in full + rest],
+    full = [i for i in range(nsg) if not used or st[i][2] - st[i][1] == used]
+    rest = [i for i in range(nsg) if used and st[i][2] - st[i][1] != used]
+    want = np.array([[i, *st[i], starts[st[i][0]], lens[st[i][0]], used] for i in full + rest],
                     dtype=np.int32).reshape(-1, 8)
     unit = read_ws(ws, offs, "unit_tab", 8 * ms, np.int32).reshape(-1, 8)
     np.testing.assert_array_equal(unit[:nsg], want)
