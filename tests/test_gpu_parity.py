@@ -404,6 +404,42 @@ def test_config4_segmented_bit_identical_to_serial(name):
         assert stops > 0  # the checkpoint path is the one measured at this size
 
 
+@pytest.mark.parametrize("kind", ["fixed", "varlen"])
+def test_lengthened_segments_bit_identical_to_serial(kind):
+    """Calls whose segment length the library lengthens past the planned one:
+    B=3 T=8192 H=16 (planned 96, chosen on the host: 102, so each sequence ends
+    in a 2-chunk segment that the first pass skips) and the varlen
+    40000+20000+9000 H=16 (planned 270, chosen in the index kernel).  Against
+    the serial call bit for bit, and against the oracle on sampled chains."""
+    from tests.span_model import chosen_seg
+    import kimi_delta_attention_02_amd as kda
+
+    if kind == "fixed":
+        w = kda_inputs.custom(B=3, T=8192, H=16, lower_bound=-5.0, seed=44, name="B3_T8192_H16")
+        lens = [8192] * 3
+    else:
+        lens = [40000, 20000, 9000]
+        w = kda_inputs.custom(seqlens=lens, H=16, lower_bound=-5.0, seed=45, name="varlen_40000+20000+9000_H16")
+    say(f"case {w.name} lengthened segments")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    planned = kda.plan_seg_chunks(w.B * w.T, w.H, w.N, "auto")
+    used = chosen_seg(planned, lens, w.H, varlen=kind == "varlen")
+    assert used > planned
+    if kind == "fixed":
+        assert kda.fixed_seg_chunks(w.B, w.T, w.H) == used
+    out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
+    out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="auto")
+    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, "auto", 0)
+    cnt = read_ws(ws, offs, "counters", 5, np.int32)
+    stops = int(cnt[3])
+    say(f"{w.name}: planned {planned}, used {int(cnt[4])}, early stops {stops}")
+    assert cnt[4] == used
+    assert torch.equal(out_c.view(torch.int16), out_s.view(torch.int16)) and torch.equal(fin_c, fin_s)
+    assert stops > 0
+    check_against_oracle(w, x, out_c, fin_c, seqs=[2], heads=[1, 14], final_dtype=w.state_dtype)
+
+
 def test_config4_slow_decay_segmented():
     """T=65536 H=16 at lower_bound -0.1: the start state's influence has not
     decayed after a segment's first 4 chunks, so the second pass runs every
