@@ -440,6 +440,37 @@ def test_lengthened_segments_bit_identical_to_serial(kind):
     check_against_oracle(w, x, out_c, fin_c, seqs=[2], heads=[1, 14], final_dtype=w.state_dtype)
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_random_varlen_mix_segment_choice(i):
+    """Seeded random varlen mixes at H=16 (2-15 sequences, 33-60K tokens) on
+    the library's own plan, where the index kernel chooses the segment length:
+    the length in use equals the placement model's choice, the result equals
+    the serial call bit for bit (lower bound -5), and sampled chains match the
+    oracle."""
+    from tests.span_model import chosen_seg
+    import kimi_delta_attention_02_amd as kda
+
+    rng = np.random.Generator(np.random.PCG64([7001, i]))
+    N = int(rng.integers(2, 16))  # N * H < 256: the automatic plan splits
+    total = int(rng.integers(33000, 60001))
+    lens = np.floor(rng.dirichlet(np.full(N, 0.6)) * total).astype(int).tolist()
+    w = kda_inputs.custom(seqlens=lens, H=16, lower_bound=-5.0, seed=7100 + i, name=f"mix{i}")
+    say(f"case {w.name}: lengths {lens}")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    planned = kda.plan_seg_chunks(w.T, w.H, w.N, "auto")
+    want = chosen_seg(planned, lens, w.H, varlen=True)
+    out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
+    out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="auto")
+    offs = kda.workspace_offsets(w.T, w.H, w.N, "auto", 0)
+    cnt = read_ws(ws, offs, "counters", 5, np.int32)
+    say(f"{w.name}: planned {planned}, model {want}, used {int(cnt[4])}, early stops {int(cnt[3])}")
+    assert cnt[4] == want and cnt[2] == 0
+    assert torch.equal(out_c.view(torch.int16), out_s.view(torch.int16)) and torch.equal(fin_c, fin_s)
+    short = min((j for j in range(N) if lens[j] > 0), key=lambda j: lens[j])
+    check_against_oracle(w, x, out_c, fin_c, seqs=[short], heads=[3, 12], final_dtype=w.state_dtype)
+
+
 def test_config4_slow_decay_segmented():
     """T=65536 H=16 at lower_bound -0.1: the start state's influence has not
     decayed after a segment's first 4 chunks, so the second pass runs every

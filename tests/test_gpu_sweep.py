@@ -5,8 +5,9 @@ length or varlen (lengths 0, 1-16, whole chunks, or ragged up to 2048), H and a 
 q/k head count, the lower bound, scale, state dtype, layout, presence and
 aliasing, and the plan (serial, forced segments of 1-12 chunks, or the
 library's own).  Every chain of every case is compared with the oracle (the
-token recurrence), with the tolerance of the other parity tests.  The sizes
-keep the oracle to about a second per case."""
+token recurrence), with the tolerance of the other parity tests, and the
+prepared call and the no-allocation entry point must give the same bits as
+fwd.  The sizes keep the oracle to about a second per case."""
 import math
 
 import numpy as np
@@ -103,3 +104,23 @@ def test_random_case_matches_oracle(i):
     if final is not None:
         fin_vk = final.transpose(-1, -2).contiguous() if kv else final
     check_against_oracle(w, xg, out, fin_vk, init=c["init"], final_dtype=c["sdt"])
+    if c["alias"]:
+        return  # a repeated call would start from the state the first one wrote
+    # the prepared call and the no-allocation entry point give the same bits
+    args = dict(A_log=d["A_log"], dt_bias=d["dt_bias"], lower_bound=x["lower_bound"], initial_state=init,
+                cu_seqlens=d["cu_seqlens"], cp_mode=c["cp"], seg_chunks=c["seg"], state_layout=c["layout"])
+    f2 = torch.full_like(final, float("nan")) if final is not None else None
+    prep = kda.prepare(q, k, d["v"], d["g"], d["beta"], x["scale"], final_state=f2, **args)
+    out2 = prep()
+    f3 = torch.full_like(final, float("nan")) if final is not None else None
+    out3 = torch.full_like(out, float("nan"))
+    if kda.get_workspace_size(w.B * w.T, H, w.N, c["cp"], c["seg"]) <= kda.NOALLOC_SCRATCH_BYTES:
+        kda.fwd_noalloc(q, k, d["v"], d["g"], d["beta"], x["scale"], out3, final_state=f3, **args)
+    else:
+        out3, f3 = out2, f2
+    torch.cuda.synchronize()
+    for o, f in ((out2, f2), (out3, f3)):
+        assert torch.equal(o.view(torch.int16), out.view(torch.int16))
+        if final is not None:
+            assert torch.equal(f.view(torch.int16) if f.dtype == torch.bfloat16 else f,
+                               final.view(torch.int16) if final.dtype == torch.bfloat16 else final)
