@@ -76,7 +76,8 @@ typedef enum { KDA_CP_AUTO = 0, KDA_CP_OFF = 1, KDA_CP_FORCE = 2 } kda_cp_mode;
  * sized for: once the sequence lengths are known (on the device, for a varlen
  * call; kda_fixed_seg_chunks, for a fixed-length one) the call may take a
  * longer one, by at most a quarter and 63 chunks, where a model of how the
- * hardware places the (segment, head) workgroups predicts a shorter run.  It
+ * hardware places the (segment, head) workgroups predicts a shorter run (a
+ * varlen call may also dispatch its shorter segments longest first).  It
  * does so for at most 16 sequences, H a multiple of 8 and N*H <= 256, and, in
  * a varlen call, where the planned length is at least 128 chunks.  The
  * length in use is in the counters and in every unit_tab row of the
@@ -90,6 +91,16 @@ int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num
  * num_heads, B, cp_mode, seg_chunks), possibly lengthened as described there.
  * Pure host arithmetic.  Returns a negative kda_status on invalid arguments. */
 int32_t kda_fixed_seg_chunks(int32_t B, int64_t T, int32_t num_heads, int32_t cp_mode, int32_t seg_chunks);
+
+/* The segment plan a varlen kda_fwd call (cu_seqlens, B = 1) takes for these
+ * sequence lengths, as its index kernel chooses it on the device:
+ * *seg_out = the segment length (0: serial), *order_out = 1 where the shorter
+ * segments are dispatched longest first (the workspace counters' order), else
+ * 0.  seq_lens: host int32[num_seqs], each >= 0; the other arguments as for
+ * kda_plan_seg_chunks.  Pure host arithmetic.  Returns KDA_OK or a negative
+ * kda_status on invalid arguments. */
+int32_t kda_varlen_seg_choice(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t cp_mode,
+                              int32_t seg_chunks, int32_t* seg_out, int32_t* order_out);
 
 /* Workspace bytes kda_fwd needs for these sizes and this plan (the pages'
  * get_workspace_size(B*T, H), plus the sequence count and segment plan, since
@@ -172,12 +183,13 @@ int32_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const void*
  * the counters, see kda_write_fixed_tables).  offs must hold KDA_WS_NUM_OFFSETS entries, filled in the
  * order of kda_ws_offset.  Returns KDA_OK or a negative kda_status. */
 typedef enum {
-  KDA_WS_COUNTERS = 0,      /* int32[5]: n_chunks, n_segs, flags, early_stops, seg_chunks; flags bits
-                               0x1..0x8 name repaired cu_seqlens faults (first != 0, decreasing,
-                               last != total, out of range), 0x100 / 0x200 a chunk-kernel wait that
-                               gave up; early_stops counts the (segment, head) pairs whose second
-                               pass matched the checkpoint and stopped there; seg_chunks is the
-                               segment length the call used (0: serial) */
+  KDA_WS_COUNTERS = 0,      /* int32[6]: n_chunks, n_segs, flags, early_stops, seg_chunks, order;
+                               flags bits 0x1..0x8 name repaired cu_seqlens faults (first != 0,
+                               decreasing, last != total, out of range), 0x100 / 0x200 a
+                               chunk-kernel wait that gave up; early_stops counts the (segment,
+                               head) pairs whose second pass matched the checkpoint and stopped
+                               there; seg_chunks is the segment length the call used (0: serial);
+                               order is 1 where unit_tab has the shorter segments longest first */
   KDA_WS_SEQ_START,         /* int32[N+1]   clamped sequence boundaries (last = end of the last sequence) */
   KDA_WS_SEQ_LEN,           /* int32[N]     clamped length */
   KDA_WS_SEQ_CHUNK_OFF,     /* int32[N+1]   prefix sums of ceil(len/16) */
@@ -199,9 +211,11 @@ typedef enum {
   KDA_WS_UNIT_TAB,          /* int32[max_segs][8] the segments in dispatch order: (segment, sequence,
                                chunk begin, chunk end, segment in sequence, sequence start token,
                                sequence length, segment length in use (0: serial)); every
-                               full-length segment first, then the
-                               shorter last segments, each group in segment order (all -1 past the
-                               live count) */
+                               full-length segment first, in segment order, then the shorter ones
+                               (a sequence's last segment, or a sequence shorter than a segment)
+                               in segment order or, where the call chose it (counters' order), by
+                               first-pass chunks, longest first, ties in segment order (all -1
+                               past the live count) */
   KDA_WS_SEG_FIX,           /* fp32 [max_segs][H][128][128] state after a segment's first 4 chunks as the
                                first pass's block of the previous segment reached it, stored only when
                                that block could not compare it with the checkpoint (CP only) */

@@ -34,6 +34,7 @@ __all__ = [
     "get_workspace_size",
     "plan_seg_chunks",
     "fixed_seg_chunks",
+    "varlen_seg_choice",
     "workspace_offsets",
     "library_path",
     "load_library",
@@ -88,6 +89,9 @@ def load_library():
     lib.kda_plan_seg_chunks.restype = i32
     lib.kda_fixed_seg_chunks.argtypes = [i32, i64, i32, i32, i32]
     lib.kda_fixed_seg_chunks.restype = i32
+    lib.kda_varlen_seg_choice.argtypes = [ctypes.POINTER(i32), i32, i32, i32, i32, ctypes.POINTER(i32),
+                                          ctypes.POINTER(i32)]
+    lib.kda_varlen_seg_choice.restype = i32
     lib.kda_get_workspace_size.argtypes = [i64, i32, i32, i32, i32]
     lib.kda_get_workspace_size.restype = sz
     lib.kda_workspace_offsets.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
@@ -150,6 +154,19 @@ def fixed_seg_chunks(B: int, T: int, num_heads: int, cp_mode="auto", seg_chunks:
     if r < 0:
         _raise(r)
     return r
+
+
+def varlen_seg_choice(seq_lens, num_heads: int, cp_mode="auto", seg_chunks: int = 0):
+    """(segment length, longest first) a varlen call with these sequence
+    lengths takes; (0, False) = serial."""
+    lens = [int(x) for x in seq_lens]
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    seg, order = ctypes.c_int32(), ctypes.c_int32()
+    r = load_library().kda_varlen_seg_choice(arr, len(lens), int(num_heads), _cp(cp_mode), int(seg_chunks),
+                                             ctypes.byref(seg), ctypes.byref(order))
+    if r < 0:
+        _raise(r)
+    return seg.value, bool(order.value)
 
 
 def get_workspace_size(total_tokens: int, num_heads: int, num_seqs: int = 1, cp_mode="auto",

@@ -162,11 +162,11 @@ int32_t fixed_seg(int32_t seg, int32_t N, int64_t T, int32_t H, bool choose) {
   if (m.seg == seg && m.N == N && m.H == H && m.T == T) return m.out;
   int nc[kda::kSpanMaxSeqs];
   for (int32_t i = 0; i < N; ++i) nc[i] = (int)((T + kda::C - 1) / kda::C);
-  int cu[32];
+  int cu[32 + kda::kSpanMaxSeqs];
   int best = INT32_MAX;
   int32_t out = seg;
   for (int c = 0; c < kda::span_candidates(seg); ++c) {
-    const int span = kda::seg_span<1>(seg + c, N, nc, H, kCheckChunks, cu);
+    const int span = kda::seg_span<1>(seg + c, N, nc, H, kCheckChunks, false, cu);  // equal lengths: one order
     if (span < best) {
       best = span;
       out = seg + c;
@@ -193,7 +193,7 @@ int32_t layout(int64_t total, int32_t H, int32_t N, int32_t cp_mode, int32_t seg
     out->off[idx] = o;
     o = align_up(o + bytes, A);
   };
-  take(KDA_WS_COUNTERS, 4 * 5);
+  take(KDA_WS_COUNTERS, 4 * 6);
   take(KDA_WS_SEQ_START, 4 * ((int64_t)N + 1));
   take(KDA_WS_SEQ_LEN, 4 * (int64_t)N);
   take(KDA_WS_SEQ_CHUNK_OFF, 4 * ((int64_t)N + 1));
@@ -459,6 +459,40 @@ int32_t kda_fixed_seg_chunks(int32_t B, int64_t T, int32_t num_heads, int32_t cp
   const int32_t seg = plan((int64_t)B * T, num_heads, B, cp_mode, seg_chunks);
   if (seg < 0) return seg;
   return fixed_seg(seg, B, T, num_heads, seg_chunks == 0);
+}
+
+int32_t kda_varlen_seg_choice(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t cp_mode,
+                              int32_t seg_chunks, int32_t* seg_out, int32_t* order_out) {
+  g_last_error.clear();
+  if (!seq_lens || !seg_out || !order_out)
+    return fail(KDA_ERR_INVALID_ARG, "seq_lens, seg_out and order_out must be non-NULL");
+  if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs %d must be >= 1", num_seqs);
+  int64_t total = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (seq_lens[i] < 0) return fail(KDA_ERR_INVALID_ARG, "seq_lens[%d] = %d is negative", i, seq_lens[i]);
+    total += seq_lens[i];
+  }
+  const int32_t seg = plan(total, num_heads, num_seqs, cp_mode, seg_chunks);
+  if (seg < 0) return seg;
+  *seg_out = seg;
+  *order_out = 0;
+  // the index kernel's choice (kda_index.hip), replayed on the host
+  if (seg_chunks != 0 || seg < kda::kSpanDeviceMinSeg || !kda::span_model_applies(seg, num_seqs, num_heads))
+    return KDA_OK;
+  int nc[kda::kSpanMaxSeqs];
+  for (int32_t i = 0; i < num_seqs; ++i) nc[i] = (seq_lens[i] + kda::C - 1) / kda::C;
+  int cu[32 + kda::kSpanMaxSeqs];
+  unsigned long long best = ~0ull;
+  for (int d = 0; d < 2; ++d)
+    for (int c = 0; c < kda::span_candidates(seg); ++c) {
+      const int span = kda::seg_span<1>(seg + c, num_seqs, nc, num_heads, kCheckChunks, d == 1, cu);
+      const unsigned long long key =
+          ((unsigned long long)(unsigned)span << 32) | ((unsigned)(seg + c) << 1) | (unsigned)d;
+      best = key < best ? key : best;
+    }
+  *seg_out = (int32_t)((best & 0xFFFFFFFFu) >> 1);
+  *order_out = (int32_t)(best & 1u);
+  return KDA_OK;
 }
 
 size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t num_seqs, int32_t cp_mode,

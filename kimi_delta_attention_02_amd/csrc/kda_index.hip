@@ -27,8 +27,8 @@
 //       sums gives chunk_tab[c] = (seq, chunk in seq) and
 //       seg_tab[s] = (seq, first chunk, end chunk, segment in seq), and puts
 //       segment s into the dispatch table unit_tab (full-length segments
-//       first, then the shorter last segments of their sequences, so that the
-//       long units start first).  Rows past the live counts are -1.
+//       first, then the shorter ones, so that the long units start first).
+//       Rows past the live counts are -1.
 // A unit_tab row is (segment, seq, first chunk, end chunk, segment in seq,
 // sequence start token, sequence length, segment length): everything the
 // chunk kernel needs to place its unit, in one 32-byte row, so that its first
@@ -36,11 +36,13 @@
 //
 // Where the library chooses the plan (seg_chunks 0) and plans segments of at
 // least kSpanDeviceMinSeg chunks, step 1 may lengthen the planned segment
-// length once the sequence lengths are known: wavefront 0 scores up to 64
-// lengths from the planned one up, one per lane, with the placement model
-// seg_span (kda_internal.h), and the best one is used for every table and
-// recorded in the counters and in every unit_tab row.  The planned length
-// sizes the workspace; a longer one needs fewer rows.
+// length once the sequence lengths are known: wavefronts 0 and 1 score up to
+// 64 lengths from the planned one up, one per lane, with the placement model
+// seg_span (kda_internal.h), wavefront 0 with the shorter segments in segment
+// order and wavefront 1 with them longest first.  The best length and order
+// are used for every table; the length is recorded in the counters and in
+// every unit_tab row, the order in the counters.  The planned length sizes the
+// workspace; a longer one needs fewer rows.
 #include "kda_internal.h"
 
 namespace kda {
@@ -92,12 +94,14 @@ struct AddOp {
 // (step 1 of the header).  When sst/coff/soff are given (LDS, N + 1 entries
 // each), the boundaries and the chunk and segment prefix sums are also kept
 // there, and the lengths are computed from the LDS copy.
-// Returns the segment length the tables use.  With choose set, span_cu (LDS,
-// 32 x 64 + kSpanMaxSeqs ints) and seg_sel (LDS) serve the choice of the
-// segment length.
+// Returns the segment length the tables use and sets desc to their order of
+// the shorter segments (1: longest first).  With choose set, span_cu (LDS,
+// 2 x (32 + kSpanMaxSeqs) x 64 + kSpanMaxSeqs ints) and span_key (LDS, 2
+// entries) serve the choice.
 __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long T_row, long long total,
                                int seg_chunks, int H, int K, bool choose, Tables t, long long* smem, int* flags,
-                               int* sst, int* coff, int* soff, int* foff, int* span_cu, int* seg_sel) {
+                               int* sst, int* coff, int* soff, int* foff, int* span_cu,
+                               unsigned long long* span_key, int& desc) {
   if (threadIdx.x == 0) *flags = 0;
   __syncthreads();
   // pass 1: boundaries b_i, i = 0..N (clamped running maximum of the offsets)
@@ -130,31 +134,39 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
   }
   __threadfence_block();
   __syncthreads();
-  // the segment length: lane s of wavefront 0 scores length seg_chunks + s
+  // the segment length and order: lane s of wavefront w scores length
+  // seg_chunks + s with the shorter segments in segment order (w = 0) or
+  // longest first (w = 1); the least (span, length, order) wins
+  desc = 0;
   if (choose && seg_chunks >= kSpanDeviceMinSeg && span_model_applies(seg_chunks, N, H)) {
-    int* nc = span_cu + 32 * 64;  // chunks of each sequence
+    constexpr int kWaveInts = (32 + kSpanMaxSeqs) * 64;  // one wavefront's cu arrays, lane-interleaved
+    int* nc = span_cu + 2 * kWaveInts;                     // chunks of each sequence
     if (threadIdx.x < N) {
       const int32_t* bnd = sst ? sst : t.seq_start;
       nc[threadIdx.x] = (bnd[threadIdx.x + 1] - bnd[threadIdx.x] + C - 1) / C;
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-      const int lane = (int)threadIdx.x;
+    if (threadIdx.x < 128) {
+      const int lane = (int)threadIdx.x & 63;
+      const int w = (int)threadIdx.x >> 6;
       unsigned long long key = ~0ull;
       if (lane < span_candidates(seg_chunks)) {
         const int len = seg_chunks + lane;
-        const int span = seg_span<64>(len, N, nc, H, K, span_cu + lane);
-        key = ((unsigned long long)(unsigned)span << 32) | (unsigned)len;
+        const int span = seg_span<64>(len, N, nc, H, K, w == 1, span_cu + w * kWaveInts + lane);
+        key = ((unsigned long long)(unsigned)span << 32) | ((unsigned)len << 1) | (unsigned)w;
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
         const unsigned long long y = __shfl_xor(key, o, 64);
         key = y < key ? y : key;
       }
-      if (lane == 0) *seg_sel = (int)(key & 0xFFFFFFFFu);
+      if (lane == 0) span_key[w] = key;
     }
     __syncthreads();
-    seg_chunks = *seg_sel;
+    const unsigned long long k0 = span_key[0], k1 = span_key[1];
+    const unsigned long long key = k0 < k1 ? k0 : k1;
+    seg_chunks = (int)((key & 0xFFFFFFFFu) >> 1);
+    desc = (int)(key & 1u);
   }
   // pass 2: lengths, chunk and segment counts, exclusive prefix sums
   long long c_carry = 0, s_carry = 0, f_carry = 0;
@@ -199,6 +211,7 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
     t.counters[CNT_FLAGS] = *flags;
     t.counters[CNT_EARLY_STOPS] = 0;
     t.counters[CNT_SEG_CHUNKS] = seg_chunks;
+    t.counters[CNT_ORDER] = desc;
   }
   return seg_chunks;
 }
@@ -207,10 +220,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __
                                                                long long total, int seg_chunks, int H, int K,
                                                                int choose, Tables t) {
   __shared__ long long smem[SCAN_WAVES];
-  __shared__ int flags, seg_sel;
-  __shared__ int span_cu[32 * 64 + kSpanMaxSeqs];
+  __shared__ int flags;
+  __shared__ int span_cu[2 * (32 + kSpanMaxSeqs) * 64 + kSpanMaxSeqs];
+  __shared__ unsigned long long span_key[2];
+  int desc;
   index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, t, smem, &flags, nullptr, nullptr, nullptr,
-                  nullptr, span_cu, &seg_sel);
+                  nullptr, span_cu, span_key, desc);
 }
 
 // largest j in [0, n) with off[j] <= x, given off[0] = 0 <= x and off non-decreasing
@@ -250,12 +265,24 @@ __device__ __forceinline__ void seg_row(int32_t* row, int sq, int idx, const int
 
 // Puts segment idx (seg_tab row `row`) into the dispatch table at its rank:
 // the full-length segments in segment order, then the others (a sequence's
-// shorter last segment) in segment order.
-__device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32_t* row, const int* soff,
-                                         const int* foff, int n_full, int seq_start, int seq_len, int seg) {
+// shorter last segment, or a sequence shorter than seg) in segment order or,
+// with desc, longest first by rest_cost (ties in segment order; desc is only
+// chosen for at most kSpanMaxSeqs sequences, so the count below is short).
+__device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32_t* row, const int* coff,
+                                         const int* soff, const int* foff, int N, int n_full, int seq_start,
+                                         int seq_len, int seg, int K, int desc) {
   const int sq = row[0], j = row[3];
   const int full_here = foff[sq + 1] - foff[sq];
-  const int rank = j < full_here ? foff[sq] + j : n_full + (soff[sq] - foff[sq]);
+  int rest_rank = soff[sq] - foff[sq];  // shorter segments of the sequences before this one
+  if (desc && j >= full_here) {
+    const int mine = rest_cost(coff[sq + 1] - coff[sq], seg, K);
+    rest_rank = 0;
+    for (int i = 0; i < N; ++i) {
+      const int c = rest_cost(coff[i + 1] - coff[i], seg, K);
+      rest_rank += c > mine || (c == mine && i < sq);  // c = -1 (no shorter segment) never counts
+    }
+  }
+  const int rank = j < full_here ? foff[sq] + j : n_full + rest_rank;
   int32_t* u = unit_tab + 8 * rank;
   u[0] = idx;
   u[1] = row[0];
@@ -267,11 +294,13 @@ __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32
   u[7] = seg;
 }
 
-__global__ __launch_bounds__(256) void kda_index_fill(int N, long long max_chunks, long long max_segs, Tables t) {
+__global__ __launch_bounds__(256) void kda_index_fill(int N, int K, long long max_chunks, long long max_segs,
+                                                      Tables t) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int n_chunks = t.counters[CNT_N_CHUNKS];
   const int n_segs = t.counters[CNT_N_SEGS];
-  const int seg_chunks = t.counters[CNT_SEG_CHUNKS];  // the length kda_index_scan chose
+  const int seg_chunks = t.counters[CNT_SEG_CHUNKS];  // the length and order kda_index_scan chose
+  const int desc = t.counters[CNT_ORDER];
   if (idx < max_chunks) {
     int a = -1, b = -1;
     if (idx < n_chunks) {
@@ -290,8 +319,8 @@ __global__ __launch_bounds__(256) void kda_index_fill(int N, long long max_chunk
       int s = owner_of(t.seq_seg_off, N + 1, (int)idx);
       while (s + 1 <= N && t.seq_seg_off[s + 1] <= (int)idx) ++s;
       seg_row(row, s, (int)idx, t.seq_chunk_off, t.seq_seg_off, seg_chunks);
-      put_unit(t.unit_tab, (int)idx, row, t.seq_seg_off, t.seq_full_off, t.seq_full_off[N], t.seq_start[s],
-               t.seq_len[s], seg_chunks);
+      put_unit(t.unit_tab, (int)idx, row, t.seq_chunk_off, t.seq_seg_off, t.seq_full_off, N, t.seq_full_off[N],
+               t.seq_start[s], t.seq_len[s], seg_chunks, K, desc);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) t.unit_tab[8 * idx + k] = -1;
@@ -308,11 +337,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* _
                                                                 long long total, int seg_chunks, int H, int K,
                                                                 int choose, int max_chunks, int max_segs, Tables t) {
   __shared__ long long smem[SCAN_WAVES];
-  __shared__ int flags, seg_sel;
+  __shared__ int flags;
   __shared__ int sst[FUSED_MAX_N + 1], coff[FUSED_MAX_N + 1], soff[FUSED_MAX_N + 1], foff[FUSED_MAX_N + 1];
-  __shared__ int span_cu[32 * 64 + kSpanMaxSeqs];
+  __shared__ int span_cu[2 * (32 + kSpanMaxSeqs) * 64 + kSpanMaxSeqs];
+  __shared__ unsigned long long span_key[2];
+  int desc;
   seg_chunks = index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, t, smem, &flags, sst, coff, soff,
-                               foff, span_cu, &seg_sel);
+                               foff, span_cu, span_key, desc);
   __syncthreads();
   const int n_chunks = coff[N], n_segs = soff[N];
   {
@@ -341,7 +372,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* _
       if (r < n_segs) {
         while (a + 1 <= N && soff[a + 1] <= r) ++a;
         seg_row(row, a, r, coff, soff, seg_chunks);
-        put_unit(t.unit_tab, r, row, soff, foff, foff[N], sst[a], sst[a + 1] - sst[a], seg_chunks);
+        put_unit(t.unit_tab, r, row, coff, soff, foff, N, foff[N], sst[a], sst[a + 1] - sst[a], seg_chunks, K, desc);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) t.unit_tab[8 * r + k] = -1;
@@ -391,7 +422,7 @@ hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t
   if (rows > 0) {
     const unsigned blocks = (unsigned)((rows + 255) / 256);
     stage_events(KDA_STAGE_INDEX, &e0, &e1);
-    hipExtLaunchKernelGGL(kda_index_fill, dim3(blocks), dim3(256), 0, st, e0, e1, 0, N, (long long)max_chunks,
+    hipExtLaunchKernelGGL(kda_index_fill, dim3(blocks), dim3(256), 0, st, e0, e1, 0, N, K, (long long)max_chunks,
                           (long long)max_segs, t);
     e = hipGetLastError();
   }

@@ -28,6 +28,7 @@ constexpr int CNT_N_SEGS = 1;
 constexpr int CNT_FLAGS = 2;
 constexpr int CNT_EARLY_STOPS = 3;  // (segment, head) pairs whose second pass stopped at the checkpoint
 constexpr int CNT_SEG_CHUNKS = 4;   // segment length in use (0: serial)
+constexpr int CNT_ORDER = 5;        // order of the shorter segments in unit_tab: 0 segment order, 1 longest first
 
 // Pointers into a carved workspace (device addresses).
 struct Tables {
@@ -259,6 +260,7 @@ __device__ __forceinline__ void fixed_counters(int N, int L, int seg, const Tabl
   t.counters[CNT_FLAGS] = 0;
   t.counters[CNT_EARLY_STOPS] = 0;
   t.counters[CNT_SEG_CHUNKS] = seg;
+  t.counters[CNT_ORDER] = 0;
 }
 
 // Every table row of a fixed-length call, rows tid, tid + nthr, ... (the same
@@ -314,18 +316,20 @@ __device__ __forceinline__ void fixed_tables(int tid, int nthr, int N, int L, in
 // seg_span replays that placement for one XCD (H a multiple of 8, so that
 // every XCD gets the same share) and returns the first pass's predicted span
 // in chunk steps: a unit costs the chunks it runs plus a fixed start cost.
-// The units come in dispatch-table order: every full-length segment, then
-// the other ones, each group in segment order.  A full segment runs K chunks
-// into the next one when that one is longer than K; a later segment of K
-// chunks or fewer ends at once; a sequence shorter than s is one unit.
-// Sequence i has nc[i] chunks; cu holds 32 ints at stride STRIDE (the CUs of
-// one XCD, engine-major).
+// The units come in dispatch-table order: every full-length segment in
+// segment order, then the shorter ones (a sequence's last segment, or a
+// sequence shorter than s), in segment order or, with desc, longest first.
+// A full segment runs K chunks into the next one when that one is longer
+// than K; a later segment of K chunks or fewer ends at once.  Sequence i has
+// nc[i] chunks; cu holds 32 + kSpanMaxSeqs ints at stride STRIDE (the CUs of
+// one XCD, engine-major, then the costs of the shorter segments).
 constexpr int kSpanStartCost = 4;    // a unit's fixed start cost, in chunk steps (measured 2 to 7)
 constexpr int kSpanCandidates = 64;  // lengths tried: seg .. seg + min(seg / 4, 63)
-constexpr int kSpanMaxSeqs = 16;
-// The index kernel spends a few microseconds on the choice (one wavefront
-// replays up to 64 placements per candidate); it makes it only for a planned
-// length of at least this many chunks, whose first pass takes ~180 us or more.
+constexpr int kSpanMaxSeqs = 16;  // a power of two (the sorting network)
+// The index kernel spends a few microseconds on the choice (a wavefront per
+// order replays up to 64 placements per candidate); it makes it only for a
+// planned length of at least this many chunks, whose first pass takes ~180 us
+// or more.
 constexpr int kSpanDeviceMinSeg = 128;
 
 __host__ __device__ inline bool span_model_applies(int seg, int N, int H) {
@@ -337,48 +341,133 @@ __host__ __device__ inline int span_candidates(int seg) {
   return 1 + (q < kSpanCandidates - 1 ? q : kSpanCandidates - 1);
 }
 
+// q = n / s and r = n - q s for 0 <= n < 2^27 and s >= 1, exactly.  On the
+// device, for s >= 128 (every length the model scores there), from a float
+// estimate, off by at most one in that range, then corrected: the quarter-rate
+// steps of a plain integer division weigh on the model's cost.  Elsewhere by
+// plain division.
+__host__ __device__ inline int span_div(int n, int s, int& r) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (s < 128) {
+    const int q = n / s;
+    r = n - q * s;
+    return q;
+  }
+  int q = (int)((float)n * __builtin_amdgcn_rcpf((float)s));
+  r = n - q * s;
+  if (r < 0) {
+    q -= 1;
+    r += s;
+  }
+  if (r >= s) {
+    q += 1;
+    r -= s;
+  }
+  return q;
+#else
+  const int q = n / s;
+  r = n - q * s;
+  return q;
+#endif
+}
+
+// The first-pass cost, in chunks, of the shorter segment of a sequence split
+// into f full segments of s chunks and rem more, or -1 when it has none: a
+// sequence shorter than s is one unit of rem chunks (0 for an empty one); a
+// later last segment of rem chunks runs them unless rem <= K.
+__host__ __device__ inline int rest_cost_of(int f, int rem, int K) {
+  if (f == 0) return rem;
+  if (rem == 0) return -1;
+  return rem > K ? rem : 0;
+}
+
+__host__ __device__ inline int rest_cost(int n, int s, int K) {
+  int rem;
+  const int f = span_div(n, s, rem);
+  return rest_cost_of(f, rem, K);
+}
+
 template <int STRIDE>
-__host__ __device__ inline int seg_span(int s, int N, const int* nc, int H, int K, int* cu) {
+__host__ __device__ inline int seg_span(int s, int N, const int* nc, int H, int K, bool desc, int* cu) {
   for (int k = 0; k < 32; ++k) cu[k * STRIDE] = 0;
   const int per = H / 8;  // workgroups of a unit's row per XCD
-  int last = 0, span = 0, blk = 0;
-  auto place = [&](int cost) {
-    for (int m = 0; m < per; ++m, ++blk) {
-      int* e = cu + (blk & 3) * 8 * STRIDE;  // its shader engine's 8 CUs
-      if (blk < 32) {  // the first 32 fill the empty CUs: engine blk % 4, its CU blk / 4, at once
-        e[(blk >> 2) * STRIDE] = cost + kSpanStartCost;
-        span = cost + kSpanStartCost > span ? cost + kSpanStartCost : span;
-        continue;
-      }
-      int best = e[0], bk = 0;
-      for (int c = 1; c < 8; ++c) {
-        const int v = e[c * STRIDE];
-        if (v < best) {
-          best = v;
-          bk = c;
-        }
-      }
-      const int st = best > last ? best : last;  // in order: never before the previous one
-      last = st;
-      const int fin = st + cost + kSpanStartCost;
-      e[bk * STRIDE] = fin;
-      span = fin > span ? fin : span;
+  int last = 0, span = 0, blk = 0, row = 0;
+  // the k-th workgroup an engine receives (its CUs at e): the first 8 fill its
+  // empty CUs at once, the later ones wait for the earliest free CU and start
+  // no earlier than the workgroup dispatched before them
+  auto on_engine = [&](int* e, int k, int cost) {
+    if (k < 8) {
+      e[k * STRIDE] = cost + kSpanStartCost;
+      span = cost + kSpanStartCost > span ? cost + kSpanStartCost : span;
+      return;
     }
+    int best = e[0], bk = 0;
+    for (int c = 1; c < 8; ++c) {
+      const int v = e[c * STRIDE];
+      if (v < best) {
+        best = v;
+        bk = c;
+      }
+    }
+    const int st = best > last ? best : last;
+    last = st;
+    const int fin = st + cost + kSpanStartCost;
+    e[bk * STRIDE] = fin;
+    span = fin > span ? fin : span;
   };
+  // A row's workgroups go to engines blk % 4, blk + 1, ...  Engines that
+  // always receive the same work are replayed once: with 2 per row (H = 16)
+  // even rows reach engines 0 and 1 and odd rows 2 and 3, so one engine stands
+  // for each pair; with a multiple of 4 (H = 32, 64, ...) every row reaches all
+  // four alike, per / 4 workgroups each.  Otherwise each workgroup is placed.
+  auto place = [&](int cost) {
+    if (per == 2) {
+      on_engine(cu + (row & 1) * 8 * STRIDE, row >> 1, cost);
+    } else if ((per & 3) == 0) {
+      for (int m = 0; m < per / 4; ++m) on_engine(cu, row * (per / 4) + m, cost);
+    } else {
+      for (int m = 0; m < per; ++m, ++blk) on_engine(cu + (blk & 3) * 8 * STRIDE, blk >> 2, cost);
+    }
+    ++row;
+  };
+  int rc[kSpanMaxSeqs];  // each sequence's shorter segment (-1: none)
+#pragma unroll
+  for (int i = 0; i < kSpanMaxSeqs; ++i) rc[i] = -1;
   for (int i = 0; i < N; ++i) {
-    const int n = nc[i], f = n / s, rem = n - f * s;
+    int rem;
+    const int f = span_div(nc[i], s, rem);
     for (int j = 0; j < f; ++j) {
       const int nn = j + 1 < f ? s : rem;  // the next segment's chunks
       place(s + (nn > K ? K : 0));
     }
+    const int c = rest_cost_of(f, rem, K);
+#pragma unroll
+    for (int q = 0; q < kSpanMaxSeqs; ++q) rc[q] = q == i ? c : rc[q];  // static indices: registers
   }
-  for (int i = 0; i < N; ++i) {
-    const int n = nc[i], f = n / s, rem = n - f * s;
-    if (f == 0)
-      place(n);
-    else if (rem > 0)
-      place(rem > K ? rem : 0);
+  if (desc) {
+    // longest first: rc sorted in descending order by a bitonic network (the
+    // placement depends on the costs alone, so ties may change places)
+#pragma unroll
+    for (int k = 2; k <= kSpanMaxSeqs; k <<= 1)
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+        for (int i = 0; i < kSpanMaxSeqs; ++i) {
+          const int l = i ^ j;
+          if (l > i) {
+            const int a = rc[i], b = rc[l];
+            const bool sw = (i & k) == 0 ? a < b : a > b;
+            rc[i] = sw ? b : a;
+            rc[l] = sw ? a : b;
+          }
+        }
   }
+  // placed from cu's second part in a rolled loop (one copy of the placement code)
+  int n_rest = 0;
+#pragma unroll
+  for (int i = 0; i < kSpanMaxSeqs; ++i)
+    if (rc[i] >= 0) cu[(32 + n_rest++) * STRIDE] = rc[i];
+  for (int i = 0; i < n_rest; ++i) place(cu[(32 + i) * STRIDE]);
   return span;
 }
 

@@ -107,6 +107,39 @@ def test_fixed_seg_chunks_follows_placement_model():
         kda.fixed_seg_chunks(1, 100, 0)
 
 
+def test_varlen_seg_choice_follows_placement_model():
+    """The library's varlen choice (replayed on the host by
+    kda_varlen_seg_choice, the index kernel's arithmetic) against the literal
+    placement model of tests/span_model.py, which places every workgroup on
+    every XCD: seeded random mixes at H = 8, 16, 24, 32, 64 (each with its own
+    form of the replay), both orders of the shorter segments, empty and tiny
+    sequences included."""
+    import numpy as np
+
+    from tests.span_model import chosen_plan
+
+    rng = np.random.Generator(np.random.PCG64(4242))
+    n_long = 0
+    for t in range(160):
+        H = int(rng.choice([8, 16, 24, 32, 64]))
+        N = int(rng.integers(1, min(16, 255 // H) + 1))
+        total = int(rng.integers(10000, 400000))
+        lens = np.floor(rng.dirichlet(np.full(N, float(rng.choice([0.3, 1.0, 3.0])))) * total).astype(int).tolist()
+        if rng.random() < 0.2:
+            lens[int(rng.integers(0, N))] = int(rng.choice([0, 1, 15, 16, 17]))
+        planned = kda.plan_seg_chunks(sum(lens), H, N, "auto")
+        got = kda.varlen_seg_choice(lens, H)
+        want = chosen_plan(planned, lens, H, varlen=True) if planned else (0, False)
+        assert got == want, (H, lens, planned, got, want)
+        n_long += got[1]
+    assert n_long > 10  # both orders were chosen
+    # explicit lengths and serial plans are kept; bad arguments raise
+    assert kda.varlen_seg_choice([65536, 1024], 16, "auto", 300) == (300, False)
+    assert kda.varlen_seg_choice([65536, 1024], 16, "off") == (0, False)
+    with pytest.raises(kda.KdaError):
+        kda.varlen_seg_choice([100, -1], 16)
+
+
 def test_workspace_layout_consistent():
     for args in [(256, 2, 1, "off", 0), (8192, 16, 2, "auto", 0), (79890, 16, 7, "force", 64), (0, 4, 3, "auto", 0)]:
         size = kda.get_workspace_size(*args)

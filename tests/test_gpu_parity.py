@@ -251,9 +251,11 @@ def _zero_inputs(w):
     # (varlen: chosen on the device, one and two-launch forms; fixed length: on the host)
     ([65536] + [1024] * 5, 0, False, 16, "auto"), ([1023, 1025, 1, 16, 4097, 8191, 65537], 0, False, 16, "auto"),
     ([300000, 5000, 70], 0, False, 16, "auto"), ([8192] * 3, 0, True, 16, "auto"), ([65536], 0, False, 16, "auto"),
-    ([24000, 3000, 1000], 0, False, 16, "auto")])
+    ([24000, 3000, 1000], 0, False, 16, "auto"),
+    # the two-launch form with the shorter segments longest first
+    ([41621, 4127, 111604, 20239, 3299, 75763, 1774, 16070], 0, False, 16, "auto")])
 def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
-    from tests.span_model import chosen_seg
+    from tests.span_model import chosen_plan, rest_cost
 
     if fixed:
         w = kda_inputs.custom(B=len(lens), T=lens[0], H=H, seed=28, name="tables fixed", init_std=None)
@@ -270,17 +272,17 @@ def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
 
     offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, mode, seg)
     planned = kda.plan_seg_chunks(w.B * w.T, w.H, w.N, mode, seg)
-    used = chosen_seg(planned, lens, H, varlen=not fixed) if seg == 0 else planned
+    used, desc = chosen_plan(planned, lens, H, varlen=not fixed) if seg == 0 else (planned, False)
     if mode == "auto":
         assert used > 0
         if fixed:
             assert kda.fixed_seg_chunks(w.B, w.T, w.H, mode, seg) == used
-    say(f"tables {len(lens)} sequences H={H} {mode}: planned {planned}, used {used}")
+    say(f"tables {len(lens)} sequences H={H} {mode}: planned {planned}, used {used}, longest first {desc}")
     ref = O.index_tables(lens, 16, used if used else None)
     N = len(lens)
-    cnt = read_ws(ws, offs, "counters", 5, np.int32)
+    cnt = read_ws(ws, offs, "counters", 6, np.int32)
     assert cnt[0] == ref["seq_chunk_off"][-1] and cnt[1] == ref["seq_seg_off"][-1] and cnt[2] == 0
-    assert cnt[4] == used
+    assert cnt[4] == used and cnt[5] == int(desc)
     np.testing.assert_array_equal(read_ws(ws, offs, "seq_chunk_off", N + 1, np.int32), ref["seq_chunk_off"])
     np.testing.assert_array_equal(read_ws(ws, offs, "seq_seg_off", N + 1, np.int32), ref["seq_seg_off"])
     nch, nsg = int(cnt[0]), int(cnt[1])
@@ -291,14 +293,18 @@ def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
     mc, ms = offs["max_chunks"], offs["max_segs"]
     assert (read_ws(ws, offs, "chunk_tab", 2 * mc, np.int32)[2 * nch:] == -1).all()
     assert (read_ws(ws, offs, "seg_tab", 4 * ms, np.int32)[4 * nsg:] == -1).all()
-    # dispatch order: every full-length segment (seg chunks), then the others,
-    # each group in segment order (serial: every sequence counts as full); a
-    # row also carries its sequence's first token and length and the segment
-    # length in use
+    # dispatch order: every full-length segment (seg chunks) in segment order,
+    # then the others in segment order or, where the call chose it, longest
+    # first by first-pass cost (serial: every sequence counts as full); a row
+    # also carries its sequence's first token and length and the segment length
+    # in use
     st = ref["seg_tab"]
     starts = np.concatenate([[0], np.cumsum(lens)])
     full = [i for i in range(nsg) if not used or st[i][2] - st[i][1] == used]
     rest = [i for i in range(nsg) if used and st[i][2] - st[i][1] != used]
+    if desc:
+        nch_of = [(L + 15) // 16 for L in lens]
+        rest = sorted(rest, key=lambda i: (-rest_cost(nch_of[st[i][0]], used), i))
     want = np.array([[i, *st[i], starts[st[i][0]], lens[st[i][0]], used] for i in full + rest],
                     dtype=np.int32).reshape(-1, 8)
     unit = read_ws(ws, offs, "unit_tab", 8 * ms, np.int32).reshape(-1, 8)
@@ -431,7 +437,7 @@ def test_lengthened_segments_bit_identical_to_serial(kind):
     out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
     out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="auto")
     offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, "auto", 0)
-    cnt = read_ws(ws, offs, "counters", 5, np.int32)
+    cnt = read_ws(ws, offs, "counters", 6, np.int32)
     stops = int(cnt[3])
     say(f"{w.name}: planned {planned}, used {int(cnt[4])}, early stops {stops}")
     assert cnt[4] == used
@@ -443,11 +449,12 @@ def test_lengthened_segments_bit_identical_to_serial(kind):
 @pytest.mark.parametrize("i", range(6))
 def test_random_varlen_mix_segment_choice(i):
     """Seeded random varlen mixes at H=16 (2-15 sequences, 33-60K tokens) on
-    the library's own plan, where the index kernel chooses the segment length:
-    the length in use equals the placement model's choice, the result equals
+    the library's own plan, where the index kernel chooses the segment length
+    and the order of the shorter segments: both equal the placement model's
+    choice, the result equals
     the serial call bit for bit (lower bound -5), and sampled chains match the
     oracle."""
-    from tests.span_model import chosen_seg
+    from tests.span_model import chosen_plan
     import kimi_delta_attention_02_amd as kda
 
     rng = np.random.Generator(np.random.PCG64([7001, i]))
@@ -459,13 +466,14 @@ def test_random_varlen_mix_segment_choice(i):
     x = kda_inputs.make_inputs(w)
     d = dev_inputs(x)
     planned = kda.plan_seg_chunks(w.T, w.H, w.N, "auto")
-    want = chosen_seg(planned, lens, w.H, varlen=True)
+    want, desc = chosen_plan(planned, lens, w.H, varlen=True)
     out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
     out_c, fin_c, ws = run_gpu(w, x, d, cp_mode="auto")
     offs = kda.workspace_offsets(w.T, w.H, w.N, "auto", 0)
-    cnt = read_ws(ws, offs, "counters", 5, np.int32)
-    say(f"{w.name}: planned {planned}, model {want}, used {int(cnt[4])}, early stops {int(cnt[3])}")
-    assert cnt[4] == want and cnt[2] == 0
+    cnt = read_ws(ws, offs, "counters", 6, np.int32)
+    say(f"{w.name}: planned {planned}, model {want} (longest first {desc}), used {int(cnt[4])} "
+        f"(longest first {bool(cnt[5])}), early stops {int(cnt[3])}")
+    assert cnt[4] == want and cnt[5] == int(desc) and cnt[2] == 0
     assert torch.equal(out_c.view(torch.int16), out_s.view(torch.int16)) and torch.equal(fin_c, fin_s)
     short = min((j for j in range(N) if lens[j] > 0), key=lambda j: lens[j])
     check_against_oracle(w, x, out_c, fin_c, seqs=[short], heads=[3, 12], final_dtype=w.state_dtype)
