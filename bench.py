@@ -334,7 +334,12 @@ def main() -> int:
     out = torch.empty_like(q)
     total = w.B * w.T
     seg = kda.plan_seg_chunks(total, w.H, w.N, a.cp, a.seg)
-    ws = torch.empty(kda.get_workspace_size(total, w.H, w.N, a.cp, a.seg), dtype=torch.uint8, device=dev)
+    need = kda.get_workspace_size(total, w.H, w.N, a.cp, a.seg)
+    if cu is not None and a.cp == "auto" and a.seg == 0:
+        # as the binding allocates: room for the segmented layout lets a skewed
+        # varlen batch split where the automatic plan would stay serial
+        need = max(need, kda.get_workspace_size(total, w.H, w.N, "force", 0))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def step():
         kda.fwd(q, k, v, g, beta, x["scale"], out, A_log=A_log, dt_bias=dt_bias, lower_bound=x["lower_bound"],

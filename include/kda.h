@@ -93,7 +93,9 @@ int32_t kda_plan_seg_chunks(int64_t total_tokens, int32_t num_heads, int32_t num
 int32_t kda_fixed_seg_chunks(int32_t B, int64_t T, int32_t num_heads, int32_t cp_mode, int32_t seg_chunks);
 
 /* The segment plan a varlen kda_fwd call (cu_seqlens, B = 1) takes for these
- * sequence lengths, as its index kernel chooses it on the device:
+ * sequence lengths, as its index kernel chooses it on the device, with a
+ * workspace of at least kda_get_workspace_size(..., KDA_CP_FORCE, 0) bytes
+ * (see kda_fwd, cp_mode):
  * *seg_out = the segment length (0: serial), *order_out = 1 where the shorter
  * segments are dispatched longest first (the workspace counters' order), else
  * 0.  seq_lens: host int32[num_seqs], each >= 0; the other arguments as for
@@ -139,7 +141,17 @@ size_t kda_get_workspace_size(int64_t total_tokens, int32_t num_heads, int32_t n
  *                  kda_get_workspace_size(B*T, H, N, cp_mode, seg_chunks) bytes;
  *                  owned by the caller, clobbered by the call, and must not be
  *                  shared by calls that may overlap.
- *   cp_mode, seg_chunks : segment plan, as for kda_plan_seg_chunks
+ *   cp_mode, seg_chunks : segment plan, as for kda_plan_seg_chunks.  A varlen
+ *                  call on the automatic plan (KDA_CP_AUTO, seg_chunks 0) with
+ *                  N*H >= 256 chains, which that plan keeps serial, splits its
+ *                  sequences after all when its workspace also holds the
+ *                  segmented layout (kda_get_workspace_size with KDA_CP_FORCE)
+ *                  and, seen on the device, its longest sequence has more than
+ *                  5/4 of the planned segment length: a skewed batch (one long
+ *                  prompt among short ones) then runs in segments instead of
+ *                  leaving the long chains as the whole pass.  The tables then
+ *                  follow kda_workspace_offsets with KDA_CP_FORCE.  The plan
+ *                  in use is in the workspace counters.
  *   stream       : hipStream_t to launch on (NULL = default stream)
  * B*T == 0 with no final_state returns KDA_OK without a launch. */
 int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,

@@ -275,6 +275,16 @@ class _Checked:
     __slots__ = ("B", "T", "H", "Hqk", "D", "N", "sdt", "out", "device")
 
 
+def _alloc_bytes(c, cpm, seg_chunks, varlen) -> int:
+    """Workspace bytes fwd and prepare allocate: the plan's, or for a varlen
+    call on the automatic plan with N*H >= 256 chains the segmented layout's
+    when larger, so that a skewed batch can split (kda_fwd, cp_mode)."""
+    need = get_workspace_size(c.B * c.T, c.H, c.N, cpm, seg_chunks)
+    if varlen and cpm == _CP["auto"] and int(seg_chunks) == 0 and c.N * c.H >= 256:
+        need = max(need, get_workspace_size(c.B * c.T, c.H, c.N, _CP["force"], 0))
+    return need
+
+
 def _check_fwd(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, state_layout,
                workspace=None) -> _Checked:
     """Every check of a forward call's tensors, before any device work
@@ -365,15 +375,18 @@ FLAG_WAIT_GAVE_UP = 0x300
 
 def read_counters(workspace, total_tokens: int, num_heads: int, num_seqs: int = 1, cp_mode="auto",
                   seg_chunks: int = 0) -> dict:
-    """The counters a call left in its workspace (copies 16 bytes to the host,
-    which waits for the call): chunks, segments, flags (FLAG_* bits) and
-    early_stops.  The sizes and plan must be the call's."""
+    """The counters a call left in its workspace (copies 24 bytes to the host,
+    which waits for the call): chunks, segments, flags (FLAG_* bits),
+    early_stops, the segment length in use (0: serial) and whether the shorter
+    segments were dispatched longest first.  The sizes and plan must be the
+    call's."""
     import numpy as np
 
     offs = workspace_offsets(total_tokens, num_heads, num_seqs, cp_mode, seg_chunks)
     o = offs["counters"]
-    c = workspace[o:o + 16].cpu().numpy().view(np.int32)
-    return {"chunks": int(c[0]), "segments": int(c[1]), "flags": int(c[2]), "early_stops": int(c[3])}
+    c = workspace[o:o + 24].cpu().numpy().view(np.int32)
+    return {"chunks": int(c[0]), "segments": int(c[1]), "flags": int(c[2]), "early_stops": int(c[3]),
+            "seg_chunks": int(c[4]), "longest_first": bool(c[5])}
 
 
 def _raise_on_flags(workspace, c: _Checked, cpm: int, seg_chunks: int):
@@ -416,7 +429,8 @@ def fwd(q, k, v, g, beta, scale: float, out=None, *, A_log, dt_bias, lower_bound
     need = get_workspace_size(c.B * c.T, c.H, c.N, cpm, seg_chunks)
     with torch.cuda.device_of(q):
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=c.device)
+            workspace = torch.empty(_alloc_bytes(c, cpm, seg_chunks, cu_seqlens is not None), dtype=torch.uint8,
+                                    device=c.device)
         stream = torch.cuda.current_stream(c.device).cuda_stream
         st = lib.kda_fwd(*_fwd_args(c, q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state,
                                     final_state, cu_seqlens, state_layout),
@@ -477,7 +491,8 @@ class PreparedFwd:
         t["out"] = c.out
         need = get_workspace_size(c.B * c.T, c.H, c.N, cpm, seg_chunks)
         if t["workspace"] is None:
-            t["workspace"] = torch.empty(need, dtype=torch.uint8, device=c.device)
+            t["workspace"] = torch.empty(_alloc_bytes(c, cpm, seg_chunks, t["cu_seqlens"] is not None),
+                                         dtype=torch.uint8, device=c.device)
         elif t["workspace"].numel() < need:
             raise ValueError(f"workspace of {t['workspace'].numel()} bytes, need {need}")
         if stream is None:

@@ -278,10 +278,24 @@ struct FwdArgs {
 
 struct Prepared {
   Layout lay;
+  // A varlen call on the automatic plan that keeps N*H >= 256 chains serial
+  // may split a sequence much longer than the others when its workspace also
+  // holds the segmented layout (split_lay, that of KDA_CP_FORCE): the index
+  // kernel then decides from the lengths (may_serial).
+  Layout split_lay;
+  bool can_split = false, may_serial = false;
   int32_t N = 0, H_qk = 0;
   int64_t total = 0;
   bool nothing = false;  // a valid call with nothing to launch
 };
+
+// Takes the segmented layout when a call that may split has room for it.
+void choose_layout(Prepared* pr, int64_t room) {
+  if (pr->can_split && room >= pr->split_lay.off[KDA_WS_TOTAL]) {
+    pr->lay = pr->split_lay;
+    pr->may_serial = true;
+  }
+}
 
 // Every check of a forward call that needs no workspace, before any HIP call.
 int32_t prepare(const FwdArgs& a, Prepared* pr) {
@@ -323,6 +337,12 @@ int32_t prepare(const FwdArgs& a, Prepared* pr) {
   if (!a.A_log || !a.dt_bias) return fail(KDA_ERR_INVALID_ARG, "A_log and dt_bias must be non-NULL");
   const int32_t st = layout(total, a.H, N, a.cp_mode, a.seg_chunks, &pr->lay);
   if (st != KDA_OK) return st;
+  if (a.cu_seqlens && a.cp_mode == KDA_CP_AUTO && a.seg_chunks == 0 && pr->lay.seg == 0 &&
+      (int64_t)N * a.H >= kSerialChains && layout(total, a.H, N, KDA_CP_FORCE, 0, &pr->split_lay) == KDA_OK) {
+    // the automatic plan's other rule still holds: at least 8 segments of work
+    const int64_t mc = (total + kda::C - 1) / kda::C;
+    pr->can_split = mc >= 8 * (int64_t)pr->split_lay.seg;
+  }
   pr->nothing = total == 0 && !a.final_state;
   return KDA_OK;
 }
@@ -378,7 +398,8 @@ int32_t launch(const FwdArgs& a, const Prepared& pr, uint8_t* ws, hipStream_t s)
   p.total_tokens = pr.total;
 
   hipError_t e;
-  e = kda::launch_index(a.cu_seqlens, N, a.T, pr.total, lay.seg, a.H, kCheckChunks, choose, mc, ms, t, s);
+  e = kda::launch_index(a.cu_seqlens, N, a.T, pr.total, lay.seg, a.H, kCheckChunks, choose, pr.may_serial, mc, ms, t,
+                        s);
   // Long units run their first (or only) pass with 4 consumer wavefronts of two
   // state tiles each, short ones with 8 of one tile (measured: 2-3 % faster
   // at 256-512 chunks per unit, 4 % slower at 36).  The second pass keeps 8:
@@ -472,10 +493,19 @@ int32_t kda_varlen_seg_choice(const int32_t* seq_lens, int32_t num_seqs, int32_t
     if (seq_lens[i] < 0) return fail(KDA_ERR_INVALID_ARG, "seq_lens[%d] = %d is negative", i, seq_lens[i]);
     total += seq_lens[i];
   }
-  const int32_t seg = plan(total, num_heads, num_seqs, cp_mode, seg_chunks);
+  int32_t seg = plan(total, num_heads, num_seqs, cp_mode, seg_chunks);
   if (seg < 0) return seg;
   *seg_out = seg;
   *order_out = 0;
+  if (seg == 0 && cp_mode == KDA_CP_AUTO && seg_chunks == 0 && (int64_t)num_seqs * num_heads >= kSerialChains) {
+    // the split of a skewed batch whose workspace holds the segmented layout
+    const int32_t f = plan(total, num_heads, num_seqs, KDA_CP_FORCE, 0);
+    const int64_t mc = (total + kda::C - 1) / kda::C;
+    int64_t max_nc = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) max_nc = std::max<int64_t>(max_nc, (seq_lens[i] + kda::C - 1) / kda::C);
+    if (f > 0 && mc >= 8 * (int64_t)f && 4 * max_nc > 5 * (int64_t)f) seg = f;
+    *seg_out = seg;
+  }
   // the index kernel's choice (kda_index.hip), replayed on the host
   if (seg_chunks != 0 || seg < kda::kSpanDeviceMinSeg || !kda::span_model_applies(seg, num_seqs, num_heads))
     return KDA_OK;
@@ -549,6 +579,7 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
   if (!workspace) return fail(KDA_ERR_INVALID_ARG, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % KDA_WORKSPACE_ALIGN != 0)
     return fail(KDA_ERR_INVALID_ARG, "workspace must be %d-byte aligned", KDA_WORKSPACE_ALIGN);
+  choose_layout(&pr, (int64_t)workspace_bytes);
   if ((int64_t)workspace_bytes < pr.lay.off[KDA_WS_TOTAL])
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %lld", workspace_bytes,
                 (long long)pr.lay.off[KDA_WS_TOTAL]);
@@ -567,6 +598,7 @@ int32_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const void*
   Prepared pr;
   int32_t st = prepare(a, &pr);
   if (st != KDA_OK || pr.nothing) return st;
+  choose_layout(&pr, (int64_t)KDA_NOALLOC_SCRATCH_BYTES);
   if (pr.lay.off[KDA_WS_TOTAL] > (int64_t)KDA_NOALLOC_SCRATCH_BYTES)
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
                 "this call needs %lld bytes of scratch, more than the %lld bytes the no-allocation entry point "

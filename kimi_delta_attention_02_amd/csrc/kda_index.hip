@@ -95,11 +95,16 @@ struct AddOp {
 // each), the boundaries and the chunk and segment prefix sums are also kept
 // there, and the lengths are computed from the LDS copy.
 // Returns the segment length the tables use and sets desc to their order of
-// the shorter segments (1: longest first).  With choose set, span_cu (LDS,
+// the shorter segments (1: longest first).  With may_serial (a call the
+// automatic plan would keep serial, N*H >= 256 chains, whose workspace holds
+// the segmented layout) the tables stay serial unless the longest sequence
+// has more than 5/4 of seg_chunks: only then does splitting shorten the pass,
+// whose serial span is at least the longest sequence's.  With choose set, span_cu (LDS,
 // 2 x (32 + kSpanMaxSeqs) x 64 + kSpanMaxSeqs ints) and span_key (LDS, 2
 // entries) serve the choice.
 __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long T_row, long long total,
-                               int seg_chunks, int H, int K, bool choose, Tables t, long long* smem, int* flags,
+                               int seg_chunks, int H, int K, bool choose, bool may_serial, Tables t,
+                               long long* smem, int* flags,
                                int* sst, int* coff, int* soff, int* foff, int* span_cu,
                                unsigned long long* span_key, int& desc) {
   if (threadIdx.x == 0) *flags = 0;
@@ -134,6 +139,22 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
   }
   __threadfence_block();
   __syncthreads();
+  if (may_serial && seg_chunks > 0) {
+    long long max_nc = 0;
+    for (int base = 0; base < N; base += SCAN_THREADS) {
+      const int i = base + (int)threadIdx.x;
+      long long nc = 0;
+      if (i < N) {
+        const long long len = sst ? (long long)sst[i + 1] - (long long)sst[i]
+                                  : (long long)t.seq_start[i + 1] - (long long)t.seq_start[i];
+        nc = (len + C - 1) / C;
+      }
+      long long tot;
+      block_inclusive_scan(nc, MaxOp(), 0LL, smem, &tot);
+      max_nc = tot > max_nc ? tot : max_nc;
+    }
+    if (4 * max_nc <= 5 * (long long)seg_chunks) seg_chunks = 0;
+  }
   // the segment length and order: lane s of wavefront w scores length
   // seg_chunks + s with the shorter segments in segment order (w = 0) or
   // longest first (w = 1); the least (span, length, order) wins
@@ -218,14 +239,14 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
 
 __global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __restrict__ cu, int N, long long T_row,
                                                                long long total, int seg_chunks, int H, int K,
-                                                               int choose, Tables t) {
+                                                               int choose, int may_serial, Tables t) {
   __shared__ long long smem[SCAN_WAVES];
   __shared__ int flags;
   __shared__ int span_cu[2 * (32 + kSpanMaxSeqs) * 64 + kSpanMaxSeqs];
   __shared__ unsigned long long span_key[2];
   int desc;
-  index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, t, smem, &flags, nullptr, nullptr, nullptr,
-                  nullptr, span_cu, span_key, desc);
+  index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, may_serial != 0, t, smem, &flags, nullptr,
+                  nullptr, nullptr, nullptr, span_cu, span_key, desc);
 }
 
 // largest j in [0, n) with off[j] <= x, given off[0] = 0 <= x and off non-decreasing
@@ -335,15 +356,16 @@ __global__ __launch_bounds__(256) void kda_index_fill(int N, int K, long long ma
 // row, then a forward walk (the owner of consecutive rows never decreases).
 __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* __restrict__ cu, int N, long long T_row,
                                                                 long long total, int seg_chunks, int H, int K,
-                                                                int choose, int max_chunks, int max_segs, Tables t) {
+                                                                int choose, int may_serial, int max_chunks,
+                                                                int max_segs, Tables t) {
   __shared__ long long smem[SCAN_WAVES];
   __shared__ int flags;
   __shared__ int sst[FUSED_MAX_N + 1], coff[FUSED_MAX_N + 1], soff[FUSED_MAX_N + 1], foff[FUSED_MAX_N + 1];
   __shared__ int span_cu[2 * (32 + kSpanMaxSeqs) * 64 + kSpanMaxSeqs];
   __shared__ unsigned long long span_key[2];
   int desc;
-  seg_chunks = index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, t, smem, &flags, sst, coff, soff,
-                               foff, span_cu, span_key, desc);
+  seg_chunks = index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, may_serial != 0, t, smem, &flags,
+                               sst, coff, soff, foff, span_cu, span_key, desc);
   __syncthreads();
   const int n_chunks = coff[N], n_segs = soff[N];
   {
@@ -402,20 +424,21 @@ hipError_t launch_index_fixed(int N, int L, int seg, Tables t, hipStream_t st) {
 }
 
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
-                        int H, int K, bool choose, int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st) {
+                        int H, int K, bool choose, bool may_serial, int64_t max_chunks, int64_t max_segs, Tables t,
+                        hipStream_t st) {
   if (!cu_seqlens) return hipSuccess;  // fixed length: written by the first chunk-kernel launch
   if (N <= FUSED_MAX_N && max_chunks <= FUSED_MAX_ROWS && max_segs <= FUSED_MAX_ROWS) {
     hipEvent_t e0, e1;
     stage_events(KDA_STAGE_INDEX, &e0, &e1);
     hipExtLaunchKernelGGL(kda_index_fused, dim3(1), dim3(SCAN_THREADS), 0, st, e0, e1, 0, cu_seqlens, N,
-                          (long long)T_row, (long long)total_tokens, seg_chunks, H, K, (int)choose, (int)max_chunks,
-                          (int)max_segs, t);
+                          (long long)T_row, (long long)total_tokens, seg_chunks, H, K, (int)choose, (int)may_serial,
+                          (int)max_chunks, (int)max_segs, t);
     return hipGetLastError();
   }
   hipEvent_t e0, e1;
   stage_events(KDA_STAGE_INDEX, &e0, &e1);
   hipExtLaunchKernelGGL(kda_index_scan, dim3(1), dim3(SCAN_THREADS), 0, st, e0, e1, 0, cu_seqlens, N,
-                        (long long)T_row, (long long)total_tokens, seg_chunks, H, K, (int)choose, t);
+                        (long long)T_row, (long long)total_tokens, seg_chunks, H, K, (int)choose, (int)may_serial, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = max_chunks > max_segs ? max_chunks : max_segs;

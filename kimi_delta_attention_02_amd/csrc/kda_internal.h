@@ -108,9 +108,12 @@ struct Seg {
 void stage_events(int stage, hipEvent_t* start, hipEvent_t* stop);
 hipError_t launch_index_fixed(int N, int L, int seg, Tables t, hipStream_t st);
 // choose: the library chooses the plan (seg_chunks is the planned, shortest
-// length; the tables may use a longer one, see seg_span); K: chk_chunks
+// length; the tables may use a longer one, see seg_span); may_serial: the
+// tables stay serial unless the lengths are skewed (kda_index.hip); K:
+// chk_chunks
 hipError_t launch_index(const int32_t* cu_seqlens, int N, int64_t T_row, int64_t total_tokens, int seg_chunks,
-                        int H, int K, bool choose, int64_t max_chunks, int64_t max_segs, Tables t, hipStream_t st);
+                        int H, int K, bool choose, bool may_serial, int64_t max_chunks, int64_t max_segs, Tables t,
+                        hipStream_t st);
 // producer/consumer chunk kernel: one launch per pass (phase 0: every segment,
 // phase 1: segments >= 1 from their start states, merged in the same launch)
 hipError_t launch_chunks(const Problem& p, Tables t, const Seg& sg, int64_t max_segs, int phase, bool segmented,

@@ -133,6 +133,19 @@ def test_varlen_seg_choice_follows_placement_model():
         assert got == want, (H, lens, planned, got, want)
         n_long += got[1]
     assert n_long > 10  # both orders were chosen
+    # N*H >= 256 chains: serial on the automatic plan unless the longest
+    # sequence has more than 5/4 of the segmented plan's length
+    skew = [32768] + [1024] * 31
+    f = kda.plan_seg_chunks(sum(skew), 16, 32, "force")
+    assert kda.plan_seg_chunks(sum(skew), 16, 32, "auto") == 0
+    assert kda.varlen_seg_choice(skew, 16) == (f, False) and f > 0
+    assert kda.varlen_seg_choice([1536] * 32, 16) == (0, False)
+    # the boundary: 39 x 1536 tokens and one of 5072 (317 chunks) plan 254-chunk
+    # segments; 317 <= 5/4 x 254 = 317.5 stays serial, 318 chunks split
+    assert kda.plan_seg_chunks(39 * 1536 + 5072, 16, 40, "force") == 254
+    assert kda.varlen_seg_choice([1536] * 39 + [5072], 16) == (0, False)
+    assert kda.varlen_seg_choice([1536] * 39 + [5088], 16) == (254, False)
+    assert kda.varlen_seg_choice(skew, 16, "off") == (0, False)
     # explicit lengths and serial plans are kept; bad arguments raise
     assert kda.varlen_seg_choice([65536, 1024], 16, "auto", 300) == (300, False)
     assert kda.varlen_seg_choice([65536, 1024], 16, "off") == (0, False)

@@ -479,6 +479,52 @@ def test_random_varlen_mix_segment_choice(i):
     check_against_oracle(w, x, out_c, fin_c, seqs=[short], heads=[3, 12], final_dtype=w.state_dtype)
 
 
+@pytest.mark.parametrize("kind", ["skewed", "balanced"])
+def test_skewed_varlen_batch_splits_on_the_automatic_plan(kind):
+    """32 sequences at H=16 (512 chains, which the automatic plan keeps
+    serial): with a workspace that also holds the segmented layout, a skewed
+    batch (32768 + 31 x 1024 tokens) splits on the device, a balanced one
+    (32 x 1536) stays serial, as kda_varlen_seg_choice says; the tables follow
+    the segmented layout's offsets; the result equals the serial call bit for
+    bit and matches the oracle on sampled chains.  With a workspace of the
+    automatic size only, the call stays serial."""
+    import kimi_delta_attention_02_amd as kda
+
+    lens = [32768] + [1024] * 31 if kind == "skewed" else [1536] * 32
+    w = kda_inputs.custom(seqlens=lens, H=16, lower_bound=-5.0, seed=53, name=f"{kind} 32 sequences")
+    say(f"case {w.name}")
+    x = kda_inputs.make_inputs(w)
+    d = dev_inputs(x)
+    out_s, fin_s, _ = run_gpu(w, x, d, cp_mode="off")
+    want, _ = kda.varlen_seg_choice(lens, w.H)
+    assert (want > 0) == (kind == "skewed")
+    ws = torch.empty(kda.get_workspace_size(w.T, w.H, w.N, "force", 0), dtype=torch.uint8, device="cuda")
+    fin = torch.empty_like(fin_s)
+    out = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], A_log=d["A_log"], dt_bias=d["dt_bias"],
+                  lower_bound=x["lower_bound"], workspace=ws, initial_state=d["initial_state"], final_state=fin,
+                  cu_seqlens=d["cu_seqlens"], cp_mode="auto", check=True)
+    cnt = kda.read_counters(ws, w.T, w.H, w.N, "auto")
+    say(f"{w.name}: segment length in use {cnt['seg_chunks']} (host replay {want}), early stops {cnt['early_stops']}")
+    assert cnt["seg_chunks"] == want and cnt["flags"] == 0
+    if want:
+        offs = kda.workspace_offsets(w.T, w.H, w.N, "force", 0)
+        ref = O.index_tables(lens, 16, want)
+        assert cnt["segments"] == ref["seq_seg_off"][-1] and cnt["early_stops"] > 0
+        np.testing.assert_array_equal(read_ws(ws, offs, "seq_seg_off", w.N + 1, np.int32), ref["seq_seg_off"])
+        np.testing.assert_array_equal(read_ws(ws, offs, "seg_tab", 4 * cnt["segments"], np.int32).reshape(-1, 4),
+                                      ref["seg_tab"])
+        unit = read_ws(ws, offs, "unit_tab", 8 * cnt["segments"], np.int32).reshape(-1, 8)
+        assert (unit[:, 7] == want).all()
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16)) and torch.equal(fin, fin_s)
+    check_against_oracle(w, x, out, fin, seqs=[0, 5], heads=[0, 9], final_dtype=w.state_dtype)
+    # a workspace of the automatic plan's size: serial, as before
+    ws2 = torch.empty(kda.get_workspace_size(w.T, w.H, w.N, "auto", 0), dtype=torch.uint8, device="cuda")
+    kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], A_log=d["A_log"], dt_bias=d["dt_bias"],
+            lower_bound=x["lower_bound"], workspace=ws2, initial_state=d["initial_state"], final_state=fin,
+            cu_seqlens=d["cu_seqlens"], cp_mode="auto", check=True)
+    assert kda.read_counters(ws2, w.T, w.H, w.N, "auto")["seg_chunks"] == 0
+
+
 def test_config4_slow_decay_segmented():
     """T=65536 H=16 at lower_bound -0.1: the start state's influence has not
     decayed after a segment's first 4 chunks, so the second pass runs every
