@@ -96,9 +96,10 @@ int32_t kda_fixed_seg_chunks(int32_t B, int64_t T, int32_t num_heads, int32_t cp
  * sequence lengths, as its index kernel chooses it on the device, with a
  * workspace of at least kda_get_workspace_size(..., KDA_CP_FORCE, 0) bytes
  * (see kda_fwd, cp_mode):
- * *seg_out = the segment length (0: serial), *order_out = 1 where the shorter
- * segments are dispatched longest first (the workspace counters' order), else
- * 0.  seq_lens: host int32[num_seqs], each >= 0; the other arguments as for
+ * *seg_out = the segment length (0: serial), *order_out = 1 where units are
+ * dispatched longest first (the workspace counters' order: the shorter
+ * segments after the full ones, or for a serial plan of at most 256 sequences
+ * every sequence), else 0.  seq_lens: host int32[num_seqs], each >= 0; the other arguments as for
  * kda_plan_seg_chunks.  Pure host arithmetic.  Returns KDA_OK or a negative
  * kda_status on invalid arguments. */
 int32_t kda_varlen_seg_choice(const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t cp_mode,
@@ -201,7 +202,7 @@ typedef enum {
                                chunk-kernel wait that gave up; early_stops counts the (segment,
                                head) pairs whose second pass matched the checkpoint and stopped
                                there; seg_chunks is the segment length the call used (0: serial);
-                               order is 1 where unit_tab has the shorter segments longest first */
+                               order is 1 where unit_tab has units longest first (see there) */
   KDA_WS_SEQ_START,         /* int32[N+1]   clamped sequence boundaries (last = end of the last sequence) */
   KDA_WS_SEQ_LEN,           /* int32[N]     clamped length */
   KDA_WS_SEQ_CHUNK_OFF,     /* int32[N+1]   prefix sums of ceil(len/16) */
@@ -226,8 +227,9 @@ typedef enum {
                                full-length segment first, in segment order, then the shorter ones
                                (a sequence's last segment, or a sequence shorter than a segment)
                                in segment order or, where the call chose it (counters' order), by
-                               first-pass chunks, longest first, ties in segment order (all -1
-                               past the live count) */
+                               first-pass chunks, longest first, ties in segment order; a serial
+                               varlen plan of at most 256 sequences has them longest first (all
+                               -1 past the live count) */
   KDA_WS_SEG_FIX,           /* fp32 [max_segs][H][128][128] state after a segment's first 4 chunks as the
                                first pass's block of the previous segment reached it, stored only when
                                that block could not compare it with the checkpoint (CP only) */

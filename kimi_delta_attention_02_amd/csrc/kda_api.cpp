@@ -506,6 +506,10 @@ int32_t kda_varlen_seg_choice(const int32_t* seq_lens, int32_t num_seqs, int32_t
     if (f > 0 && mc >= 8 * (int64_t)f && 4 * max_nc > 5 * (int64_t)f) seg = f;
     *seg_out = seg;
   }
+  if (seg == 0) {  // a serial varlen plan goes longest first up to kLptMaxSeqs sequences
+    *order_out = num_seqs <= kda::kLptMaxSeqs ? 1 : 0;
+    return KDA_OK;
+  }
   // the index kernel's choice (kda_index.hip), replayed on the host
   if (seg_chunks != 0 || seg < kda::kSpanDeviceMinSeg || !kda::span_model_applies(seg, num_seqs, num_heads))
     return KDA_OK;

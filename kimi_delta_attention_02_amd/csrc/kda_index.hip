@@ -94,8 +94,9 @@ struct AddOp {
 // (step 1 of the header).  When sst/coff/soff are given (LDS, N + 1 entries
 // each), the boundaries and the chunk and segment prefix sums are also kept
 // there, and the lengths are computed from the LDS copy.
-// Returns the segment length the tables use and sets desc to their order of
-// the shorter segments (1: longest first).  With may_serial (a call the
+// Returns the segment length the tables use and sets desc to their order (1:
+// longest first; the shorter segments of a segmented plan, every sequence of
+// a serial one).  With may_serial (a call the
 // automatic plan would keep serial, N*H >= 256 chains, whose workspace holds
 // the segmented layout) the tables stay serial unless the longest sequence
 // has more than 5/4 of seg_chunks: only then does splitting shorten the pass,
@@ -189,6 +190,10 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
     seg_chunks = (int)((key & 0xFFFFFFFFu) >> 1);
     desc = (int)(key & 1u);
   }
+  // a serial varlen plan dispatches its sequences longest first (the chains
+  // of a batch of N*H >= 256 then run in several rounds, which list scheduling
+  // packs best longest first; below that every unit starts at once)
+  if (seg_chunks == 0 && cu && N <= kLptMaxSeqs) desc = 1;
   // pass 2: lengths, chunk and segment counts, exclusive prefix sums
   long long c_carry = 0, s_carry = 0, f_carry = 0;
   if (threadIdx.x == 0) {
@@ -289,11 +294,31 @@ __device__ __forceinline__ void seg_row(int32_t* row, int sq, int idx, const int
 // shorter last segment, or a sequence shorter than seg) in segment order or,
 // with desc, longest first by rest_cost (ties in segment order; desc is only
 // chosen for at most kSpanMaxSeqs sequences, so the count below is short).
+// A serial plan (seg 0) has one unit per sequence: in sequence order, or with
+// desc (at most kLptMaxSeqs sequences) longest first, ties in sequence order.
 __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32_t* row, const int* coff,
                                          const int* soff, const int* foff, int N, int n_full, int seq_start,
                                          int seq_len, int seg, int K, int desc) {
   const int sq = row[0], j = row[3];
   const int full_here = foff[sq + 1] - foff[sq];
+  if (seg == 0 && desc) {
+    const int mine = coff[sq + 1] - coff[sq];
+    int rank = 0;
+    for (int i = 0; i < N; ++i) {
+      const int c = coff[i + 1] - coff[i];
+      rank += c > mine || (c == mine && i < sq);
+    }
+    int32_t* u = unit_tab + 8 * rank;
+    u[0] = idx;
+    u[1] = row[0];
+    u[2] = row[1];
+    u[3] = row[2];
+    u[4] = row[3];
+    u[5] = seq_start;
+    u[6] = seq_len;
+    u[7] = 0;
+    return;
+  }
   int rest_rank = soff[sq] - foff[sq];  // shorter segments of the sequences before this one
   if (desc && j >= full_here) {
     const int mine = rest_cost(coff[sq + 1] - coff[sq], seg, K);

@@ -28,7 +28,8 @@ constexpr int CNT_N_SEGS = 1;
 constexpr int CNT_FLAGS = 2;
 constexpr int CNT_EARLY_STOPS = 3;  // (segment, head) pairs whose second pass stopped at the checkpoint
 constexpr int CNT_SEG_CHUNKS = 4;   // segment length in use (0: serial)
-constexpr int CNT_ORDER = 5;        // order of the shorter segments in unit_tab: 0 segment order, 1 longest first
+constexpr int CNT_ORDER = 5;        // unit_tab order: 0 segment order, 1 longest first (see kda_index.hip)
+constexpr int kLptMaxSeqs = 256;    // a serial varlen plan of at most this many sequences goes longest first
 
 // Pointers into a carved workspace (device addresses).
 struct Tables {

@@ -129,7 +129,7 @@ def test_varlen_seg_choice_follows_placement_model():
             lens[int(rng.integers(0, N))] = int(rng.choice([0, 1, 15, 16, 17]))
         planned = kda.plan_seg_chunks(sum(lens), H, N, "auto")
         got = kda.varlen_seg_choice(lens, H)
-        want = chosen_plan(planned, lens, H, varlen=True) if planned else (0, False)
+        want = chosen_plan(planned, lens, H, varlen=True) if planned else (0, True)  # serial: longest first
         assert got == want, (H, lens, planned, got, want)
         n_long += got[1]
     assert n_long > 10  # both orders were chosen
@@ -139,16 +139,17 @@ def test_varlen_seg_choice_follows_placement_model():
     f = kda.plan_seg_chunks(sum(skew), 16, 32, "force")
     assert kda.plan_seg_chunks(sum(skew), 16, 32, "auto") == 0
     assert kda.varlen_seg_choice(skew, 16) == (f, False) and f > 0
-    assert kda.varlen_seg_choice([1536] * 32, 16) == (0, False)
+    assert kda.varlen_seg_choice([1536] * 32, 16) == (0, True)  # serial, longest first
     # the boundary: 39 x 1536 tokens and one of 5072 (317 chunks) plan 254-chunk
     # segments; 317 <= 5/4 x 254 = 317.5 stays serial, 318 chunks split
     assert kda.plan_seg_chunks(39 * 1536 + 5072, 16, 40, "force") == 254
-    assert kda.varlen_seg_choice([1536] * 39 + [5072], 16) == (0, False)
+    assert kda.varlen_seg_choice([1536] * 39 + [5072], 16) == (0, True)
     assert kda.varlen_seg_choice([1536] * 39 + [5088], 16) == (254, False)
-    assert kda.varlen_seg_choice(skew, 16, "off") == (0, False)
+    assert kda.varlen_seg_choice(skew, 16, "off") == (0, True)
+    assert kda.varlen_seg_choice([100] * 300, 16, "off") == (0, False)  # over 256 sequences: sequence order
     # explicit lengths and serial plans are kept; bad arguments raise
     assert kda.varlen_seg_choice([65536, 1024], 16, "auto", 300) == (300, False)
-    assert kda.varlen_seg_choice([65536, 1024], 16, "off") == (0, False)
+    assert kda.varlen_seg_choice([65536, 1024], 16, "off") == (0, True)
     with pytest.raises(kda.KdaError):
         kda.varlen_seg_choice([100, -1], 16)
 

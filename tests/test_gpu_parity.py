@@ -273,6 +273,8 @@ def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
     offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, mode, seg)
     planned = kda.plan_seg_chunks(w.B * w.T, w.H, w.N, mode, seg)
     used, desc = chosen_plan(planned, lens, H, varlen=not fixed) if seg == 0 else (planned, False)
+    if used == 0 and not fixed and len(lens) <= 256:
+        desc = True  # a serial varlen plan goes longest first
     if mode == "auto":
         assert used > 0
         if fixed:
@@ -302,9 +304,11 @@ def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
     starts = np.concatenate([[0], np.cumsum(lens)])
     full = [i for i in range(nsg) if not used or st[i][2] - st[i][1] == used]
     rest = [i for i in range(nsg) if used and st[i][2] - st[i][1] != used]
-    if desc:
-        nch_of = [(L + 15) // 16 for L in lens]
+    nch_of = [(L + 15) // 16 for L in lens]
+    if desc and used:
         rest = sorted(rest, key=lambda i: (-rest_cost(nch_of[st[i][0]], used), i))
+    elif desc:  # serial: every sequence, longest first
+        full = sorted(full, key=lambda i: (-nch_of[st[i][0]], i))
     want = np.array([[i, *st[i], starts[st[i][0]], lens[st[i][0]], used] for i in full + rest],
                     dtype=np.int32).reshape(-1, 8)
     unit = read_ws(ws, offs, "unit_tab", 8 * ms, np.int32).reshape(-1, 8)
