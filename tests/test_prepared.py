@@ -78,4 +78,5 @@ def test_check_flag_raises_on_clamped_offsets():
     kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], A_log=d["A_log"], dt_bias=d["dt_bias"],
             lower_bound=x["lower_bound"], cu_seqlens=good, cp_mode="off", workspace=ws, check=True)
     cnt = kda.read_counters(ws, 60, 1, 3, "off")
-    assert cnt == {"chunks": 1 + 2 + 2, "segments": 3, "flags": 0, "early_stops": 0}
+    assert cnt == {"chunks": 1 + 2 + 2, "segments": 3, "flags": 0, "early_stops": 0, "seg_chunks": 0,
+                   "longest_first": True}  # a serial varlen plan: sequences longest first
