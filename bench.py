@@ -369,9 +369,8 @@ def main() -> int:
     # whole steps).  Timed region 2, right after it: the same K steps again
     # with the library's per-kernel events on, for the stage split and the
     # chunk kernel's own duration (the roofline); region 2 does not feed
-    # ms_per_step.  The graph replays come last: kernels that follow them on
-    # this stack ran measurably slower (72 against 65 us for the first pass
-    # of B=2 T=4096 H=16), so nothing timed for the line comes after them.
+    # ms_per_step.  The graph replays come last, after W untimed replays of
+    # their own, so that nothing timed for the line follows them.
     tev = HipTimingEvents()
     evs = [tev.create() for _ in range(a.steps + 1)]
     tev.record(evs[0], stream)
@@ -412,6 +411,9 @@ def main() -> int:
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
+    torch.cuda.synchronize()
+    for _ in range(a.warmup):  # the first launches of a new graph carry one-time costs
+        graph.replay()
     torch.cuda.synchronize()
     gev = [tev.create() for _ in range(2)]
     tev.record(gev[0], stream)
