@@ -503,7 +503,10 @@ int32_t kda_varlen_seg_choice(const int32_t* seq_lens, int32_t num_seqs, int32_t
     const int64_t mc = (total + kda::C - 1) / kda::C;
     int64_t max_nc = 0;
     for (int32_t i = 0; i < num_seqs; ++i) max_nc = std::max<int64_t>(max_nc, (seq_lens[i] + kda::C - 1) / kda::C);
-    if (f > 0 && mc >= 8 * (int64_t)f && 4 * max_nc > 5 * (int64_t)f) seg = f;
+    if (f > 0 && mc >= 8 * (int64_t)f && 4 * max_nc > 5 * (int64_t)f) {
+      seg = f;
+      *order_out = num_seqs <= kda::kLptMaxSeqs ? 1 : 0;  // the shorter units longest first
+    }
     *seg_out = seg;
   }
   if (seg == 0) {  // a serial varlen plan goes longest first up to kLptMaxSeqs sequences

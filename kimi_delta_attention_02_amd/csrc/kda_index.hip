@@ -90,6 +90,28 @@ struct AddOp {
 
 }  // namespace
 
+// Longest-first ranks of the N <= kLptMaxSeqs sequences into lpt_rank (LDS),
+// one per thread: the key is the unit's first-pass chunks, that of the
+// shorter segment for a segmented plan (-1: it has none); ties in sequence
+// order.  coff: the chunk prefix sums (LDS or global, complete).
+__device__ void lpt_ranks(const int* coff, int N, int seg, int K, int* lpt_key, int* lpt_rank) {
+  if ((int)threadIdx.x < N) {
+    const int n = coff[threadIdx.x + 1] - coff[threadIdx.x];
+    lpt_key[threadIdx.x] = seg > 0 ? rest_cost(n, seg, K) : n;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < N) {
+    const int me = (int)threadIdx.x, mine = lpt_key[me];
+    int rank = 0;
+    for (int i = 0; i < N; ++i) {
+      const int c = lpt_key[i];
+      rank += c > mine || (c == mine && i < me);
+    }
+    lpt_rank[me] = rank;
+  }
+  __syncthreads();
+}
+
 // Clamped boundaries, lengths, chunk and segment prefix sums and the counters
 // (step 1 of the header).  When sst/coff/soff are given (LDS, N + 1 entries
 // each), the boundaries and the chunk and segment prefix sums are also kept
@@ -140,6 +162,9 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
   }
   __threadfence_block();
   __syncthreads();
+  // a split of N*H >= 256 chains leaves many shorter units, which run in
+  // several rounds after the full segments: longest first packs them best
+  desc = 0;
   if (may_serial && seg_chunks > 0) {
     long long max_nc = 0;
     for (int base = 0; base < N; base += SCAN_THREADS) {
@@ -154,12 +179,14 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
       block_inclusive_scan(nc, MaxOp(), 0LL, smem, &tot);
       max_nc = tot > max_nc ? tot : max_nc;
     }
-    if (4 * max_nc <= 5 * (long long)seg_chunks) seg_chunks = 0;
+    if (4 * max_nc <= 5 * (long long)seg_chunks)
+      seg_chunks = 0;
+    else if (N <= kLptMaxSeqs)
+      desc = 1;
   }
   // the segment length and order: lane s of wavefront w scores length
   // seg_chunks + s with the shorter segments in segment order (w = 0) or
   // longest first (w = 1); the least (span, length, order) wins
-  desc = 0;
   if (choose && seg_chunks >= kSpanDeviceMinSeg && span_model_applies(seg_chunks, N, H)) {
     constexpr int kWaveInts = (32 + kSpanMaxSeqs) * 64;  // one wavefront's cu arrays, lane-interleaved
     int* nc = span_cu + 2 * kWaveInts;                     // chunks of each sequence
@@ -242,17 +269,6 @@ __device__ int index_scan_body(const int32_t* __restrict__ cu, int N, long long 
   return seg_chunks;
 }
 
-__global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __restrict__ cu, int N, long long T_row,
-                                                               long long total, int seg_chunks, int H, int K,
-                                                               int choose, int may_serial, Tables t) {
-  __shared__ long long smem[SCAN_WAVES];
-  __shared__ int flags;
-  __shared__ int span_cu[2 * (32 + kSpanMaxSeqs) * 64 + kSpanMaxSeqs];
-  __shared__ unsigned long long span_key[2];
-  int desc;
-  index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, may_serial != 0, t, smem, &flags, nullptr,
-                  nullptr, nullptr, nullptr, span_cu, span_key, desc);
-}
 
 // largest j in [0, n) with off[j] <= x, given off[0] = 0 <= x and off non-decreasing
 __device__ __forceinline__ int owner_of(const int32_t* off, int n, int x) {
@@ -293,20 +309,26 @@ __device__ __forceinline__ void seg_row(int32_t* row, int sq, int idx, const int
 // the full-length segments in segment order, then the others (a sequence's
 // shorter last segment, or a sequence shorter than seg) in segment order or,
 // with desc, longest first by rest_cost (ties in segment order; desc is only
-// chosen for at most kSpanMaxSeqs sequences, so the count below is short).
+// chosen for at most kLptMaxSeqs sequences, so the count below is short).
 // A serial plan (seg 0) has one unit per sequence: in sequence order, or with
 // desc (at most kLptMaxSeqs sequences) longest first, ties in sequence order.
+// lpt_rank, where given, holds each sequence's longest-first rank (that of its
+// shorter segment, for a segmented plan); else the rank is counted here.
 __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32_t* row, const int* coff,
                                          const int* soff, const int* foff, int N, int n_full, int seq_start,
-                                         int seq_len, int seg, int K, int desc) {
+                                         int seq_len, int seg, int K, int desc, const int* lpt_rank) {
   const int sq = row[0], j = row[3];
   const int full_here = foff[sq + 1] - foff[sq];
   if (seg == 0 && desc) {
-    const int mine = coff[sq + 1] - coff[sq];
     int rank = 0;
-    for (int i = 0; i < N; ++i) {
-      const int c = coff[i + 1] - coff[i];
-      rank += c > mine || (c == mine && i < sq);
+    if (lpt_rank) {
+      rank = lpt_rank[sq];
+    } else {
+      const int mine = coff[sq + 1] - coff[sq];
+      for (int i = 0; i < N; ++i) {
+        const int c = coff[i + 1] - coff[i];
+        rank += c > mine || (c == mine && i < sq);
+      }
     }
     int32_t* u = unit_tab + 8 * rank;
     u[0] = idx;
@@ -320,7 +342,9 @@ __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32
     return;
   }
   int rest_rank = soff[sq] - foff[sq];  // shorter segments of the sequences before this one
-  if (desc && j >= full_here) {
+  if (desc && j >= full_here && lpt_rank) {
+    rest_rank = lpt_rank[sq];
+  } else if (desc && j >= full_here) {
     const int mine = rest_cost(coff[sq + 1] - coff[sq], seg, K);
     rest_rank = 0;
     for (int i = 0; i < N; ++i) {
@@ -338,6 +362,37 @@ __device__ __forceinline__ void put_unit(int32_t* unit_tab, int idx, const int32
   u[5] = seq_start;
   u[6] = seq_len;
   u[7] = seg;
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void kda_index_scan(const int32_t* __restrict__ cu, int N, long long T_row,
+                                                               long long total, int seg_chunks, int H, int K,
+                                                               int choose, int may_serial, Tables t) {
+  __shared__ long long smem[SCAN_WAVES];
+  __shared__ int flags;
+  __shared__ int span_cu[2 * (32 + kSpanMaxSeqs) * 64 + kSpanMaxSeqs];
+  __shared__ unsigned long long span_key[2];
+  __shared__ int lpt_key[kLptMaxSeqs], lpt_rank[kLptMaxSeqs];
+  int desc;
+  seg_chunks = index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, may_serial != 0, t, smem, &flags,
+                               nullptr, nullptr, nullptr, nullptr, span_cu, span_key, desc);
+  if (!desc) return;
+  // the longest-first rows, one thread per sequence; kda_index_fill writes
+  // the others (the prefix sums were stored by this workgroup above)
+  __threadfence_block();
+  __syncthreads();
+  lpt_ranks(t.seq_chunk_off, N, seg_chunks, K, lpt_key, lpt_rank);
+  const int sq = (int)threadIdx.x;
+  if (sq < N) {
+    const int ns = t.seq_seg_off[sq + 1] - t.seq_seg_off[sq];
+    const int nf = t.seq_full_off[sq + 1] - t.seq_full_off[sq];
+    if (seg_chunks == 0 || ns > nf) {  // a serial unit, or this sequence's shorter segment
+      const int idx = t.seq_seg_off[sq + 1] - 1;
+      int32_t row[4];
+      seg_row(row, sq, idx, t.seq_chunk_off, t.seq_seg_off, seg_chunks);
+      put_unit(t.unit_tab, idx, row, t.seq_chunk_off, t.seq_seg_off, t.seq_full_off, N, t.seq_full_off[N],
+               t.seq_start[sq], t.seq_len[sq], seg_chunks, K, desc, lpt_rank);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void kda_index_fill(int N, int K, long long max_chunks, long long max_segs,
@@ -365,8 +420,11 @@ __global__ __launch_bounds__(256) void kda_index_fill(int N, int K, long long ma
       int s = owner_of(t.seq_seg_off, N + 1, (int)idx);
       while (s + 1 <= N && t.seq_seg_off[s + 1] <= (int)idx) ++s;
       seg_row(row, s, (int)idx, t.seq_chunk_off, t.seq_seg_off, seg_chunks);
-      put_unit(t.unit_tab, (int)idx, row, t.seq_chunk_off, t.seq_seg_off, t.seq_full_off, N, t.seq_full_off[N],
-               t.seq_start[s], t.seq_len[s], seg_chunks, K, desc);
+      // with desc, kda_index_scan wrote the longest-first rows (a serial
+      // plan's, or the shorter segments)
+      if (!desc || (seg_chunks > 0 && row[3] < t.seq_full_off[s + 1] - t.seq_full_off[s]))
+        put_unit(t.unit_tab, (int)idx, row, t.seq_chunk_off, t.seq_seg_off, t.seq_full_off, N, t.seq_full_off[N],
+                 t.seq_start[s], t.seq_len[s], seg_chunks, K, desc, nullptr);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) t.unit_tab[8 * idx + k] = -1;
@@ -392,6 +450,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* _
   seg_chunks = index_scan_body(cu, N, T_row, total, seg_chunks, H, K, choose != 0, may_serial != 0, t, smem, &flags,
                                sst, coff, soff, foff, span_cu, span_key, desc);
   __syncthreads();
+  // longest-first ranks, once per sequence (desc is set for at most
+  // kLptMaxSeqs sequences): the key is the unit's first-pass chunks, that of
+  // the shorter segment for a segmented plan (-1: it has none)
+  __shared__ int lpt_key[kLptMaxSeqs], lpt_rank[kLptMaxSeqs];
+  if (desc) lpt_ranks(coff, N, seg_chunks, K, lpt_key, lpt_rank);
   const int n_chunks = coff[N], n_segs = soff[N];
   {
     const int per = (max_chunks + SCAN_THREADS - 1) / SCAN_THREADS;
@@ -419,7 +482,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_index_fused(const int32_t* _
       if (r < n_segs) {
         while (a + 1 <= N && soff[a + 1] <= r) ++a;
         seg_row(row, a, r, coff, soff, seg_chunks);
-        put_unit(t.unit_tab, r, row, coff, soff, foff, N, foff[N], sst[a], sst[a + 1] - sst[a], seg_chunks, K, desc);
+        put_unit(t.unit_tab, r, row, coff, soff, foff, N, foff[N], sst[a], sst[a + 1] - sst[a], seg_chunks, K, desc,
+                 desc ? lpt_rank : nullptr);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) t.unit_tab[8 * r + k] = -1;

@@ -138,13 +138,13 @@ def test_varlen_seg_choice_follows_placement_model():
     skew = [32768] + [1024] * 31
     f = kda.plan_seg_chunks(sum(skew), 16, 32, "force")
     assert kda.plan_seg_chunks(sum(skew), 16, 32, "auto") == 0
-    assert kda.varlen_seg_choice(skew, 16) == (f, False) and f > 0
+    assert kda.varlen_seg_choice(skew, 16) == (f, True) and f > 0  # shorter units longest first
     assert kda.varlen_seg_choice([1536] * 32, 16) == (0, True)  # serial, longest first
     # the boundary: 39 x 1536 tokens and one of 5072 (317 chunks) plan 254-chunk
     # segments; 317 <= 5/4 x 254 = 317.5 stays serial, 318 chunks split
     assert kda.plan_seg_chunks(39 * 1536 + 5072, 16, 40, "force") == 254
     assert kda.varlen_seg_choice([1536] * 39 + [5072], 16) == (0, True)
-    assert kda.varlen_seg_choice([1536] * 39 + [5088], 16) == (254, False)
+    assert kda.varlen_seg_choice([1536] * 39 + [5088], 16) == (254, True)
     assert kda.varlen_seg_choice(skew, 16, "off") == (0, True)
     assert kda.varlen_seg_choice([100] * 300, 16, "off") == (0, False)  # over 256 sequences: sequence order
     # explicit lengths and serial plans are kept; bad arguments raise

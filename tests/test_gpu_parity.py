@@ -253,7 +253,12 @@ def _zero_inputs(w):
     ([300000, 5000, 70], 0, False, 16, "auto"), ([8192] * 3, 0, True, 16, "auto"), ([65536], 0, False, 16, "auto"),
     ([24000, 3000, 1000], 0, False, 16, "auto"),
     # the two-launch form with the shorter segments longest first
-    ([41621, 4127, 111604, 20239, 3299, 75763, 1774, 16070], 0, False, 16, "auto")])
+    ([41621, 4127, 111604, 20239, 3299, 75763, 1774, 16070], 0, False, 16, "auto"),
+    # the two-launch form, serial, sequences longest first
+    ([70000] * 4 + [1000] * 20, 0, False, 1, "off"),
+    # the two-launch form, a skewed batch of N*H >= 256 chains split on the
+    # automatic plan (a workspace of the segmented size)
+    ([200000] + [2000] * 40, 0, False, 8, "auto-split")])
 def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
     from tests.span_model import chosen_plan, rest_cost
 
@@ -263,18 +268,26 @@ def test_index_tables_bit_exact(lens, seg, fixed, H, mode):
         w = kda_inputs.custom(seqlens=lens, H=H, seed=28, name="tables", init_std=None)
     x, d = _zero_inputs(w)
     mode = mode or ("force" if seg else "off")
-    _, _, ws = run_gpu(w, x, d, cp_mode=mode, seg_chunks=seg, want_final=False)
     import kimi_delta_attention_02_amd as kda
+
+    split = mode == "auto-split"
+    mode = "auto" if split else mode
+    big = kda.get_workspace_size(w.B * w.T, w.H, w.N, "force", 0) if split else None
+    _, _, ws = run_gpu(w, x, d, cp_mode=mode, seg_chunks=seg, want_final=False,
+                       workspace=None if big is None else torch.empty(big, dtype=torch.uint8, device="cuda"))
 
     if fixed:  # kda_fwd computes these rows in closed form without storing them
         kda.write_fixed_tables(w.B, w.T, w.H, mode, seg, ws)
         torch.cuda.synchronize()
 
-    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, mode, seg)
+    offs = kda.workspace_offsets(w.B * w.T, w.H, w.N, "force" if split else mode, seg)
     planned = kda.plan_seg_chunks(w.B * w.T, w.H, w.N, mode, seg)
     used, desc = chosen_plan(planned, lens, H, varlen=not fixed) if seg == 0 else (planned, False)
     if used == 0 and not fixed and len(lens) <= 256:
         desc = True  # a serial varlen plan goes longest first
+    if split:  # the host replay of the device's split decision
+        used, desc = kda.varlen_seg_choice(lens, H)
+        assert used > 0 and desc
     if mode == "auto":
         assert used > 0
         if fixed:
@@ -517,7 +530,17 @@ def test_skewed_varlen_batch_splits_on_the_automatic_plan(kind):
         np.testing.assert_array_equal(read_ws(ws, offs, "seq_seg_off", w.N + 1, np.int32), ref["seq_seg_off"])
         np.testing.assert_array_equal(read_ws(ws, offs, "seg_tab", 4 * cnt["segments"], np.int32).reshape(-1, 4),
                                       ref["seg_tab"])
+        # the full segments in segment order, then the shorter units longest first
+        from tests.span_model import rest_cost
+
+        st = ref["seg_tab"]
+        nch_of = [(L + 15) // 16 for L in lens]
+        full = [i for i in range(len(st)) if st[i][2] - st[i][1] == want]
+        rest = sorted((i for i in range(len(st)) if st[i][2] - st[i][1] != want),
+                      key=lambda i: (-rest_cost(nch_of[st[i][0]], want), i))
+        assert cnt["longest_first"]
         unit = read_ws(ws, offs, "unit_tab", 8 * cnt["segments"], np.int32).reshape(-1, 8)
+        np.testing.assert_array_equal(unit[:, 0], full + rest)
         assert (unit[:, 7] == want).all()
     assert torch.equal(out.view(torch.int16), out_s.view(torch.int16)) and torch.equal(fin, fin_s)
     check_against_oracle(w, x, out, fin, seqs=[0, 5], heads=[0, 9], final_dtype=w.state_dtype)
