@@ -338,7 +338,8 @@ def main() -> int:
     if cu is not None and a.cp == "auto" and a.seg == 0:
         # as the binding allocates: room for the segmented layout lets a skewed
         # varlen batch split where the automatic plan would stay serial
-        need = max(need, kda.get_workspace_size(total, w.H, w.N, "force", 0))
+        split = kda.get_workspace_size(total, w.H, w.N, "force", 0)
+        need = max(need, split) if split <= kda.SPLIT_WORKSPACE_CAP else need
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def step():

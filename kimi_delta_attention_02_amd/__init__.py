@@ -275,13 +275,21 @@ class _Checked:
     __slots__ = ("B", "T", "H", "Hqk", "D", "N", "sdt", "out", "device")
 
 
+SPLIT_WORKSPACE_CAP = 512 << 20
+
+
 def _alloc_bytes(c, cpm, seg_chunks, varlen) -> int:
     """Workspace bytes fwd and prepare allocate: the plan's, or for a varlen
     call on the automatic plan with N*H >= 256 chains the segmented layout's
-    when larger, so that a skewed batch can split (kda_fwd, cp_mode)."""
+    when larger, so that a skewed batch can split (kda_fwd, cp_mode).  The
+    segmented layout takes about (256 + N*H) x 320 KiB; beyond
+    SPLIT_WORKSPACE_CAP bytes the plan's is allocated (the call then stays
+    serial; pass a larger workspace to let it split)."""
     need = get_workspace_size(c.B * c.T, c.H, c.N, cpm, seg_chunks)
     if varlen and cpm == _CP["auto"] and int(seg_chunks) == 0 and c.N * c.H >= 256:
-        need = max(need, get_workspace_size(c.B * c.T, c.H, c.N, _CP["force"], 0))
+        split = get_workspace_size(c.B * c.T, c.H, c.N, _CP["force"], 0)
+        if split <= SPLIT_WORKSPACE_CAP:
+            need = max(need, split)
     return need
 
 

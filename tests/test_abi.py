@@ -154,6 +154,30 @@ def test_varlen_seg_choice_follows_placement_model():
         kda.varlen_seg_choice([100, -1], 16)
 
 
+def test_automatic_workspace_makes_room_for_a_split_up_to_the_cap():
+    """fwd and prepare allocate the segmented layout's workspace for a varlen
+    call on the automatic plan with N*H >= 256 chains (so that a skewed batch
+    can split), but only up to SPLIT_WORKSPACE_CAP; otherwise the plan's own."""
+    from types import SimpleNamespace as C
+
+    def alloc(N, H, T, cp="auto", seg=0, varlen=True):
+        return kda._alloc_bytes(C(B=1, T=T, H=H, N=N), kda._CP[cp], seg, varlen)
+
+    def size(N, H, T, cp, seg=0):
+        return kda.get_workspace_size(T, H, N, cp, seg)
+
+    for N, H, T in [(32, 8, 64512), (41, 8, 280000), (32, 16, 65536)]:  # N*H >= 256, split size under the cap
+        assert size(N, H, T, "force") <= kda.SPLIT_WORKSPACE_CAP
+        assert alloc(N, H, T) == max(size(N, H, T, "auto"), size(N, H, T, "force"))
+        assert alloc(N, H, T, varlen=False) == size(N, H, T, "auto")
+        assert alloc(N, H, T, cp="off") == size(N, H, T, "off")
+        assert alloc(N, H, T, seg=4) == size(N, H, T, "auto", 4)
+    assert alloc(15, 16, 65536) == size(15, 16, 65536, "auto")  # N*H = 240 < 256
+    for N, H, T in [(64, 32, 131072), (256, 16, 262144)]:  # split size over the cap
+        assert size(N, H, T, "force") > kda.SPLIT_WORKSPACE_CAP
+        assert alloc(N, H, T) == size(N, H, T, "auto")
+
+
 def test_workspace_layout_consistent():
     for args in [(256, 2, 1, "off", 0), (8192, 16, 2, "auto", 0), (79890, 16, 7, "force", 64), (0, 4, 3, "auto", 0)]:
         size = kda.get_workspace_size(*args)
