@@ -176,6 +176,11 @@ int32_t kda_fwd(const void* q, const void* k, const void* v, const void* g, cons
  *     A segmented plan needs about 320 KiB per (segment, head) unit plus the
  *     index tables: one sequence of 64K tokens at H = 16 on the automatic
  *     plan takes 85 MiB, a serial plan of it 30 KiB.
+ *   - The array counts as the workspace room for kda_fwd's skewed-batch
+ *     split: a varlen call on the automatic plan with N*H >= 256 chains may
+ *     split wherever the segmented layout fits in it, so it matches a kda_fwd
+ *     call given a workspace of at least the KDA_CP_FORCE size, not one of the
+ *     automatic plan's size.
  *   - Every call on one GPU shares that GPU's array, which keeps the last
  *     call's contents; no part of it needs to start at zero.  Calls that may
  *     overlap on one GPU (other streams, other host threads) race on it and
