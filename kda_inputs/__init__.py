@@ -161,3 +161,55 @@ def make_inputs(w: Workload) -> dict:
     out["scale"] = float(np.float32(w.scale))
     out["lower_bound"] = float(np.float32(w.lower_bound))
     return out
+
+
+def make_device_inputs(w: Workload, device, rows_per_draw: int = 16) -> dict:
+    """Draw a fixed-length workload's tensors on a device, for sizes whose
+    host draw would take minutes (billions of elements).
+
+    q, k, v, g, beta and the initial state come from torch's generator of that
+    device, seeded with w.seed and drawn in that order: fp32 standard normals
+    times the stated standard deviation, rounded to bf16 (nearest, ties to
+    even) where the tensor is bf16, drawn over the batch dimension in pieces of
+    rows_per_draw rows so that the fp32 draw stays small.  A_log and dt_bias
+    are small and come from numpy as in make_inputs (PCG64(w.seed), in that
+    order).  Device tensors are torch tensors (bf16 as torch.bfloat16); A_log
+    and dt_bias are returned as float32 numpy arrays, to be moved by the
+    caller.  A check against the oracle reads the slices it needs back from
+    the device: those are the inputs, not results.
+    """
+    import torch
+
+    if w.seqlens is not None:
+        raise ValueError("make_device_inputs draws fixed-length workloads (view the result as B = 1 for varlen)")
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(w.seed))
+
+    def draw(shape, std, dtype):
+        t = torch.empty(shape, dtype=dtype, device=device)
+        for r0 in range(0, shape[0], rows_per_draw):
+            r1 = min(shape[0], r0 + rows_per_draw)
+            x = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=gen, device=device, dtype=torch.float32)
+            if std != 1.0:
+                x.mul_(std)
+            t[r0:r1] = x.to(dtype)
+            del x
+        return t
+
+    out = {}
+    shp = (w.B, w.T, w.H, HEAD_DIM)
+    for name in ("q", "k", "v", "g"):
+        out[name] = draw(shp, w.x_std, torch.bfloat16)
+    out["beta"] = draw((w.B, w.T, w.H), w.x_std, torch.bfloat16)
+    if w.init_std is not None:
+        sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
+        out["initial_state"] = draw((w.N, w.H, HEAD_DIM, HEAD_DIM), w.init_std, sdt)
+    else:
+        out["initial_state"] = None
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    out["A_log"] = _normal(rng, (w.H,), w.a_log_std)
+    out["dt_bias"] = _normal(rng, (w.H, HEAD_DIM), w.dt_bias_std)
+    out["cu_seqlens"] = None
+    out["scale"] = float(np.float32(w.scale))
+    out["lower_bound"] = float(np.float32(w.lower_bound))
+    return out
