@@ -27,7 +27,8 @@ and, beside it, the bandwidth of a plain device copy measured in the same run.
 Host time per call is reported under "path" three ways: fwd() from Python,
 the prepared call (kda.prepare: checked and marshalled once), and the C ABI's
 own share (the library's host timer).  The same call is also captured once in
-a HIP graph and replayed K times, last.
+a HIP graph and replayed K times, last, after the same preheat and warmup
+as the plain calls (the capture leaves the device idle and the clock falls).
 
 The CPU baseline times the fp64 oracle (unchanged) on a bounded sample of the
 same workload, before any GPU work starts: its first tokens (whole sequences
@@ -346,18 +347,22 @@ def main() -> int:
         kda.fwd(q, k, v, g, beta, x["scale"], out, A_log=A_log, dt_bias=dt_bias, lower_bound=x["lower_bound"],
                 workspace=ws, initial_state=init, final_state=final, cu_seqlens=cu, cp_mode=a.cp, seg_chunks=a.seg)
 
-    # preheat: batches of calls, each waited for, until --preheat-ms of wall
-    # time has passed (the device is busy for nearly all of it)
-    preheat_calls = 0
-    h0 = time.perf_counter()
-    batch = 1
-    while (time.perf_counter() - h0) * 1e3 < a.preheat_ms:
-        for _ in range(batch):
-            step()
-        torch.cuda.synchronize()
-        preheat_calls += batch
-        batch = min(2 * batch, 64)
-    preheat_ms = (time.perf_counter() - h0) * 1e3
+    def preheat(fn):
+        """Batches of calls, each waited for, until --preheat-ms of wall time
+        has passed (the device is busy for nearly all of it); returns the
+        calls made and the time taken."""
+        calls = 0
+        h0 = time.perf_counter()
+        batch = 1
+        while (time.perf_counter() - h0) * 1e3 < a.preheat_ms:
+            for _ in range(batch):
+                fn()
+            torch.cuda.synchronize()
+            calls += batch
+            batch = min(2 * batch, 64)
+        return calls, (time.perf_counter() - h0) * 1e3
+
+    preheat_calls, preheat_ms = preheat(step)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -413,7 +418,10 @@ def main() -> int:
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
-    for _ in range(a.warmup):  # the first launches of a new graph carry one-time costs
+    # the capture and instantiation leave the device idle, and the clock
+    # falls; the replays get the plain calls' preheat and warmup
+    graph_preheat_calls, _ = preheat(graph.replay)
+    for _ in range(a.warmup):
         graph.replay()
     torch.cuda.synchronize()
     gev = [tev.create() for _ in range(2)]
@@ -506,8 +514,10 @@ def main() -> int:
             "host_us_per_call": round(host_us, 1),
             "prepared_host_us_per_call": round(prep_host_us, 2),
             "c_abi_host_us_per_call": round(cabi_us / max(cabi_calls, 1), 2),
-            # the call captured in a HIP graph, replayed K times
+            # the call captured in a HIP graph, replayed K times (after
+            # graph_preheat_calls untimed replays and W more)
             "graph_ms_per_step": round(graph_ms, 4),
+            "graph_preheat_calls": graph_preheat_calls,
             "graph_host_us_per_call": round(graph_host_us, 1),
         },
         "stages_ms_per_step": {n: round(t / a.steps, 4) for n, (t, c) in stages.items() if c},
