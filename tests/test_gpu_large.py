@@ -14,7 +14,12 @@ generator, and run
     (the index tables then take the two-launch form: 132,000 chunk rows).
 In each call the chains that cross those two boundaries, and the last one,
 are compared with the fp64 oracle (the token recurrence) on three heads, from
-host copies of just their inputs."""
+host copies of just their inputs.
+
+Two more limits: the largest head count the interface accepts (65535, so that
+a token's row of H x 128 elements stays under the 2^24 of the kernels' 24-bit
+row multiplies), fixed length and varlen; and 300,000 ragged sequences at one
+head (a grid of as many chains, and the two-launch index tables)."""
 import numpy as np
 import pytest
 
@@ -68,25 +73,28 @@ def _call(d, q, k, v, g, beta, init, final, cu=None, cp_mode="auto", seg_chunks=
     return out
 
 
-def _check_spans(name, d, out, final, spans):
+def _check_spans(name, d, out, final, spans, heads=HEADS, n_heads=H, init=None):
     """spans: (state index, first token in the flattened token order, length)
     of the chains to compare; their inputs are copied to the host and run
-    through the oracle as one varlen problem."""
+    through the oracle as one varlen problem (init: the initial states, by
+    default the inputs' own)."""
     lens = [L for _, _, L in spans]
     x = {}
     for n in ("q", "k", "v", "g", "beta"):
         f = _flat(d[n])
         x[n] = np.concatenate([_bits(f[:, t0:t0 + L]) for _, t0, L in spans], axis=1)
     idx = torch.tensor([i for i, _, _ in spans], device="cuda")
-    x["initial_state"] = d["initial_state"][idx].cpu().numpy()
+    s0 = d["initial_state"] if init is None else init
+    x["initial_state"] = None if s0 is False else s0[idx].cpu().numpy()
     for n in ("A_log", "dt_bias", "scale", "lower_bound"):
         x[n] = d[n]
     cu = np.zeros(len(spans) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     x["cu_seqlens"] = cu
-    w = kda_inputs.custom(seqlens=lens, H=H, lower_bound=d["lower_bound"], name=name)
+    w = kda_inputs.custom(seqlens=lens, H=n_heads, lower_bound=d["lower_bound"], name=name)
     out_sub = torch.cat([_flat(out)[:, t0:t0 + L] for _, t0, L in spans], dim=1)
-    check_against_oracle(w, x, out_sub, final[idx], heads=HEADS, final_dtype="fp32")
+    check_against_oracle(w, x, out_sub, None if final is None else final[idx], heads=heads,
+                         init=s0 is not False, final_dtype="fp32")
 
 
 def _covering(starts, lens, tokens):
@@ -94,6 +102,65 @@ def _covering(starts, lens, tokens):
     ends = np.asarray(starts) + np.asarray(lens)
     pick = [int(np.searchsorted(ends, t, side="right")) for t in tokens] + [len(lens) - 1]
     return sorted(set(pick))
+
+
+def _device_inputs(w, need):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    free, _ = torch.cuda.mem_get_info()
+    if free < need:
+        pytest.skip(f"needs {need >> 30} GiB of free device memory, {free >> 30} GiB free")
+    say(f"drawing {w.name} on the device")
+    d = kda_inputs.make_device_inputs(w, "cuda")
+    d["A_log_dev"] = torch.from_numpy(d["A_log"]).cuda()
+    d["dt_bias_dev"] = torch.from_numpy(d["dt_bias"]).cuda()
+    return d
+
+
+def test_maximum_head_count():
+    Hm = 65535
+    w = kda_inputs.custom(B=1, T=21, H=Hm, lower_bound=-1.0, init_std=0.05, state_dtype="fp32", seed=43,
+                          name="kda_fwd_B1_T21_H65535")
+    d = _device_inputs(w, 30 << 30)
+    heads = [0, 1, 40000, Hm - 1]
+    fin = torch.full((1, Hm, D, D), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"{w.name}: fixed length, {Hm} chains of one chunk and a 5-token tail")
+    out = _call(d, d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], fin)
+    _check_spans(w.name, d, out, fin, [(0, 0, 21)], heads=heads, n_heads=Hm)
+    del fin
+    # the same tokens as two sequences (5 and 16 tokens), no initial state
+    fin2 = torch.full((2, Hm, D, D), float("nan"), dtype=torch.float32, device="cuda")
+    cu = torch.tensor([0, 5, 21], dtype=torch.int32, device="cuda")
+    say(f"{w.name}: varlen 5 + 16 tokens, {2 * Hm} chains")
+    out2 = _call(d, d["q"], d["k"], d["v"], d["g"], d["beta"], None, fin2, cu=cu)
+    _check_spans(f"{w.name} varlen", d, out2, fin2, [(0, 0, 5), (1, 5, 16)], heads=heads, n_heads=Hm, init=False)
+    del d, out, out2, fin2
+    torch.cuda.empty_cache()
+
+
+def test_many_sequences():
+    rng = np.random.Generator(np.random.PCG64(44))
+    lens = rng.integers(0, 41, size=300000)
+    lens[:5] = [0, 1, 16, 17, 0]
+    total = int(lens.sum())
+    w = kda_inputs.custom(B=1, T=total, H=1, lower_bound=-3.0, init_std=None, seed=45, name="varlen300000_H1")
+    d = _device_inputs(w, 40 << 30)
+    N = len(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    fin = torch.full((N, 1, D, D), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"{w.name}: {N} sequences, {total} tokens")
+    out = _call(d, d["q"], d["k"], d["v"], d["g"], d["beta"], None, fin, cu=cu)
+    pick = sorted(set(list(range(6)) + rng.choice(N, size=40, replace=False).tolist() + [N - 1]))
+    # every chain has an end state (zero for an empty sequence), every token an output
+    assert not torch.isnan(fin).any().item()
+    assert not torch.isnan(out).any().item()
+    empty = torch.from_numpy(np.flatnonzero(lens == 0)).cuda()
+    assert not fin[empty].any().item()
+    _check_spans(w.name, d, out, fin, [(i, int(starts[i]), int(lens[i])) for i in pick], heads=[0], n_heads=1,
+                 init=False)
+    del d, out, fin
+    torch.cuda.empty_cache()
 
 
 def test_fixed_length_past_2_32_elements(big):
