@@ -3,7 +3,9 @@
 Both run the same kernels on the same plan, so their results must agree bit
 for bit.  Two calls in a row, the second smaller, so that the second one runs
 over the scratch array the first left behind (nothing in it may be assumed to
-start at zero).  Both also stay within the oracle's tolerance."""
+start at zero).  Both also stay within the oracle's tolerance.  A skewed
+varlen batch of 256 chains shows that the array counts as room for the
+automatic plan's split, as a kda_fwd workspace of the segmented size does."""
 import pytest
 
 import kda_inputs
@@ -23,7 +25,9 @@ def _need_gpu():
     kda.load_library()
 
 
-def _both(w, cp_mode, seg_chunks, heads):
+def _both(w, cp_mode, seg_chunks, heads, groups=None):
+    """groups: lists of sequences compared with the oracle separately (each
+    against its own RMS); by default all at once."""
     import kimi_delta_attention_02_amd as kda
 
     say(f"case noalloc {w.name} cp={cp_mode} seg={seg_chunks}")
@@ -51,7 +55,9 @@ def _both(w, cp_mode, seg_chunks, heads):
                          f2.view(torch.int16) if sdt == torch.bfloat16 else f2.view(torch.int32))
     say(f"noalloc {w.name}: out identical={same_o} final identical={same_f}")
     assert same_o and same_f
-    check_against_oracle(w, x, o2, f2, heads=heads, final_dtype=w.state_dtype)
+    for seqs in groups or [None]:
+        check_against_oracle(w, x, o2, f2, seqs=seqs, heads=heads, final_dtype=w.state_dtype)
+    return x, d, o2
 
 
 def test_noalloc_equals_fwd_two_calls_second_smaller():
@@ -61,3 +67,27 @@ def test_noalloc_equals_fwd_two_calls_second_smaller():
     w = kda_inputs.custom(seqlens=[300, 17, 0, 520], H=4, lower_bound=-1.0, state_dtype="bf16", seed=41,
                           name="noalloc_varlen4_H4")
     _both(w, "force", 3, heads=None)
+
+
+def test_noalloc_splits_a_skewed_batch_like_fwd():
+    import kimi_delta_attention_02_amd as kda
+
+    # one 3000-token sequence among 255 of 4 tokens, H = 1: 256 chains, which the
+    # automatic plan keeps serial unless the workspace holds the segmented layout
+    # (89 MiB here, within the array; fwd allocates it for such calls).  At lower
+    # bound 0 the segmented result differs from the serial one in its low bits,
+    # so equal bits mean that both calls took the split.  Without decay the long
+    # sequence's state grows to ~6 times the short ones' RMS, so the two kinds are
+    # held to the oracle's tolerance each against their own RMS.
+    lens = [3000] + [4] * 255
+    assert kda.varlen_seg_choice(lens, 1) == (16, True)
+    assert kda.get_workspace_size(sum(lens), 1, len(lens), "force", 0) <= kda.NOALLOC_SCRATCH_BYTES
+    w = kda_inputs.custom(seqlens=lens, H=1, lower_bound=0.0, state_dtype="fp32", seed=47,
+                          name="noalloc_skewed_256x1")
+    x, d, o2 = _both(w, "auto", 0, heads=None, groups=[[0], list(range(1, len(lens)))])
+    serial = torch.full_like(o2, float("nan"))
+    kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], serial, A_log=d["A_log"], dt_bias=d["dt_bias"],
+            lower_bound=x["lower_bound"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], cp_mode="off",
+            check=True)
+    torch.cuda.synchronize()
+    assert not torch.equal(serial.view(torch.int16), o2.view(torch.int16))
