@@ -3,7 +3,12 @@
 The call allocates nothing, never synchronises and records no memset (the
 index kernel clears the counters itself), so it can be captured.  Every
 replay is checked against an eager call on the same inputs, with the
-program's own eager work and synchronisations between the replays."""
+program's own eager work and synchronisations between the replays.  The eager
+reference calls run on the graph's own workspace, or on a workspace of their
+own, so that the graph's workspace sees only replays back to back: a replay
+keeps the captured call's epoch, and the flags each replay leaves behind must
+not pass for the next one's (the second pass clears them).  At lower bound
+-0.1 no segment's transition vanishes, and every replay merges and reruns."""
 import pytest
 
 import kda_inputs
@@ -13,13 +18,14 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cp", ["off", "force"])
-def test_graph_replays_equal_eager_calls(cp):
+@pytest.mark.parametrize("cp,ref_ws,lb", [("off", "same", -5.0), ("force", "same", -5.0),
+                                          ("force", "separate", -5.0), ("force", "separate", -0.1)])
+def test_graph_replays_equal_eager_calls(cp, ref_ws, lb):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from tests.gpu_util import dev_inputs
 
-    w = kda_inputs.custom(seqlens=[300, 90, 257], H=2, lower_bound=-5.0, seed=51, name=f"graph {cp}")
+    w = kda_inputs.custom(seqlens=[300, 90, 257], H=2, lower_bound=lb, seed=51, name=f"graph {cp}")
     d = dev_inputs(kda_inputs.make_inputs(w))
     x = kda_inputs.make_inputs(w)
     N, H = w.N, w.H
@@ -28,9 +34,11 @@ def test_graph_replays_equal_eager_calls(cp):
     fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device="cuda")
     init = d["initial_state"].clone()
 
-    def call(o, f):
+    ws_ref = ws if ref_ws == "same" else torch.empty_like(ws)
+
+    def call(o, f, wsp=ws):
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], o, A_log=d["A_log"], dt_bias=d["dt_bias"],
-                lower_bound=x["lower_bound"], workspace=ws, initial_state=init, final_state=f,
+                lower_bound=x["lower_bound"], workspace=wsp, initial_state=init, final_state=f,
                 cu_seqlens=d["cu_seqlens"], cp_mode=cp, seg_chunks=5)
 
     call(out, fin)  # warm up outside the capture
@@ -50,7 +58,7 @@ def test_graph_replays_equal_eager_calls(cp):
         torch.cuda.synchronize()
         o_ref = torch.empty_like(out)
         f_ref = torch.empty_like(fin)
-        call(o_ref, f_ref)
+        call(o_ref, f_ref, ws_ref)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {rep}: output differs"
         assert torch.equal(fin, f_ref), f"replay {rep}: final state differs"
